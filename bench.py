@@ -1,0 +1,183 @@
+"""Benchmark of the fused LM-head linear + cross-entropy path on one gfx950 GPU.
+
+A step is one forward (logprob, lse, entropy) plus one backward (dX, dW) of the
+M=8192, H=8192, V=131072 bf16 workload with entropy on and grad_logprob = 1/M,
+through the libflce C ABI.  Inputs are seeded synthetic bf16 (no dataset), resident
+in HBM before timing starts.  FLOPs follow the four-classifier-GEMM convention:
+2MHV for the forward, 8MHV for forward + backward (forward logits, recomputed
+logits, dX, dW).
+
+Prints one JSON line.  Also measures, with HIP events on the launch stream, the
+dominant kernel (the fused GEMM + online-softmax forward kernel, launched alone
+through flce_forward_partials) against the dense bf16 MFMA peak, and times the fp64
+CPU oracle on a bounded sample of the same workload.
+"""
+import os
+
+# the oracle's BLAS must use every core this job may run on; set before numpy loads
+_CORES = len(os.sched_getaffinity(0))
+for _v in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(_CORES))
+
+import argparse  # noqa: E402
+import json  # noqa: E402
+import sys  # noqa: E402
+import time  # noqa: E402
+
+import numpy as np  # noqa: E402
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+METRIC = "fwd & fwd+bwd TFLOP/s (% bf16 MFMA peak), M=8192 H=8192 V=131072"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, help="workload config (default 4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the oracle sample (0: sized for ~15 s)")
+    return ap.parse_args()
+
+
+def cpu_baseline(case, rows_req):
+    """Time the fp64 oracle (forward + backward) on the first R tokens of the workload."""
+    from oracle import flce_ref as ref
+    M, H, V = case.M, case.H, case.V
+    Wd = ref.decode_bf16(case.W)
+    # calibrate on 8 rows, then size the sample for ~15 s of CPU work
+    R0 = 8
+    t0 = time.perf_counter()
+    _run_oracle_rows(ref, case, Wd, R0)
+    t_cal = time.perf_counter() - t0
+    R = rows_req if rows_req > 0 else int(max(8, min(M, R0 * 15.0 / max(t_cal, 1e-3))))
+    t0 = time.perf_counter()
+    _run_oracle_rows(ref, case, Wd, R)
+    dt = time.perf_counter() - t0
+    flops = 8.0 * R * H * V
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _CORES, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, forward + backward of the first {R} of {M} tokens "
+                      f"(H={H}, V={V}, full vocabulary), {dt:.1f} s wall; rate counted as "
+                      f"8*R*H*V like the GPU step (the oracle itself does 6*R*H*V, no recompute)"}
+
+
+def _run_oracle_rows(ref, case, Wd, R):
+    rows = np.arange(R)
+    o = ref.forward_rows(case.X, case.W, case.targets, rows, case.ignore_index, case.scale,
+                         case.compute_entropy, Wd=Wd)
+    Xd = ref.decode_bf16(case.X[:R])
+    glp = None if case.grad_logprob is None else case.grad_logprob[:R]
+    gent = None if case.grad_entropy is None else case.grad_entropy[:R]
+    dX, dW = ref.backward_f64(Xd, Wd, case.targets[:R], case.ignore_index, case.scale, glp, gent)
+    return o, dX, dW
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from log_prob_amd import flce
+    from synth import inputs
+    from tests.gpu_util import to_dev
+
+    cfg = args.config
+    case = inputs.config_case(cfg)
+    M, H, V = case.M, case.H, case.V
+    dev = torch.device("cuda:0")
+    X, W, t, glp, gent = to_dev(case, dev)
+    ent = case.compute_entropy or gent is not None
+    fwd_b, bwd_b = flce.workspace_query(M, H, V, ent)
+    ws = torch.empty(max(fwd_b, bwd_b), dtype=torch.uint8, device=dev)
+    logprob = torch.empty(M, dtype=torch.float32, device=dev)
+    lse = torch.empty_like(logprob)
+    entropy = torch.empty_like(logprob) if ent else None
+    dX = torch.empty_like(X)
+    dW = torch.empty_like(W)
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        flce.forward(X, W, t, case.ignore_index, case.scale, ent, workspace=ws,
+                     out=(logprob, lse, entropy))
+
+    def step():
+        fwd()
+        flce.backward(X, W, t, lse, entropy if gent is not None else None, glp, gent,
+                      case.ignore_index, case.scale, workspace=ws, out=(dX, dW))
+
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-job timing: K steps bracketed by synchronisation
+    t0 = time.perf_counter()
+    step_ms = timed(step, args.steps)
+    wall = time.perf_counter() - t0
+    ms = float(np.mean(step_ms))
+    ms_med = float(np.median(step_ms))
+
+    # forward alone and the dominant kernel alone (HIP events on the launch stream)
+    for _ in range(2):
+        fwd()
+    fwd_ms = float(np.median(timed(fwd, max(args.steps, 5))))
+    part = lambda: flce.forward_partials(X, W, t, case.ignore_index, case.scale, ent, workspace=ws)
+    part()
+    k_ms = timed(part, max(args.steps, 5))
+    k_avg = float(np.mean(k_ms))
+
+    flop_f = 2.0 * M * H * V
+    flop_fb = 8.0 * M * H * V
+    tf_fb = flop_fb / (ms * 1e-3) / 1e12
+    tf_f = flop_f / (fwd_ms * 1e-3) / 1e12
+    k_tf = flop_f / (k_avg * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(tf_fb, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"fused linear+CE forward+backward, M={M} H={H} V={V} bf16, "
+                               f"entropy {'on' if ent else 'off'}, scale={case.scale:g}",
+                   "M": M, "H": H, "V": V, "flops_per_step": flop_fb},
+        "pct_peak": round(100.0 * tf_fb / PEAK_BF16_TFLOPS, 2),
+        "ms_per_step_median": round(ms_med, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_tflops": round(tf_f, 2),
+        "fwd_pct_peak": round(100.0 * tf_f / PEAK_BF16_TFLOPS, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "mfma", "kernel": "fwd_tile_kernel (fused GEMM + online softmax)",
+                     "achieved": round(k_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(k_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(k_avg, 4), "flops_per_launch": flop_f},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

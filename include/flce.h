@@ -1,0 +1,153 @@
+/*
+ * libflce: fused LM-head linear + cross-entropy (per-token log-prob, log-sum-exp
+ * and optional entropy) for AMD gfx950, forward and backward, without ever
+ * materialising the [M, V] logits.
+ *
+ * The operation (Liger-Kernel commit "native Blackwell tensor-parallel fused
+ * scaled linear cross-entropy", section "Summary": the classifier GEMM fused with
+ * NLL/LSE and optional entropy; SkyRL PR 2141 "perf(megatron): autotune fused
+ * LM-head Triton kernels", sections "Summary"/"Overview": per-token log-probs,
+ * optional entropy via compute_entropy, LSE seeded from the true row maximum):
+ *
+ *   z[m, v]    = scale * sum_k X[m, k] * W[v, k]        bf16 inputs, fp32 accumulation
+ *   lse[m]     = log sum_v exp z[m, v]
+ *   logprob[m] = z[m, t[m]] - lse[m]
+ *   entropy[m] = -sum_v p[m, v] log p[m, v],  p = softmax(z[m, :])
+ *
+ * A row m is valid iff t[m] != ignore_index and 0 <= t[m] < V.  Invalid rows get
+ * logprob = 0 and entropy = 0 (lse is still written) and contribute nothing to
+ * the gradients.
+ *
+ * Backward, for a loss L with dL/dlogprob = grad_logprob and dL/dentropy =
+ * grad_entropy (Liger-Kernel PR 1294 "Triton MoE improvements and chunked GRPO
+ * improvements", "Kernel design notes": logits tiles are recomputed to form
+ * grad_logits in the input dtype, then the two grad GEMMs):
+ *
+ *   dz[m, v] = a[m] (1[v = t[m]] - p[m, v]) + b[m] p[m, v] (E[m] - z[m, v])
+ *   a = grad_logprob * valid, b = grad_entropy * valid, E = lse - entropy
+ *   dX = scale * dz W,  dW = scale * dz^T X            (bf16 results)
+ *
+ * Layouts: every matrix is row-major and contiguous.  X is [M, H] bf16, W is
+ * [V, H] bf16 (the nn.Linear weight layout, logits = X W^T), targets is [M]
+ * int64.  All pointers are device pointers except the size_t outputs of
+ * flce_workspace_query.
+ *
+ * Ownership and ordering: the caller owns every buffer (inputs, outputs and the
+ * workspace).  The library never allocates or frees device memory and never
+ * synchronises: a call validates its arguments on the host, enqueues kernels on
+ * `stream` and returns; results are valid in stream order.  Inputs are never
+ * written.  Outputs are overwritten, not accumulated.  Workspace contents are not
+ * preserved between calls; forward -> backward state travels only through the
+ * caller-held lse and entropy outputs.  Calls on different streams may run
+ * concurrently if they use different workspaces and outputs.
+ *
+ * Errors: return codes only; nothing aborts.  All argument checks happen on the
+ * host before any HIP call, so a rejected call enqueues nothing.  After
+ * FLCE_ERR_HIP some kernels of the call may already have been enqueued.
+ * flce_last_error_message() gives a thread-local description of the last failure.
+ */
+#ifndef LIBFLCE_FLCE_H
+#define LIBFLCE_FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* hipStream_t is `struct ihipStream_t *`; NULL = default stream */
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_VALUE = 1,       /* NULL pointer, size <= 0, bad flag, non-finite scale */
+  FLCE_ERR_UNSUPPORTED = 2,         /* H % 8 != 0, pointer not 16-byte aligned, size too large */
+  FLCE_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below what the call needs */
+  FLCE_ERR_HIP = 4                  /* a HIP launch failed; see flce_last_error_message() */
+} flce_status_t;
+
+/*
+ * Workspace bytes needed by flce_forward (*fwd_bytes) and the preferred size for
+ * flce_backward (*bwd_bytes) for this problem shape.  One buffer of
+ * max(*fwd_bytes, *bwd_bytes) serves both.  Either output pointer may be NULL.
+ * Sizes: 1 <= M < 2^31, 1 <= H < 2^20 with H % 8 == 0, 1 <= V < 2^31.
+ */
+flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_entropy,
+                                   size_t* fwd_bytes, size_t* bwd_bytes);
+
+/*
+ * Smallest workspace flce_backward accepts.  The backward walks the vocabulary
+ * in chunks whose width it derives from the workspace it is given: the
+ * preferred size holds every column in one chunk, the minimum holds one tile
+ * column (256 vocabulary entries) per chunk plus an fp32 dX accumulator.
+ * Results differ between chunk widths only by fp32 summation order in dX.
+ */
+flce_status_t flce_backward_workspace_min(int64_t M, int64_t H, int64_t V, size_t* bytes);
+
+/* Chunk width (vocabulary columns) flce_backward would use with this workspace. */
+flce_status_t flce_backward_chunk_cols(int64_t M, int64_t H, int64_t V, size_t workspace_bytes,
+                                       int64_t* chunk_cols);
+
+/*
+ * Forward.  Writes logprob[M], lse[M] and, if compute_entropy == 1, entropy[M]
+ * (all fp32).  entropy may be NULL only when compute_entropy == 0.
+ * scale is the temperature factor applied to the fp32 accumulator (1/T).
+ * workspace: device memory of at least *fwd_bytes from flce_workspace_query,
+ * 256-byte aligned.
+ */
+flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets,
+                           int64_t M, int64_t H, int64_t V, int64_t ignore_index, float scale,
+                           int compute_entropy, float* logprob, float* lse, float* entropy,
+                           void* workspace, size_t workspace_bytes, struct ihipStream_t* stream);
+
+/*
+ * The two halves of flce_forward, for callers that exchange or inspect the
+ * per-tile statistics (a vocabulary-sharded caller gathers them across shards
+ * before merging).  flce_forward_partials runs the fused GEMM + online-softmax
+ * kernel and leaves in the workspace, for every row m and 256-column vocabulary
+ * tile j (j < ceil(V / 256), Mpad = 256 * ceil(M / 256)), at float offsets
+ *   j * Mpad + m                       max_v z[m, v] over the tile
+ *   (n_vt + j) * Mpad + m              sum_v exp(z[m, v] - max)
+ *   (2 n_vt + j) * Mpad + m            sum_v exp(z[m, v] - max) (z[m, v] - max)  (entropy only)
+ * and after the 2 (or 3) partial arrays (each rounded up to 256 bytes) the
+ * target logit z[m, t[m]] of every valid row.  flce_forward_merge turns them into
+ * logprob, lse and entropy; its arguments must match the partials call.
+ */
+flce_status_t flce_forward_partials(const void* X, const void* W, const int64_t* targets,
+                                    int64_t M, int64_t H, int64_t V, int64_t ignore_index,
+                                    float scale, int compute_entropy, void* workspace,
+                                    size_t workspace_bytes, struct ihipStream_t* stream);
+
+flce_status_t flce_forward_merge(const int64_t* targets, int64_t M, int64_t H, int64_t V,
+                                 int64_t ignore_index, int compute_entropy, float* logprob,
+                                 float* lse, float* entropy, const void* workspace,
+                                 size_t workspace_bytes, struct ihipStream_t* stream);
+
+/*
+ * Backward.  Recomputes the logits, forms dz and writes dX [M, H] and dW [V, H]
+ * in bf16.  lse comes from flce_forward; entropy (from flce_forward with
+ * compute_entropy == 1) is required iff grad_entropy != NULL.  grad_logprob and
+ * grad_entropy are fp32 [M]; NULL means zero (both NULL writes zero gradients).
+ * workspace: at least flce_backward_workspace_min bytes, 256-byte aligned.
+ */
+flce_status_t flce_backward(const void* X, const void* W, const int64_t* targets,
+                            int64_t M, int64_t H, int64_t V, int64_t ignore_index, float scale,
+                            const float* lse, const float* entropy,
+                            const float* grad_logprob, const float* grad_entropy,
+                            void* dX, void* dW,
+                            void* workspace, size_t workspace_bytes, struct ihipStream_t* stream);
+
+/* Static description of a status code. */
+const char* flce_status_string(flce_status_t status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* flce_last_error_message(void);
+
+/* Library version as "major.minor.patch". */
+const char* flce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFLCE_FLCE_H */

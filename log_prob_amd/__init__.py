@@ -1,0 +1,5 @@
+"""libflce: fused LM-head linear + cross-entropy (log-prob, LSE, entropy) for gfx950.
+
+`log_prob_amd.flce` is the ctypes binding of the C ABI declared in include/flce.h.
+"""
+__all__ = ["flce"]

@@ -1,0 +1,89 @@
+// Internal interface between the libflce host code (flce_api.cpp) and its HIP
+// kernels (flce_kernels.hip).  Not installed; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flce {
+
+constexpr int kTile = 256;  // workgroup tile edge used by every kernel
+
+struct FwdTileArgs {
+  const uint16_t* X;        // bf16 [M, H]
+  const uint16_t* W;        // bf16 [V, H]
+  const int64_t* targets;   // [M]
+  int M, H, V;
+  int64_t ignore_index;
+  float scale;
+  int n_mt, n_vt;           // tiles along M and V
+  int Mpad;                 // n_mt * 256: row stride of the partial arrays
+  float* part_m;            // [n_vt, Mpad] tile row max of z
+  float* part_s;            // [n_vt, Mpad] sum exp(z - m)
+  float* part_u;            // [n_vt, Mpad] sum exp(z - m) (z - m)   (entropy only)
+  float* zt;                // [Mpad] target logit (written by the owning tile)
+};
+
+struct FwdMergeArgs {
+  const int64_t* targets;
+  int M, V;
+  int64_t ignore_index;
+  int n_vt, Mpad;
+  const float* part_m;
+  const float* part_s;
+  const float* part_u;
+  const float* zt;
+  float* logprob;
+  float* lse;
+  float* entropy;
+};
+
+struct DlogitsArgs {
+  const uint16_t* X;
+  const uint16_t* W;
+  const int64_t* targets;
+  int M, H, V;
+  int64_t ignore_index;
+  float scale;
+  const float* lse;
+  const float* entropy;       // needed iff grad_entropy != NULL
+  const float* grad_logprob;  // NULL = 0
+  const float* grad_entropy;  // NULL = 0
+  int vbase;                  // first vocabulary column of the chunk
+  int n_mt, n_vt;             // tiles along M and along the chunk
+  uint16_t* dz;               // bf16 [Mpad, ldz]: scale * dz of the chunk
+  long ldz;
+};
+
+struct GemmDwArgs {
+  const uint16_t* dz;   // bf16 [Mpad, ldz]
+  long ldz;
+  const uint16_t* X;    // bf16 [M, H]
+  uint16_t* dW;         // bf16 [V, H]
+  int M, Mpad, H, V;
+  int vbase;
+  int chunk_cols;       // padded width of the chunk (multiple of 256)
+  int n_i, n_h;         // tiles along the chunk and along H
+};
+
+struct GemmDxArgs {
+  const uint16_t* dz;   // bf16 [Mpad, ldz]
+  long ldz;
+  const uint16_t* W;    // bf16 [V, H]
+  float* acc;           // fp32 [M, H] accumulator across chunks (modes 1-3)
+  uint16_t* dX;         // bf16 [M, H]
+  int M, H, V;
+  int vbase;
+  int kcols;            // padded width of the chunk (multiple of 256)
+  int n_m, n_h;
+  int mode;             // 0 write bf16, 1 write acc, 2 add to acc, 3 add and write bf16
+};
+
+hipError_t launch_fwd_tile(const FwdTileArgs& a, bool entropy, hipStream_t s);
+hipError_t launch_fwd_merge(const FwdMergeArgs& a, bool entropy, hipStream_t s);
+hipError_t launch_dlogits(const DlogitsArgs& a, bool entropy_grad, hipStream_t s);
+hipError_t launch_gemm_dw(const GemmDwArgs& a, hipStream_t s);
+hipError_t launch_gemm_dx(const GemmDxArgs& a, hipStream_t s);
+hipError_t launch_fill_zero_u16(uint16_t* p, long n, hipStream_t s);
+
+}  // namespace flce

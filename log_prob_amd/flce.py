@@ -1,0 +1,208 @@
+"""Thin ctypes binding of libflce (the C ABI in include/flce.h).
+
+Only argument marshalling lives here: every step of the computation runs in the
+HIP kernels of libflce.so.  torch supplies device memory and the current stream.
+If the library is missing, loading fails loudly; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflce.so")
+
+FLCE_OK = 0
+STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_INVALID_VALUE", 2: "FLCE_ERR_UNSUPPORTED",
+          3: "FLCE_ERR_WORKSPACE_TOO_SMALL", 4: "FLCE_ERR_HIP"}
+
+# Every symbol include/flce.h declares.
+EXPORTS = ("flce_workspace_query", "flce_backward_workspace_min", "flce_backward_chunk_cols",
+           "flce_forward", "flce_forward_partials", "flce_forward_merge", "flce_backward", "flce_status_string", "flce_last_error_message",
+           "flce_version")
+
+_lib = None
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libflce.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libflce.so not built at {path}; run `python -m log_prob_amd.build`")
+    lib = ctypes.CDLL(path)
+    c = ctypes
+    P, I64, SZ = c.c_void_p, c.c_int64, c.c_size_t
+    lib.flce_workspace_query.argtypes = [I64, I64, I64, c.c_int, c.POINTER(SZ), c.POINTER(SZ)]
+    lib.flce_backward_workspace_min.argtypes = [I64, I64, I64, c.POINTER(SZ)]
+    lib.flce_backward_chunk_cols.argtypes = [I64, I64, I64, SZ, c.POINTER(I64)]
+    lib.flce_forward.argtypes = [P, P, P, I64, I64, I64, I64, c.c_float, c.c_int, P, P, P, P, SZ, P]
+    lib.flce_forward_partials.argtypes = [P, P, P, I64, I64, I64, I64, c.c_float, c.c_int, P, SZ,
+                                          P]
+    lib.flce_forward_merge.argtypes = [P, I64, I64, I64, I64, c.c_int, P, P, P, P, SZ, P]
+    lib.flce_backward.argtypes = [P, P, P, I64, I64, I64, I64, c.c_float, P, P, P, P, P, P, P,
+                                  SZ, P]
+    for name in ("flce_workspace_query", "flce_backward_workspace_min", "flce_backward_chunk_cols",
+                 "flce_forward", "flce_forward_partials", "flce_forward_merge", "flce_backward"):
+        getattr(lib, name).restype = c.c_int
+    lib.flce_status_string.argtypes = [c.c_int]
+    lib.flce_status_string.restype = c.c_char_p
+    lib.flce_last_error_message.argtypes = []
+    lib.flce_last_error_message.restype = c.c_char_p
+    lib.flce_version.argtypes = []
+    lib.flce_version.restype = c.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != FLCE_OK:
+        raise FlceError(status, load().flce_last_error_message().decode())
+
+
+def workspace_query(M: int, H: int, V: int, compute_entropy: bool = True) -> Tuple[int, int]:
+    fwd, bwd = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().flce_workspace_query(M, H, V, int(bool(compute_entropy)), ctypes.byref(fwd),
+                                       ctypes.byref(bwd)))
+    return fwd.value, bwd.value
+
+
+def backward_workspace_min(M: int, H: int, V: int) -> int:
+    b = ctypes.c_size_t()
+    _check(load().flce_backward_workspace_min(M, H, V, ctypes.byref(b)))
+    return b.value
+
+
+def backward_chunk_cols(M: int, H: int, V: int, workspace_bytes: int) -> int:
+    c = ctypes.c_int64()
+    _check(load().flce_backward_chunk_cols(M, H, V, workspace_bytes, ctypes.byref(c)))
+    return c.value
+
+
+# ----------------------------------------------------------------------------
+# torch-facing wrappers
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, name, dtype, shape):
+    import torch
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def alloc_workspace(nbytes: int, device):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def forward(X, W, targets, ignore_index: int = -100, scale: float = 1.0,
+            compute_entropy: bool = True, workspace=None, out=None):
+    """(logprob, lse, entropy-or-None) as fp32 [M] tensors, on X's device and stream."""
+    import torch
+    M, H = X.shape
+    V = W.shape[0]
+    _require(X, "X", torch.bfloat16, (M, H))
+    _require(W, "W", torch.bfloat16, (V, H))
+    _require(targets, "targets", torch.int64, (M,))
+    dev = X.device
+    if out is None:
+        logprob = torch.empty(M, dtype=torch.float32, device=dev)
+        lse = torch.empty(M, dtype=torch.float32, device=dev)
+        entropy = torch.empty(M, dtype=torch.float32, device=dev) if compute_entropy else None
+    else:
+        logprob, lse, entropy = out
+    if workspace is None:
+        fwd_b, _ = workspace_query(M, H, V, compute_entropy)
+        workspace = alloc_workspace(fwd_b, dev)
+    _check(load().flce_forward(_ptr(X), _ptr(W), _ptr(targets), M, H, V, int(ignore_index),
+                               float(scale), int(bool(compute_entropy)), _ptr(logprob), _ptr(lse),
+                               _ptr(entropy), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return logprob, lse, entropy
+
+
+def forward_partials(X, W, targets, ignore_index: int = -100, scale: float = 1.0,
+                     compute_entropy: bool = True, workspace=None):
+    """Run only the fused GEMM + online-softmax kernel; partials stay in `workspace`."""
+    import torch
+    M, H = X.shape
+    V = W.shape[0]
+    _require(X, "X", torch.bfloat16, (M, H))
+    _require(W, "W", torch.bfloat16, (V, H))
+    _require(targets, "targets", torch.int64, (M,))
+    if workspace is None:
+        workspace = alloc_workspace(workspace_query(M, H, V, compute_entropy)[0], X.device)
+    _check(load().flce_forward_partials(_ptr(X), _ptr(W), _ptr(targets), M, H, V,
+                                        int(ignore_index), float(scale),
+                                        int(bool(compute_entropy)), _ptr(workspace),
+                                        workspace.numel(), _stream(X.device)))
+    return workspace
+
+
+def forward_merge(targets, M: int, H: int, V: int, workspace, ignore_index: int = -100,
+                  compute_entropy: bool = True, out=None):
+    """Merge partials left by forward_partials into (logprob, lse, entropy-or-None)."""
+    import torch
+    _require(targets, "targets", torch.int64, (M,))
+    dev = targets.device
+    if out is None:
+        logprob = torch.empty(M, dtype=torch.float32, device=dev)
+        lse = torch.empty(M, dtype=torch.float32, device=dev)
+        entropy = torch.empty(M, dtype=torch.float32, device=dev) if compute_entropy else None
+    else:
+        logprob, lse, entropy = out
+    _check(load().flce_forward_merge(_ptr(targets), M, H, V, int(ignore_index),
+                                     int(bool(compute_entropy)), _ptr(logprob), _ptr(lse),
+                                     _ptr(entropy), _ptr(workspace), workspace.numel(),
+                                     _stream(dev)))
+    return logprob, lse, entropy
+
+
+def backward(X, W, targets, lse, entropy=None, grad_logprob=None, grad_entropy=None,
+             ignore_index: int = -100, scale: float = 1.0, workspace=None, out=None):
+    """(dX, dW) as bf16 tensors shaped like X and W."""
+    import torch
+    M, H = X.shape
+    V = W.shape[0]
+    _require(X, "X", torch.bfloat16, (M, H))
+    _require(W, "W", torch.bfloat16, (V, H))
+    _require(targets, "targets", torch.int64, (M,))
+    _require(lse, "lse", torch.float32, (M,))
+    for name, t in (("entropy", entropy), ("grad_logprob", grad_logprob),
+                    ("grad_entropy", grad_entropy)):
+        if t is not None:
+            _require(t, name, torch.float32, (M,))
+    dev = X.device
+    if out is None:
+        dX = torch.empty_like(X)
+        dW = torch.empty_like(W)
+    else:
+        dX, dW = out
+    if workspace is None:
+        _, bwd_b = workspace_query(M, H, V, entropy is not None)
+        workspace = alloc_workspace(bwd_b, dev)
+    _check(load().flce_backward(_ptr(X), _ptr(W), _ptr(targets), M, H, V, int(ignore_index),
+                                float(scale), _ptr(lse), _ptr(entropy), _ptr(grad_logprob),
+                                _ptr(grad_entropy), _ptr(dX), _ptr(dW), _ptr(workspace),
+                                workspace.numel(), _stream(dev)))
+    return dX, dW

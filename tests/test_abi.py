@@ -1,0 +1,123 @@
+"""The C ABI on the CPU: the library loads, exports what include/flce.h declares, and
+rejects bad arguments before touching HIP (so no device is needed here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from log_prob_amd import flce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "flce.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(flce_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = flce.load()
+    declared = _header_functions()
+    assert declared == sorted(flce.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    lib = flce.load()
+    assert re.fullmatch(rb"\d+\.\d+\.\d+", lib.flce_version())
+    for code, name in flce.STATUS.items():
+        assert lib.flce_status_string(code).decode() == name
+
+
+def test_workspace_query_values():
+    # forward: m, s, u partials of [ceil(V/256), Mpad] fp32 + zt [Mpad]
+    fwd, bwd = flce.workspace_query(8192, 8192, 131072, True)
+    assert fwd == 3 * 512 * 8192 * 4 + 8192 * 4
+    fwd0, _ = flce.workspace_query(8192, 8192, 131072, False)
+    assert fwd0 == 2 * 512 * 8192 * 4 + 8192 * 4
+    # backward preferred: one 2 GiB d-logit chunk covers the whole vocabulary here
+    assert bwd == 8192 * 131072 * 2
+    assert flce.backward_chunk_cols(8192, 8192, 131072, bwd) == 131072
+    # smaller workspaces shrink the chunk, down to one 256-column tile plus fp32 dX
+    mn = flce.backward_workspace_min(8192, 8192, 131072)
+    assert mn == 8192 * 256 * 2 + 8192 * 8192 * 4
+    assert flce.backward_chunk_cols(8192, 8192, 131072, mn) == 256
+    # ragged shapes are padded to whole tiles
+    fwd, _ = flce.workspace_query(64, 128, 1000, True)
+    assert fwd == 3 * 4 * 256 * 4 + 256 * 4
+    _, bwd = flce.workspace_query(32767, 2048, 151936, True)
+    c = flce.backward_chunk_cols(32767, 2048, 151936, bwd)
+    assert c % 256 == 0 and 256 <= c < 151936 + 256
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+P = ctypes.c_void_p
+
+
+def _fwd(lib, X=16, W=16, t=16, M=4, H=8, V=3, ign=-100, scale=1.0, ent=1, lp=16, lse=16,
+         entropy=16, ws=256, wsb=1 << 20):
+    return lib.flce_forward(X, W, t, M, H, V, ign, scale, ent, lp, lse, entropy, ws, wsb, None)
+
+
+def test_forward_argument_errors():
+    lib = flce.load()
+    INV, UNS, WS = 1, 2, 3
+    assert _fwd(lib, X=None) == INV
+    assert _fwd(lib, t=None) == INV
+    assert _fwd(lib, lse=None) == INV
+    assert _fwd(lib, ws=None) == INV
+    assert _fwd(lib, M=0) == INV
+    assert _fwd(lib, V=-1) == INV
+    assert _fwd(lib, ent=2) == INV
+    assert _fwd(lib, entropy=None) == INV
+    assert _fwd(lib, scale=float("nan")) == INV
+    assert _fwd(lib, scale=float("inf")) == INV
+    assert _fwd(lib, H=12) == UNS
+    assert _fwd(lib, X=24) == UNS
+    assert _fwd(lib, ws=128) == UNS
+    assert _fwd(lib, M=1 << 31) == UNS
+    assert _fwd(lib, wsb=100) == WS
+    assert b"workspace" in lib.flce_last_error_message()
+
+
+def test_forward_entropy_null_allowed_when_off():
+    lib = flce.load()
+    # passes validation and only then fails on the (absent) device: anything but 1/2/3
+    st = _fwd(lib, ent=0, entropy=None, wsb=10)
+    assert st == 3   # still too small a workspace: validation order is arguments first
+
+
+def _bwd(lib, X=16, W=16, t=16, M=4, H=8, V=3, ign=-100, scale=1.0, lse=16, ent=16, glp=16,
+         gent=16, dX=16, dW=16, ws=256, wsb=1 << 20):
+    return lib.flce_backward(X, W, t, M, H, V, ign, scale, lse, ent, glp, gent, dX, dW, ws, wsb,
+                             None)
+
+
+def test_backward_argument_errors():
+    lib = flce.load()
+    INV, UNS, WS = 1, 2, 3
+    assert _bwd(lib, lse=None) == INV
+    assert _bwd(lib, dX=None) == INV
+    assert _bwd(lib, dW=None) == INV
+    assert _bwd(lib, ent=None) == INV          # grad_entropy needs the entropy output
+    assert _bwd(lib, H=0) == INV
+    assert _bwd(lib, scale=float("-inf")) == INV
+    assert _bwd(lib, H=4) == UNS
+    assert _bwd(lib, dW=18) == UNS
+    assert _bwd(lib, wsb=0) == WS
+    mn = flce.backward_workspace_min(4, 8, 3)
+    assert _bwd(lib, wsb=mn - 1) == WS
+
+
+def test_python_wrapper_raises():
+    with pytest.raises(flce.FlceError) as e:
+        flce.workspace_query(0, 8, 8)
+    assert e.value.status == 1
+    with pytest.raises(flce.FlceError):
+        flce.backward_chunk_cols(100, 64, 1000, 10)

@@ -1,0 +1,148 @@
+"""GPU parity: libflce (through the C ABI) against the fp64 oracle, element by element,
+on seeded inputs small enough for the oracle, spanning several 256 x 256 tiles and
+ragged tails in M, V and K, plus the degenerate cases of the method."""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import flce_ref as ref
+from synth import inputs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+# name, case_id, M, H, V, make_case kwargs
+CASES = [
+    ("config1_tiny", 1, 64, 128, 1000, dict(ignore_frac=0.05, grad_mode="inv_m")),
+    ("multi_tile_ragged", 101, 600, 320, 1500, dict(ignore_frac=0.05, grad_mode="normal")),
+    ("aligned_tiles", 102, 512, 256, 2048, dict(grad_mode="inv_m", ignore_frac=0.02)),
+    ("logprob_only_T07", 103, 257, 72, 257,
+     dict(scale=1 / 0.7, compute_entropy=False, grad_mode="normal_lp")),
+    ("big_rows_x64", 104, 513, 136, 3000,
+     dict(ignore_frac=0.1, big_rows_frac=0.1, big_factor=64.0, grad_mode="normal")),
+    ("k_tail_H200", 105, 300, 200, 700, dict(grad_mode="normal", ignore_frac=0.1)),
+    ("single_row", 106, 1, 64, 1000, dict(grad_mode="normal")),
+    ("single_vocab", 107, 100, 64, 1, dict(grad_mode="normal")),
+    ("min_H8", 108, 70, 8, 300, dict(grad_mode="normal")),
+    ("odd_vocab_50257", 109, 40, 64, 50257, dict(grad_mode="normal", ignore_frac=0.05)),
+    ("negative_scale", 110, 128, 64, 500, dict(scale=-0.5, grad_mode="normal")),
+    ("m_4097_tail", 111, 4097, 64, 300, dict(grad_mode="normal", ignore_frac=0.02)),
+]
+
+
+def _case(spec):
+    name, cid, M, H, V, kw = spec
+    return inputs.make_case(name, cid, M, H, V, **kw)
+
+
+def _oracle(c):
+    o = ref.forward(c.X, c.W, c.targets, c.ignore_index, c.scale, True)
+    dX, dW = ref.backward(c.X, c.W, c.targets, c.ignore_index, c.scale, c.grad_logprob,
+                          c.grad_entropy)
+    return o, dX, dW
+
+
+@pytest.mark.parametrize("spec", CASES, ids=[c[0] for c in CASES])
+def test_parity_small(spec):
+    c = _case(spec)
+    print(f"[parity] {spec[0]} M={c.M} H={c.H} V={c.V}", flush=True)
+    res = gu.run_flce(c)
+    o, dX, dW = _oracle(c)
+    gu.check_forward(res, o, c.compute_entropy, spec[0])
+    gu.check_grads(res["dX"], res["dW"], dX, dW, spec[0])
+    # ignored rows: exact zeros
+    valid = ref.valid_rows(c.targets, c.V, c.ignore_index)
+    assert np.all(res["logprob"][~valid] == 0.0)
+    if c.compute_entropy:
+        assert np.all(res["entropy"][~valid] == 0.0)
+    assert np.all(res["dX"][~valid] == 0.0)
+
+
+def test_strongly_negative_rows():
+    """Every logit of a row far below zero (about -200): lse must still be exact-ish."""
+    c = inputs.make_case("neg", 120, 300, 64, 900, grad_mode="normal")
+    X = inputs.decode_bf16_to_f32(c.X).copy()
+    W = inputs.decode_bf16_to_f32(c.W).copy()
+    X[:, 0] = -200.0    # a bias feature: every logit of every row shifted by -200 * W[:, 0]
+    W[:, 0] = 1.0
+    c.X = inputs.f32_to_bf16_bits(X)
+    c.W = inputs.f32_to_bf16_bits(W)
+    res = gu.run_flce(c)
+    o, dX, dW = _oracle(c)
+    assert np.all(o["lse"] < -150)
+    gu.check_forward(res, o, True, "strongly_negative")
+    gu.check_grads(res["dX"], res["dW"], dX, dW, "strongly_negative")
+
+
+def test_ignore_index_inside_vocab_and_out_of_range_targets():
+    c = inputs.make_case("ign", 121, 200, 64, 700, grad_mode="normal")
+    c.ignore_index = 5
+    c.targets[::7] = 5
+    c.targets[3] = 700          # == V: out of range, treated as ignored
+    c.targets[4] = -3           # negative, not ignore_index: ignored
+    res = gu.run_flce(c)
+    o, dX, dW = _oracle(c)
+    gu.check_forward(res, o, True, "ignore_inside")
+    gu.check_grads(res["dX"], res["dW"], dX, dW, "ignore_inside")
+    assert res["logprob"][3] == 0.0 and res["logprob"][4] == 0.0
+
+
+def test_chunked_backward_matches():
+    """The smallest workspace forces 256-column chunks and the fp32 dX accumulator."""
+    import torch
+    from log_prob_amd import flce
+    c = inputs.make_case("chunk", 122, 300, 136, 1300, grad_mode="normal", ignore_frac=0.1)
+    mn = flce.backward_workspace_min(c.M, c.H, c.V)
+    assert flce.backward_chunk_cols(c.M, c.H, c.V, mn) == 256
+    ws = torch.empty(mn, dtype=torch.uint8, device="cuda")
+    res_small = gu.run_flce(c, bwd_ws=ws)
+    res_full = gu.run_flce(c)
+    o, dX, dW = _oracle(c)
+    gu.check_grads(res_small["dX"], res_small["dW"], dX, dW, "chunked")
+    # dW is computed chunk by chunk either way: identical; dX differs only in fp32 order
+    np.testing.assert_array_equal(res_small["dW"], res_full["dW"])
+    # one bf16 ulp (2^-8 relative) at most, from fp32 summation order before rounding
+    assert gu.rel_max(res_small["dX"], res_full["dX"]) <= 5e-3
+
+
+def test_zero_grads_write_zeros():
+    import torch
+    from log_prob_amd import flce
+    c = inputs.make_case("zero", 123, 100, 64, 300, grad_mode="none")
+    X, W, t, _, _ = gu.to_dev(c)
+    lp, lse, ent = flce.forward(X, W, t)
+    dX = torch.full_like(X, 3.0)
+    dW = torch.full_like(W, 3.0)
+    flce.backward(X, W, t, lse, None, None, None, out=(dX, dW))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dX).item() == 0 and torch.count_nonzero(dW).item() == 0
+
+
+def test_repeat_is_bitwise_deterministic_and_poison_safe():
+    """Two runs give identical bits, also when the workspace starts full of NaN bytes."""
+    import torch
+    from log_prob_amd import flce
+    c = inputs.make_case("det", 124, 700, 136, 2100, grad_mode="normal", ignore_frac=0.05)
+    X, W, t, glp, gent = gu.to_dev(c)
+    fb, bb = flce.workspace_query(c.M, c.H, c.V, True)
+    outs = []
+    for poison in (False, True):
+        ws = torch.empty(max(fb, bb), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xFF if poison else 0)
+        lp, lse, ent = flce.forward(X, W, t, workspace=ws)
+        ws.fill_(0xFF if poison else 0)
+        dX, dW = flce.backward(X, W, t, lse, ent, glp, gent, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([v.clone() for v in (lp, lse, ent, dX, dW)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+def test_grad_zero_sum_property():
+    """Rows of d-logits sum to zero, so every dW column sums to ~0 (at any size)."""
+    c = inputs.make_case("zs", 125, 1024, 256, 4096, grad_mode="normal")
+    res = gu.run_flce(c)
+    dW = res["dW"]
+    assert np.abs(dW.sum(0)).max() <= 2e-2 * np.abs(dW).sum(0).max()
