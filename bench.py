@@ -42,7 +42,80 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the oracle sample (0: sized for ~15 s)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--kernel-only", choices=["fwd"], default=None,
+                    help="only launch the fused forward kernel three times (for counter passes)")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="only time the library bf16 GEMM (torch.matmul) of the same logits shape")
     return ap.parse_args()
+
+
+def blas_reference(case, steps):
+    """Context, not a product path: the vendor bf16 GEMM for z = X W^T of the same shape,
+    which materialises the logits the fused kernel never writes."""
+    import torch
+    M, H, V = case.M, case.H, case.V
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(M, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(V, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(M, V, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b.t(), out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.matmul(a, b.t(), out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tf = 2.0 * M * H * V / (ms * 1e-3) / 1e12
+    print(json.dumps({"blas_reference": "torch.matmul bf16 X @ W^T", "M": M, "H": H, "V": V,
+                      "ms": round(ms, 4), "tflops": round(tf, 2),
+                      "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
+
+
+PROFILE = os.path.join(ROOT, "profiles", "fwd_bwd_M8192_H8192_V131072.md")
+KERNEL_SOURCES = ("log_prob_amd/csrc/flce_kernels.hip", "log_prob_amd/csrc/flce_internal.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per fwd_tile launch from the committed rocprofv3 counter summary, or
+    None if the kernel sources changed since those counters were taken."""
+    try:
+        kv = {}
+        with open(PROFILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith(("|", "#")):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return float(kv["fwd_tile_traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib):
+    """A plain copy kernel of known size: reads and writes mib MiB, three times."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
 def cpu_baseline(case, rows_req):
@@ -50,15 +123,17 @@ def cpu_baseline(case, rows_req):
     from oracle import flce_ref as ref
     M, H, V = case.M, case.H, case.V
     Wd = ref.decode_bf16(case.W)
-    # calibrate on 8 rows, then size the sample for ~15 s of CPU work
-    R0 = 8
-    t0 = time.perf_counter()
-    _run_oracle_rows(ref, case, Wd, R0)
-    t_cal = time.perf_counter() - t0
-    R = rows_req if rows_req > 0 else int(max(8, min(M, R0 * 15.0 / max(t_cal, 1e-3))))
-    t0 = time.perf_counter()
-    _run_oracle_rows(ref, case, Wd, R)
-    dt = time.perf_counter() - t0
+    # grow the sample until one timed pass takes 10-30 s of CPU work (the first
+    # call also warms up the BLAS threads)
+    _run_oracle_rows(ref, case, Wd, 8)
+    R = rows_req if rows_req > 0 else 64
+    while True:
+        t0 = time.perf_counter()
+        _run_oracle_rows(ref, case, Wd, R)
+        dt = time.perf_counter() - t0
+        if rows_req > 0 or dt >= 10.0 or R >= M:
+            break
+        R = int(min(M, max(R + 1, R * min(8.0, 15.0 / max(dt, 1e-3)))))
     flops = 8.0 * R * H * V
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _CORES, "kind": "oracle",
             "sample": f"fp64 NumPy oracle, forward + backward of the first {R} of {M} tokens "
@@ -79,6 +154,9 @@ def _run_oracle_rows(ref, case, Wd, R):
 
 def main():
     args = parse()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               f"multi-GPU path", file=sys.stderr)
@@ -89,6 +167,11 @@ def main():
     from tests.gpu_util import to_dev
 
     cfg = args.config
+    if args.blas_reference:
+        import types
+        blas_reference(types.SimpleNamespace(**{k: inputs.CONFIGS[cfg][k] for k in "MHV"}),
+                       max(args.steps, 5))
+        return
     case = inputs.config_case(cfg)
     M, H, V = case.M, case.H, case.V
     dev = torch.device("cuda:0")
@@ -122,14 +205,30 @@ def main():
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in evs]
 
+    if args.kernel_only == "fwd":
+        for _ in range(3):
+            flce.forward_partials(X, W, t, case.ignore_index, case.scale, ent, workspace=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_only": "fwd_tile", "launches": 3}), flush=True)
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # whole-job timing: K steps bracketed by synchronisation
+    # whole-job timing: exactly K steps bracketed by synchronisation (wall clock); HIP
+    # events around each step give the per-step spread
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_ms = timed(step, args.steps)
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = float(np.mean(step_ms))
+    step_ms = [a.elapsed_time(b) for a, b in evs]
+    ms = wall * 1e3 / args.steps
     ms_med = float(np.median(step_ms))
 
     # forward alone and the dominant kernel alone (HIP events on the launch stream)
@@ -164,14 +263,16 @@ def main():
                                f"entropy {'on' if ent else 'off'}, scale={case.scale:g}",
                    "M": M, "H": H, "V": V, "flops_per_step": flop_fb},
         "pct_peak": round(100.0 * tf_fb / PEAK_BF16_TFLOPS, 2),
-        "ms_per_step_median": round(ms_med, 4),
+        "ms_per_step_event_median": round(ms_med, 4),
         "fwd_ms": round(fwd_ms, 4),
         "fwd_tflops": round(tf_f, 2),
         "fwd_pct_peak": round(100.0 * tf_f / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed": round(wall, 3),
         "roofline": {"bound": "mfma", "kernel": "fwd_tile_kernel (fused GEMM + online softmax)",
                      "achieved": round(k_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(k_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(k_tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "HBM bytes/launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, scaled)",
+                     "algorithmic_bytes": 2 * M * H + 2 * V * H + 8 * M + 12 * M,
                      "avg_launch_ms": round(k_avg, 4), "flops_per_launch": flop_f},
     }
     if not args.no_cpu_baseline:

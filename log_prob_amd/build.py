@@ -36,7 +36,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     cc = hipcc()
     with tempfile.TemporaryDirectory() as tmp:
         objs = []
@@ -48,13 +48,13 @@ def build(verbose: bool = False, extra_flags=()) -> str:
                 print(" ".join(cmd), flush=True)
             subprocess.run(cmd, check=True)
             objs.append(obj)
-        out_tmp = LIB + ".tmp"
+        out_tmp = out + ".tmp"
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        os.replace(out_tmp, LIB)
-    return LIB
+        os.replace(out_tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -36,6 +36,9 @@ constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 constexpr size_t kAlign = 256;
 // Preferred size of one d-logit chunk buffer: 2 GiB.
 constexpr size_t kDzBudget = size_t(2) << 30;
+// Widest d-logit chunk: keeps every byte offset the kernels form inside one
+// 256-row tile of the chunk buffer below 2^30.
+constexpr int64_t kMaxChunk = int64_t(1) << 21;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -88,6 +91,7 @@ int64_t preferred_chunk(int64_t M, int64_t V) {
   const int64_t Vpad = cdiv(V, kTile) * kTile;
   int64_t c = int64_t(kDzBudget / (size_t(Mpad) * 2)) / kTile * kTile;
   if (c < kTile) c = kTile;
+  if (c > kMaxChunk) c = kMaxChunk;
   return c < Vpad ? c : Vpad;
 }
 
@@ -95,10 +99,11 @@ int64_t preferred_chunk(int64_t M, int64_t V) {
 int64_t chunk_for_workspace(int64_t M, int64_t H, int64_t V, size_t bytes) {
   const int64_t Mpad = cdiv(M, kTile) * kTile;
   const int64_t Vpad = cdiv(V, kTile) * kTile;
-  if (bwd_bytes_for_chunk(M, H, V, Vpad) <= bytes) return Vpad;
+  if (Vpad <= kMaxChunk && bwd_bytes_for_chunk(M, H, V, Vpad) <= bytes) return Vpad;
   const size_t acc = align_up(size_t(M) * size_t(H) * sizeof(float));
   if (bytes <= acc) return 0;
   int64_t c = int64_t((bytes - acc) / (size_t(Mpad) * 2)) / kTile * kTile;
+  if (c > kMaxChunk) c = kMaxChunk;
   while (c >= kTile && bwd_bytes_for_chunk(M, H, V, c) > bytes) c -= kTile;
   if (c >= Vpad) c = Vpad - kTile;
   return c >= kTile ? c : 0;

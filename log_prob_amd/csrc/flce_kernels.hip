@@ -16,46 +16,77 @@
 //   gemm_dw      dW[chunk] = dz_chunk^T X          (K = tokens)
 //   gemm_dx      dX (+)= dz_chunk W[chunk]          (K = chunk columns)
 //
-// All tiles are 256 x 256 with K staged 64 at a time through double-buffered
-// LDS (2 x 64 KiB) and v_mfma_f32_32x32x16_bf16.  Operands whose K dimension is
-// contiguous in memory are copied to LDS as 16-byte chunks; operands whose M/N
-// dimension is contiguous are loaded as 8x8 blocks and transposed in registers,
-// so the LDS layout (K contiguous, 128 bytes per row, XOR-swizzled 16-byte
-// chunks) and the MFMA fragment reads are the same for every operand.
+// Every kernel computes 256 x 256 output tiles with 4 waves of 128 x 128 and
+// v_mfma_f32_32x32x16_bf16.  K is staged 64 at a time through double-buffered LDS
+// (2 x 64 KiB) by direct-to-LDS buffer loads: no staging registers, and lanes whose
+// 16 bytes lie outside the operand get an out-of-range offset, which the buffer
+// unit turns into zeros.  An operand whose K dimension is contiguous in memory is
+// kept in LDS as 128-byte K rows and read with ds_read_b128; an operand whose M/N
+// dimension is contiguous is kept as 512-byte K rows and read with the gfx950
+// transposing read ds_read_b64_tr_b16, which hands each lane 4 consecutive K values
+// of one column.  Both layouts XOR-swizzle 16- or 32-byte blocks by row so the
+// fragment reads are free of bank conflicts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "flce_internal.h"
 
+#define LDS_AS __attribute__((address_space(3)))
+
 namespace flce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TILE = 256;               // rows and columns of a workgroup tile
-constexpr int BK = 64;                  // K per LDS stage
-constexpr int NTHREADS = 256;           // 4 waves of 64
-constexpr int TILE_BYTES = TILE * BK * 2;          // one operand tile in LDS: 32 KiB
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;        // A and B
-constexpr int LDS_MAIN = 2 * STAGE_BYTES;          // double buffered: 128 KiB
+constexpr int TILE = 256;        // rows and columns of a workgroup tile
+constexpr int NTHREADS = 256;    // 4 waves of 64
+// Pipeline shape (tuning builds may override the defaults).
+#ifndef FLCE_BKS
+#define FLCE_BKS 64
+#endif
+#ifndef FLCE_NST
+#define FLCE_NST 2
+#endif
+#ifndef FLCE_FRAG_PREFETCH
+#define FLCE_FRAG_PREFETCH 1
+#endif
+#ifndef FLCE_DMA_SPREAD
+#define FLCE_DMA_SPREAD 1
+#endif
+#ifndef FLCE_STAGGER
+#define FLCE_STAGGER 0
+#endif
+constexpr int BKS = FLCE_BKS;    // K per LDS stage
+constexpr int NST = FLCE_NST;    // LDS stages (loads run NST - 1 stages ahead)
+constexpr bool FRAG_PREFETCH = FLCE_FRAG_PREFETCH != 0;  // read kk + 1 before kk's MFMAs
+constexpr int DMA_SPREAD = FLCE_DMA_SPREAD;  // MFMA sub-steps a stage's loads are spread over
+// Workgroups start their K loop at one of STAGGER evenly spaced K steps (and wrap
+// around).  Operand rows are a power-of-two number of bytes apart, so at a fixed K
+// offset every row of every tile falls on the same few L2 channels; rotating the
+// start spreads the concurrent workgroups over all channels.
+constexpr int STAGGER = FLCE_STAGGER;
+constexpr int TILE_BYTES = TILE * BKS * 2;            // one operand tile: 16 KiB
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;           // A and B
+constexpr int LDS_MAIN = NST * STAGE_BYTES > 2 * TILE * TILE ? NST * STAGE_BYTES
+                                                             : 2 * TILE * TILE;  // 128 KiB
+constexpr int DMA_PER_TILE = TILE_BYTES / 1024 / 4;   // 16-byte x 64-lane loads per wave
+constexpr int DMA_PER_STAGE = 2 * DMA_PER_TILE;
+static_assert(LDS_MAIN >= 2 * TILE * TILE, "LDS must also hold a 256 x 256 bf16 output tile");
+static_assert(LDS_MAIN <= 128 * 1024, "LDS budget");
+constexpr uint32_t OOB_OFFSET = 0x80000000u;  // beyond every descriptor's num_records
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
-// LDS tile addressing: row r holds 64 bf16 of K (8 chunks of 16 bytes).  Chunk c
-// of row r lives at chunk position c ^ swz(r).  swz mixes the low and the next
-// three row bits so that both 8 consecutive rows (MFMA fragment reads) and rows
-// 8 apart (transposed staging writes) fall on distinct chunk positions.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int r, int c) { return (r << 7) + ((c ^ swz(r)) << 4); }
-
-// Workgroup id -> tile coordinates.  Workgroups are handed to the 8 XCDs round
-// robin, so id b runs on XCD b % 8.  The first step renumbers ids so that each
-// XCD receives a contiguous range of logical ids; the second walks logical ids
-// in groups of `group_m` tile rows, tile row fastest, so the ~32 workgroups
-// resident on one XCD share a few operand tiles in that XCD's L2.
+// Tile coordinates.  Workgroups are handed to the 8 XCDs round robin, so id b runs
+// on XCD b % 8.  Ids are renumbered so each XCD receives a contiguous range of
+// logical ids, walked in groups of `group_m` tile rows (tile row fastest): the ~32
+// workgroups resident on one XCD then share a few operand tiles in its L2.
 __device__ __forceinline__ void tile_coords(int bid, int nblocks, int n_m, int n_n, int group_m,
                                             int& tm, int& tn) {
   const int per = nblocks >> 3;
@@ -71,164 +102,278 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int n_m, int n
 }
 
 // ---------------------------------------------------------------------------
-// Global -> register staging of one 256 x 64 operand tile (8 x 16 bytes per thread).
-//
-// KC (K contiguous): the operand is [rows][K] with leading dimension ld; the tile
-// is rows [0, 256) relative to `base`, K range [k0, k0 + 64).  Thread t loads
-// chunk ids t + 256 i: row id / 8, chunk id % 8 (8 threads read one 128-byte row
-// segment).  Rows >= nrows and chunks at or past K read as zero.
-//
-// MN (M/N contiguous): the operand is [K][cols] with leading dimension ld; the
-// tile is columns [0, 256) relative to `base`.  Thread t loads the 8 x 8 block of
-// K rows 8 (t / 32) + i and columns 8 (t % 32) + j; 32 threads read one 512-byte
-// row segment.  Columns >= ncols and K rows >= K read as zero.
-struct Stage {
-  u32x4 v[8];
+// One operand of the mainloop, as seen by a workgroup.
+//  K-contiguous (KC): `base` is element (row 0 of the tile, k = 0) of a [rows][K]
+//     matrix with leading dimension ld; `valid` rows of the tile exist.
+//  M/N-contiguous (MN): `base` is element (k = 0, column 0 of the tile) of a
+//     [K][cols] matrix with leading dimension ld; `valid` columns of the tile exist.
+// `kvalid` is the K extent that exists; `span` the number of elements from `base`
+// to the end of the underlying allocation (a bound for the buffer descriptor).
+struct TileSrc {
+  const uint16_t* base;
+  long ld;
+  int valid;
+  int kvalid;
+  long span;
+};
+
+// LDS layout of a KC tile: 256 rows of BKS bf16 (BKS / 8 chunks of 16 bytes);
+// chunk c of row r sits at chunk position c ^ kc_swz(r).  The 16 consecutive rows
+// one ds_read_b128 cycle serves land on distinct (bank-row, chunk) positions.
+constexpr int KC_ROW_BYTES = BKS * 2;
+constexpr int KC_CHUNKS = BKS / 8;
+__device__ __forceinline__ int kc_swz(int r) {
+  return KC_CHUNKS == 8 ? ((r ^ (r >> 3)) & 7) : ((r >> 2) & (KC_CHUNKS - 1));
+}
+
+// LDS layout of an MN tile: BKS K rows of 256 bf16 (16 blocks of 32 bytes); block b
+// of K row k sits at block position b ^ (k & 7).  The 4 consecutive K rows one
+// transposing read touches land on distinct blocks.
+
+// One 64-lane direct-to-LDS load: lane i's 16 bytes from byte offset voff of the
+// buffer go to LDS address lds_addr + 16 i.  Issued as inline assembly so that the
+// compiler does not treat the fragment reads of the other stages as dependent on
+// it; the mainloop waits for these loads itself (s_waitcnt vmcnt) before the
+// barrier that publishes a stage.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, long bytes) {
+  const unsigned long a = (unsigned long)base;
+  const uint32_t nrec = bytes <= 0 ? 0u : (bytes >= 0x7fffffffL ? 0x7fffffffu : (uint32_t)bytes);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
+  r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane((int)nrec);
+  r.w = (int)RSRC_WORD3;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
+  return (uint32_t)(uintptr_t)(LDS_AS const char*)p;
+}
+
+// Direct-to-LDS loads of one 256 x BKS operand tile for K offset k0.  The tile is
+// filled by 4 waves x DMA_PER_TILE loads; load j of wave w fills LDS bytes
+// [(w DMA_PER_TILE + j) KiB, + 1 KiB) of the tile, lane i the 16 bytes at i * 16.
+struct TileDma {
+  i32x4 rsrc;
+  uint32_t lds0;
 };
 
 template <bool KC>
-__device__ __forceinline__ void stage_load(Stage& s, const uint16_t* __restrict__ base, long ld,
-                                           int nrows_or_cols, int K, int k0) {
-  const int t = threadIdx.x;
-  if constexpr (KC) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int id = t + NTHREADS * i;
-      const int r = id >> 3, c = id & 7;
-      const int k = k0 + (c << 3);
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (r < nrows_or_cols && k < K)
-        val = *reinterpret_cast<const u32x4*>(base + (long)r * ld + k);
-      s.v[i] = val;
-    }
-  } else {
-    const int cb = t & 31, kb = t >> 5;
-    const int col = cb << 3;
-    const bool col_ok = col < nrows_or_cols;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = k0 + (kb << 3) + i;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (col_ok && k < K) val = *reinterpret_cast<const u32x4*>(base + (long)k * ld + col);
-      s.v[i] = val;
-    }
-  }
-}
-
-__device__ __forceinline__ unsigned pack_lo(unsigned a, unsigned b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ unsigned pack_hi(unsigned a, unsigned b) {
-  return (a >> 16) | (b & 0xffff0000u);
+__device__ __forceinline__ TileDma tile_dma(const TileSrc& s, int k0, const char* lds_tile) {
+  const long koff = KC ? (long)k0 : (long)k0 * s.ld;
+  return TileDma{make_rsrc(s.base + koff, (s.span - koff) * 2), lds_addr_of(lds_tile)};
 }
 
 template <bool KC>
-__device__ __forceinline__ void stage_store(const Stage& s, char* __restrict__ tile) {
-  const int t = threadIdx.x;
-  if constexpr (KC) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int id = t + NTHREADS * i;
-      *reinterpret_cast<u32x4*>(tile + lds_off(id >> 3, id & 7)) = s.v[i];
-    }
-  } else {
-    // s.v[i] holds K row i of the block (8 columns); write column j of the block
-    // as one 16-byte K chunk: element i of output j = element j of input i.
-    const int cb = t & 31, kb = t >> 5;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int w = j >> 1;
-      u32x4 o;
-      if ((j & 1) == 0) {
-        o.x = pack_lo(s.v[0][w], s.v[1][w]);
-        o.y = pack_lo(s.v[2][w], s.v[3][w]);
-        o.z = pack_lo(s.v[4][w], s.v[5][w]);
-        o.w = pack_lo(s.v[6][w], s.v[7][w]);
-      } else {
-        o.x = pack_hi(s.v[0][w], s.v[1][w]);
-        o.y = pack_hi(s.v[2][w], s.v[3][w]);
-        o.z = pack_hi(s.v[4][w], s.v[5][w]);
-        o.w = pack_hi(s.v[6][w], s.v[7][w]);
-      }
-      *reinterpret_cast<u32x4*>(tile + lds_off((cb << 3) + j, kb)) = o;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// The MFMA mainloop shared by every kernel.  The workgroup computes the 256 x 256
-// tile D = A B^T (A: 256 x K, B: 256 x K, both logically K-contiguous) as 4 waves
-// of WM x WN (wave w at rows (w / (256/WN)) * WM, columns (w % (256/WN)) * WN).
-// acc[mb][nb] is the 32 x 32 block at (32 mb, 32 nb) of the wave tile, in the
-// v_mfma_f32_32x32x16 layout: lane l, element e holds row 8 (e / 4) + 4 (l / 32)
-// + e % 4 and column l % 32.
-template <int WM, int WN>
-struct WaveTile {
-  static constexpr int MB = WM / 32;
-  static constexpr int NB = WN / 32;
-  static constexpr int WAVES_N = TILE / WN;
-  f32x16 acc[MB][NB];
-};
-
-template <bool A_KC, bool B_KC, int WM, int WN>
-__device__ __forceinline__ void mainloop(WaveTile<WM, WN>& wt, char* __restrict__ smem,
-                                         const uint16_t* __restrict__ A, long lda, int a_valid,
-                                         int a_kvalid,
-                                         const uint16_t* __restrict__ B, long ldb, int b_valid,
-                                         int b_kvalid, int K) {
-  using WT = WaveTile<WM, WN>;
+__device__ __forceinline__ void tile_dma_issue(const TileDma& d, const TileSrc& s, int k0, int j) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wr0 = (wave / WT::WAVES_N) * WM;
-  const int wc0 = (wave % WT::WAVES_N) * WN;
-#pragma unroll
-  for (int mb = 0; mb < WT::MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < WT::NB; ++nb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) wt.acc[mb][nb][e] = 0.f;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int blk = wave * DMA_PER_TILE + j;
+  const int G = blk * 64 + lane;  // 16-byte granule of the tile this lane fills
+  uint32_t voff;
+  if constexpr (KC) {
+    const int r = G / KC_CHUNKS;
+    const int c = (G % KC_CHUNKS) ^ kc_swz(r);
+    const bool ok = r < s.valid && k0 + 8 * c < s.kvalid;
+    voff = ok ? (uint32_t)(((long)r * s.ld + 8 * c) * 2) : OOB_OFFSET;
+  } else {
+    const int k = G >> 5;
+    const int q = (G & 31) ^ ((k & 7) << 1);
+    const bool ok = k0 + k < s.kvalid && 8 * q < s.valid;
+    voff = ok ? (uint32_t)(((long)k * s.ld + 8 * q) * 2) : OOB_OFFSET;
+  }
+  dma16(d.rsrc, voff, d.lds0 + blk * 1024);
+}
 
-  const int nk = (K + BK - 1) / BK;
-  Stage sa, sb;
-  stage_load<A_KC>(sa, A, lda, a_valid, a_kvalid, 0);
-  stage_load<B_KC>(sb, B, ldb, b_valid, b_kvalid, 0);
-  stage_store<A_KC>(sa, smem);
-  stage_store<B_KC>(sb, smem + TILE_BYTES);
+template <bool KC>
+__device__ __forceinline__ void load_tile_async(const TileSrc& s, int k0, const char* lds_tile) {
+  const TileDma d = tile_dma<KC>(s, k0, lds_tile);
+#pragma unroll
+  for (int j = 0; j < DMA_PER_TILE; ++j) tile_dma_issue<KC>(d, s, k0, j);
+}
+
+// The loads of one whole stage (A then B), issued piece by piece between MFMA groups.
+template <bool A_KC, bool B_KC>
+struct StageDma {
+  TileDma a, b;
+  const TileSrc* A;
+  const TileSrc* B;
+  int k0;
+  bool active;
+  __device__ __forceinline__ void issue_piece(int piece) {
+    constexpr int PER = (DMA_PER_STAGE + DMA_SPREAD - 1) / DMA_SPREAD;
+    if (!active) return;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int j = piece * PER + q;
+      if (j < DMA_PER_TILE)
+        tile_dma_issue<A_KC>(a, *A, k0, j);
+      else if (j < DMA_PER_STAGE)
+        tile_dma_issue<B_KC>(b, *B, k0, j - DMA_PER_TILE);
+    }
+  }
+};
+
+// MFMA fragment (8 consecutive K values 16 kk + 8 (lane / 32) + 0..7 of tile row or
+// column `idx0 + lane % 32`) from a KC tile.
+__device__ __forceinline__ bf16x8 frag_kc(const char* tile, int idx0, int kk, int lane) {
+  const int r = idx0 + (lane & 31);
+  const int c = 2 * kk + (lane >> 5);
+  return *reinterpret_cast<const bf16x8*>(tile + r * KC_ROW_BYTES + ((c ^ kc_swz(r)) << 4));
+}
+
+// The same fragment from an MN tile, with two transposing reads.  In each 16-lane
+// group, lane i reads 4 columns (4 (i % 4) .. + 3 of the group's 16) of K row i / 4;
+// the read hands lane j of the group column j of those 4 K rows.
+__device__ __forceinline__ bf16x8 frag_mn(const char* tile, int idx0, int kk, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int c0 = idx0 + 16 * (g & 1) + 4 * (i & 3);
+  i16x4 h[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int k = 16 * kk + 8 * (g >> 1) + 4 * hh + (i >> 2);
+    const int off = (k << 9) + ((((c0 >> 4) ^ (k & 7))) << 5) + ((c0 & 15) << 1);
+    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(tile + off));
+  }
+  const i16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <bool KC>
+__device__ __forceinline__ bf16x8 frag(const char* tile, int idx0, int kk, int lane) {
+  if constexpr (KC)
+    return frag_kc(tile, idx0, kk, lane);
+  else
+    return frag_mn(tile, idx0, kk, lane);
+}
+
+template <bool A_KC, bool B_KC>
+__device__ __forceinline__ void read_frags(bf16x8 (&af)[4], bf16x8 (&bfr)[4], const char* stage,
+                                           int wr0, int wc0, int kk, int lane) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) af[mb] = frag<A_KC>(stage, wr0 + 32 * mb, kk, lane);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) bfr[nb] = frag<B_KC>(stage + TILE_BYTES, wc0 + 32 * nb, kk, lane);
+}
+
+__device__ __forceinline__ void mfma_4x4(f32x16 (&acc)[4][4], const bf16x8 (&af)[4],
+                                         const bf16x8 (&bfr)[4]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+}
+
+// The BKS / 16 MFMA sub-steps of one stage.  With FRAG_PREFETCH the fragments of
+// sub-step kk + 1 are read (into the other register set) before the 16 MFMAs of
+// sub-step kk are issued, so LDS latency hides under matrix work; the loads of a
+// later stage are issued in DMA_SPREAD pieces between the MFMA groups, so the
+// address FIFO never holds up the matrix pipe for long.
+template <bool A_KC, bool B_KC>
+__device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const char* stage, int wr0,
+                                              int wc0, int lane, StageDma<A_KC, B_KC>& dma) {
+  constexpr int KK = BKS / 16;
+  static_assert(DMA_SPREAD >= 1 && DMA_SPREAD <= KK, "DMA_SPREAD must be 1 .. BKS / 16");
+  if constexpr (FRAG_PREFETCH) {
+    bf16x8 af[2][4], bfr[2][4];
+    read_frags<A_KC, B_KC>(af[0], bfr[0], stage, wr0, wc0, 0, lane);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK)
+        read_frags<A_KC, B_KC>(af[(kk + 1) & 1], bfr[(kk + 1) & 1], stage, wr0, wc0, kk + 1, lane);
+      if (kk < DMA_SPREAD) dma.issue_piece(kk);
+      mfma_4x4(acc, af[kk & 1], bfr[kk & 1]);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      bf16x8 af[4], bfr[4];
+      read_frags<A_KC, B_KC>(af, bfr, stage, wr0, wc0, kk, lane);
+      if (kk < DMA_SPREAD) dma.issue_piece(kk);
+      mfma_4x4(acc, af, bfr);
+    }
+  }
+}
+
+// s_waitcnt until at most n of this wave's vector-memory operations are outstanding
+// (expcnt and lgkmcnt left unconstrained).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// Wait until the loads of the stage after the one just computed have landed, given
+// that `ahead` later stages (0 .. NST - 2) may still be in flight.
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if constexpr (NST >= 4) {
+    if (ahead >= 2) { wait_vmcnt<2 * DMA_PER_STAGE>(); return; }
+  }
+  if constexpr (NST >= 3) {
+    if (ahead >= 1) { wait_vmcnt<DMA_PER_STAGE>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+// The MFMA mainloop shared by every kernel: D = A B^T over K for the workgroup's
+// 256 x 256 tile, as 4 waves of 128 x 128 (wave w at rows 128 (w / 2), columns
+// 128 (w % 2)).  acc[mb][nb] is the 32 x 32 block at (32 mb, 32 nb) of the wave
+// tile in the v_mfma_f32_32x32x16 layout: lane l, element e holds row
+// 8 (e / 4) + 4 (l / 32) + e % 4 and column l % 32.
+//
+// Pipeline: NST LDS stages; at step kt the loads of step kt + NST - 1 are issued
+// into the stage computed at step kt - 1 (released by the barrier that ended that
+// step), the fragments of stage kt are read and multiplied, then the wave waits for
+// its own loads of step kt + 1 and the barrier publishes that stage to all waves.
+template <bool A_KC, bool B_KC>
+__device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, const TileSrc& A,
+                                         const TileSrc& B, int K) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
+
+  const int nk = (K + BKS - 1) / BKS;
+  // K step processed at loop position i: (kt0 + i) mod nk
+  const int kt0 = STAGGER > 1 ? (int)(((long)(blockIdx.x % (STAGGER > 1 ? STAGGER : 1)) * nk) / (STAGGER > 1 ? STAGGER : 1)) : 0;
+  auto kstep = [&](int i) { const int t = kt0 + i; return t >= nk ? t - nk : t; };
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) {
+    if (st < nk) {
+      load_tile_async<A_KC>(A, kstep(st) * BKS, smem + st * STAGE_BYTES);
+      load_tile_async<B_KC>(B, kstep(st) * BKS, smem + st * STAGE_BYTES + TILE_BYTES);
+    }
+  }
+  wait_stage(min(nk - 1, NST - 2));
   __syncthreads();
-
-  const int frag_row = lane & 31;
-  const int frag_half = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * STAGE_BYTES;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      stage_load<A_KC>(sa, A, lda, a_valid, a_kvalid, (kt + 1) * BK);
-      stage_load<B_KC>(sb, B, ldb, b_valid, b_kvalid, (kt + 1) * BK);
+    const int ahead_kt = kt + NST - 1;
+    char* dst = smem + (ahead_kt % NST) * STAGE_BYTES;
+    StageDma<A_KC, B_KC> dma;
+    dma.active = ahead_kt < nk;
+    dma.A = &A;
+    dma.B = &B;
+    dma.k0 = kstep(ahead_kt < nk ? ahead_kt : 0) * BKS;
+    if (dma.active) {
+      dma.a = tile_dma<A_KC>(A, dma.k0, dst);
+      dma.b = tile_dma<B_KC>(B, dma.k0, dst + TILE_BYTES);
     }
-    const char* As = cur;
-    const char* Bs = cur + TILE_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int chunk = 2 * kk + frag_half;
-      bf16x8 af[WT::MB], bfr[WT::NB];
-#pragma unroll
-      for (int mb = 0; mb < WT::MB; ++mb)
-        af[mb] = *reinterpret_cast<const bf16x8*>(As + lds_off(wr0 + 32 * mb + frag_row, chunk));
-#pragma unroll
-      for (int nb = 0; nb < WT::NB; ++nb)
-        bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(wc0 + 32 * nb + frag_row, chunk));
-#pragma unroll
-      for (int mb = 0; mb < WT::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < WT::NB; ++nb)
-          wt.acc[mb][nb] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], wt.acc[mb][nb], 0, 0, 0);
-    }
-    if (more) {
-      char* nxt = smem + ((kt + 1) & 1) * STAGE_BYTES;
-      stage_store<A_KC>(sa, nxt);
-      stage_store<B_KC>(sb, nxt + TILE_BYTES);
-    }
+    compute_stage<A_KC, B_KC>(acc, smem + (kt % NST) * STAGE_BYTES, wr0, wc0, lane, dma);
+    // stages issued after step kt + 1 that may still be in flight
+    wait_stage(min(max(nk - 1 - (kt + 1), 0), NST - 2));
     __syncthreads();
   }
 }
@@ -240,55 +385,88 @@ __device__ __forceinline__ int acc_row(int lane, int e) {
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
-// Reduce-scatter over the 32 lanes that share a half-wave: on entry every lane
-// holds 32 values v[q]; on exit lane l holds in v[0] the reduction over those
-// lanes of v[l % 32].
-template <class Op>
-__device__ __forceinline__ void reduce_scatter32(float (&v)[32], int lane, Op op) {
+// Reduce-scatter over the 32 lanes of a half-wave.  v holds 32 P values, entry
+// 32 p + j being slot j of group p.  On exit v[32 p] holds the reduction over the
+// half-wave of slot (lane % 32) of group p.
+template <int P, class Op>
+__device__ __forceinline__ void reduce_scatter32(float (&v)[32 * P], int lane, Op op) {
 #pragma unroll
   for (int s = 16; s >= 1; s >>= 1) {
     const bool upper = (lane & s) != 0;
 #pragma unroll
-    for (int i = 0; i < s; ++i) {
-      const float send = upper ? v[i] : v[i + s];
-      const float keep = upper ? v[i + s] : v[i];
-      v[i] = op(keep, shfl_xor(send, s));
-    }
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int i = 0; i < s; ++i) {
+        const float lo = v[32 * p + i], hi = v[32 * p + i + s];
+        const float send = upper ? lo : hi;
+        const float keep = upper ? hi : lo;
+        v[32 * p + i] = op(keep, shfl_xor(send, s));
+      }
   }
 }
 
-// Inverse of reduce_scatter32's distribution: lane l holds v[0] for slot l % 32;
-// on exit every lane holds all 32 slots of its half-wave.
-__device__ __forceinline__ void all_gather32(float (&v)[32], int lane) {
+// Inverse distribution: v[32 p] holds slot (lane % 32) of group p; on exit every
+// lane holds all 32 slots of every group.
+template <int P>
+__device__ __forceinline__ void all_gather32(float (&v)[32 * P], int lane) {
 #pragma unroll
   for (int s = 1; s <= 16; s <<= 1) {
     const bool upper = (lane & s) != 0;
 #pragma unroll
-    for (int i = 0; i < s; ++i) {
-      const float other = shfl_xor(v[i], s);
-      const float lo = upper ? other : v[i];
-      const float hi = upper ? v[i] : other;
-      v[i] = lo;
-      v[i + s] = hi;
-    }
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int i = 0; i < s; ++i) {
+        const float mine = v[32 * p + i];
+        const float other = shfl_xor(mine, s);
+        v[32 * p + i] = upper ? other : mine;
+        v[32 * p + i + s] = upper ? mine : other;
+      }
   }
 }
 
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  unsigned u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Copy a 256 x 256 bf16 tile staged row-major in LDS (512 bytes per row; rows
+// 0..127 in `lo`, 128..255 in `hi`) to rows [row0, row0 + nrows) and columns
+// [col0, col0 + ncols) of a row-major matrix with leading dimension ld; ncols is a
+// multiple of 8.  16-byte stores, 32 lanes per row.
+__device__ __forceinline__ void store_tile_bf16(const char* lo, const char* hi, uint16_t* dst,
+                                                long ld, int nrows, int ncols) {
+  const int t = threadIdx.x;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int G = it * NTHREADS + t;
+    const int r = G >> 5, c = (G & 31) << 3;
+    const char* src = (r < 128 ? lo : hi) + ((r & 127) << 9) + (c << 1);
+    if (r < nrows && c < ncols)
+      *reinterpret_cast<u32x4*>(dst + (long)r * ld + c) = *reinterpret_cast<const u32x4*>(src);
+  }
+}
+
+// Staging slot of tile element (rl, cl) for store_tile_bf16.
+__device__ __forceinline__ uint16_t* out_slot(char* lo, char* hi, int rl, int cl) {
+  return reinterpret_cast<uint16_t*>((rl < 128 ? lo : hi) + ((rl & 127) << 9) + (cl << 1));
+}
+
 // ---------------------------------------------------------------------------
-// Forward tile kernel.  Wave tile 64 x 256 (4 waves stacked along M), so each wave
-// owns complete rows of the workgroup's V tile and reduces them on its own.
-// Lane l holds, for row slot q = 16 mb + e (mb < 2, e < 16), the 8 columns
-// 32 nb + l % 32 of wave row 32 mb + acc_row(l, e).
+// Forward tile kernel.  Per wave: lane l holds, for row slot q = 16 mb + e (64 of
+// them), the 4 columns 32 nb + l % 32 of its wave tile.  The wave reduces its 128
+// columns per row (max, then shifted sums); the two waves sharing rows are merged
+// through LDS and thread t writes the partials of tile row t.
 template <bool ENT>
 __global__ __launch_bounds__(NTHREADS) void fwd_tile_kernel(FwdTileArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_MAIN];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_MAIN];
   __shared__ int t_local[TILE];
   int mt, vt;
   tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, 8, mt, vt);
   const int row0 = mt * TILE, col0 = vt * TILE;
   const int tid = threadIdx.x;
   {
-    // target column relative to this tile, or -1 if not a valid target in it
+    // target column relative to this tile, or -1 if no valid target lies in it
     const int r = row0 + tid;
     int tl = -1;
     if (r < p.M) {
@@ -299,69 +477,69 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tile_kernel(FwdTileArgs p) {
     t_local[tid] = tl;
   }
 
-  WaveTile<64, 256> wt;
-  mainloop<true, true, 64, 256>(wt, smem, p.X + (long)row0 * p.H, p.H, p.M - row0, p.H,
-                                p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, p.H);
+  f32x16 acc[4][4];
+  const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, (long)(p.M - row0) * p.H};
+  const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, (long)(p.V - col0) * p.H};
+  mainloop<true, true>(acc, smem, A, B, p.H);
 
   const int lane = tid & 63, wave = tid >> 6;
-  const int wr0 = wave * 64;
+  const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
   const int lc = lane & 31;
   const float c1 = p.scale * LOG2E;  // logits in log2 units: z2 = acc * c1
-
-  // scale into log2 units; mask columns past V (only the last V tile has any)
   const bool ragged = col0 + TILE > p.V;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const bool colok = !ragged || (col0 + 32 * nb + lc < p.V);
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        wt.acc[mb][nb][e] = colok ? wt.acc[mb][nb][e] * c1 : -INFINITY;
-    }
 
-  // target logit: the unique lane holding column t[row] writes z[row, t] = z2 / log2(e)
+  // scale into log2 units; columns past V become -inf (only the last V tile has any)
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int nb = 0; nb < 4; ++nb) {
+    const bool colok = !ragged || (col0 + wc0 + 32 * nb + lc < p.V);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mb][nb][e] = colok ? acc[mb][nb][e] * c1 : -INFINITY;
+  }
+
+  // target logit: the unique lane holding column t[row] writes z[row, t]
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int rl = wr0 + 32 * mb + acc_row(lane, e);
-      const int d = t_local[rl] - lc;
-      if (d >= 0 && (d & 31) == 0) {
+      const int d = t_local[rl] - wc0 - lc;
+      if (d >= 0 && d < 128 && (d & 31) == 0) {
         float z = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-          if ((d >> 5) == nb) z = wt.acc[mb][nb][e];
+        for (int nb = 0; nb < 4; ++nb)
+          if ((d >> 5) == nb) z = acc[mb][nb][e];
         p.zt[row0 + rl] = z * LN2;
       }
     }
 
-  // tile row maxima
-  float mx[32];
+  // row maxima of the wave's 128 columns
+  float mx[64];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float m = wt.acc[mb][0][e];
-#pragma unroll
-      for (int nb = 1; nb < 8; ++nb) m = fmaxf(m, wt.acc[mb][nb][e]);
+      float m = fmaxf(fmaxf(acc[mb][0][e], acc[mb][1][e]), fmaxf(acc[mb][2][e], acc[mb][3][e]));
       mx[16 * mb + e] = m;
     }
-  reduce_scatter32(mx, lane, [](float a, float b) { return fmaxf(a, b); });
-  const float my_max = mx[0];
-  all_gather32(mx, lane);
+  reduce_scatter32<2>(mx, lane, [](float a, float b) { return fmaxf(a, b); });
+  const float my_max0 = mx[0], my_max1 = mx[32];
+  all_gather32<2>(mx, lane);
 
-  // shifted sums: s = sum exp2(z2 - m2), u = sum exp2(z2 - m2) (z2 - m2)
-  float sv[32], uv[32];
+  // shifted sums s = sum exp2(z2 - m2) and u = sum exp2(z2 - m2) (z2 - m2); a row
+  // with no column in this wave (ragged tile) keeps m = -inf, s = u = 0
+  float sv[64], uv[ENT ? 64 : 1];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float m = mx[16 * mb + e];
+      const float mref = m == -INFINITY ? 0.f : m;
       float s = 0.f, u = 0.f;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const float d = wt.acc[mb][nb][e] - m;
+      for (int nb = 0; nb < 4; ++nb) {
+        const float d = acc[mb][nb][e] - mref;
         const float pe = __builtin_amdgcn_exp2f(d);
         s += pe;
         if constexpr (ENT) u += pe * fmaxf(d, -3.0e38f);
@@ -369,16 +547,40 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tile_kernel(FwdTileArgs p) {
       sv[16 * mb + e] = s;
       if constexpr (ENT) uv[16 * mb + e] = u;
     }
-  reduce_scatter32(sv, lane, [](float a, float b) { return a + b; });
-  if constexpr (ENT) reduce_scatter32(uv, lane, [](float a, float b) { return a + b; });
+  reduce_scatter32<2>(sv, lane, [](float a, float b) { return a + b; });
+  if constexpr (ENT) reduce_scatter32<2>(uv, lane, [](float a, float b) { return a + b; });
 
-  // lane l now owns row slot q = l % 32
-  const int q = lc;
-  const int row = row0 + wr0 + 32 * (q >> 4) + acc_row(lane, q & 15);
-  const long off = (long)vt * p.Mpad + row;
-  p.part_m[off] = my_max * LN2;
-  p.part_s[off] = sv[0];
-  if constexpr (ENT) p.part_u[off] = uv[0] * LN2;
+  // merge the two column halves of each row through LDS (the stages are free now)
+  float* comb = reinterpret_cast<float*>(smem);  // [2 halves][3 stats][256 rows]
+  const int wn = wave & 1;
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    const int j = lc;
+    const int mb = 2 * pp + (j >> 4), e = j & 15;
+    const int rl = wr0 + 32 * mb + acc_row(lane, e);
+    comb[(wn * 3 + 0) * TILE + rl] = (pp ? my_max1 : my_max0) * LN2;
+    comb[(wn * 3 + 1) * TILE + rl] = sv[32 * pp];
+    comb[(wn * 3 + 2) * TILE + rl] = ENT ? uv[ENT ? 32 * pp : 0] * LN2 : 0.f;
+  }
+  __syncthreads();
+  {
+    const float m0 = comb[0 * TILE + tid], s0 = comb[1 * TILE + tid], u0 = comb[2 * TILE + tid];
+    const float m1 = comb[3 * TILE + tid], s1 = comb[4 * TILE + tid], u1 = comb[5 * TILE + tid];
+    float m, s, u;
+    if (s1 == 0.f) {
+      m = m0; s = s0; u = u0;
+    } else {
+      m = fmaxf(m0, m1);
+      const float d0 = m0 - m, d1 = m1 - m;
+      const float a0 = __expf(d0), a1 = __expf(d1);
+      s = s0 * a0 + s1 * a1;
+      u = a0 * (u0 + d0 * s0) + a1 * (u1 + d1 * s1);
+    }
+    const long off = (long)vt * p.Mpad + row0 + tid;
+    p.part_m[off] = m;
+    p.part_s[off] = s;
+    if constexpr (ENT) p.part_u[off] = u;
+  }
 }
 
 // Merge of the per-tile partials of each row: m* = max m_j, S = sum s_j e^(m_j - m*),
@@ -408,18 +610,12 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdMergeArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Backward d-logits for one vocabulary chunk: dzs = scale * dz in bf16, written
-// to a [Mpad, ldz] buffer (chunk column j = vocabulary column vbase + j).  Columns
-// past V and rows past M are written as zero.
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  unsigned u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
+// Backward d-logits for one vocabulary chunk: dzs = scale * dz in bf16, written to
+// a [Mpad, ldz] buffer (chunk column j = vocabulary column vbase + j).  Columns past
+// V and rows past M are written as zero.
 template <bool ENTGRAD>
 __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_MAIN];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_MAIN];
   __shared__ float r_lse2[TILE], r_a[TILE], r_b[TILE], r_E[TILE];
   __shared__ int t_local[TILE];
   int mt, vt;
@@ -450,48 +646,51 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
     t_local[tid] = tl;
   }
 
-  WaveTile<64, 256> wt;
-  mainloop<true, true, 64, 256>(wt, smem, p.X + (long)row0 * p.H, p.H, p.M - row0, p.H,
-                                p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, p.H);
+  f32x16 acc[4][4];
+  const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, (long)(p.M - row0) * p.H};
+  const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, (long)(p.V - col0) * p.H};
+  mainloop<true, true>(acc, smem, A, B, p.H);
 
   const int lane = tid & 63, wave = tid >> 6;
-  const int wr0 = wave * 64;
+  const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
   const int lc = lane & 31;
   const float c1 = p.scale * LOG2E;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int rl = wr0 + 32 * mb + acc_row(lane, e);
       const float lse2 = r_lse2[rl], a = r_a[rl], b = r_b[rl], E = r_E[rl];
       const int tl = t_local[rl];
-      uint16_t* out = p.dz + (long)(row0 + rl) * p.ldz + ccol0 + lc;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int cl = 32 * nb + lc;
-        const float acc = wt.acc[mb][nb][e];
-        const float pr = __builtin_amdgcn_exp2f(acc * c1 - lse2);
+      for (int nb = 0; nb < 4; ++nb) {
+        const int cl = wc0 + 32 * nb + lc;
+        const float av = acc[mb][nb][e];
+        const float pr = __builtin_amdgcn_exp2f(av * c1 - lse2);
         float d = (cl == tl ? a : 0.f) - a * pr;
-        if constexpr (ENTGRAD) d += b * pr * (E - acc * p.scale);
+        if constexpr (ENTGRAD) d += b * pr * (E - av * p.scale);
         d *= p.scale;
         if (col0 + cl >= p.V) d = 0.f;
-        out[32 * nb] = f32_to_bf16_rne(d);
+        *out_slot(smem, smem + 128 * 512, rl, cl) = f32_to_bf16_rne(d);
       }
     }
+  __syncthreads();
+  store_tile_bf16(smem, smem + 128 * 512, p.dz + (long)row0 * p.ldz + ccol0, p.ldz, TILE, TILE);
 }
 
 // ---------------------------------------------------------------------------
-// Plain GEMMs of the backward, 4 waves of 128 x 128.
-// dW[vbase + i, h] = sum_m dzs[m, i] X[m, h]    (A = dzs^T: MN-contiguous; B = X^T: MN-contiguous)
+// dW[vbase + i, h] = sum_m dzs[m, i] X[m, h]: A = dzs^T (MN), B = X^T (MN), K = Mpad.
 __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_MAIN];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_MAIN];
   int ti, th;
   tile_coords(blockIdx.x, gridDim.x, p.n_i, p.n_h, 8, ti, th);
   const int i0 = ti * TILE, h0 = th * TILE;
-  WaveTile<128, 128> wt;
-  // K runs over the Mpad rows of dzs (rows past M hold zeros); X has only M rows.
-  mainloop<false, false, 128, 128>(wt, smem, p.dz + i0, p.ldz, p.chunk_cols - i0, p.Mpad,
-                                   p.X + h0, p.H, p.H - h0, p.M, p.Mpad);
+  f32x16 acc[4][4];
+  // dzs has Mpad rows (rows past M hold zeros); X has only M rows.
+  const TileSrc A{p.dz + i0, p.ldz, p.chunk_cols - i0, p.Mpad, (long)p.Mpad * p.ldz - i0};
+  const TileSrc B{p.X + h0, p.H, p.H - h0, p.M, (long)p.M * p.H - h0};
+  mainloop<false, false>(acc, smem, A, B, p.Mpad);
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
   const int lc = lane & 31;
@@ -499,52 +698,67 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int i = i0 + wr0 + 32 * mb + acc_row(lane, e);
-      const int v = p.vbase + i;
-      if (i >= p.chunk_cols || v >= p.V) continue;
-      uint16_t* out = p.dW + (long)v * p.H;
+      const int rl = wr0 + 32 * mb + acc_row(lane, e);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int h = h0 + wc0 + 32 * nb + lc;
-        if (h < p.H) out[h] = f32_to_bf16_rne(wt.acc[mb][nb][e]);
-      }
+      for (int nb = 0; nb < 4; ++nb)
+        *out_slot(smem, smem + 128 * 512, rl, wc0 + 32 * nb + lc) = f32_to_bf16_rne(acc[mb][nb][e]);
     }
+  __syncthreads();
+  const int rows = min(min(TILE, p.chunk_cols - i0), p.V - (p.vbase + i0));
+  store_tile_bf16(smem, smem + 128 * 512, p.dW + (long)(p.vbase + i0) * p.H + h0, p.H, rows, p.H - h0);
 }
 
-// dX[m, h] (+)= sum_i dzs[m, i] W[vbase + i, h]  (A = dzs: K-contiguous; B = W^T: MN-contiguous)
+// dX[m, h] (+)= sum_i dzs[m, i] W[vbase + i, h]: A = dzs (KC), B = W^T (MN), K = kcols.
 // mode 0: write bf16; 1: write fp32 accumulator; 2: accumulate fp32; 3: accumulate and write bf16.
 __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_MAIN];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_MAIN];
   int tm, th;
   tile_coords(blockIdx.x, gridDim.x, p.n_m, p.n_h, 8, tm, th);
   const int m0 = tm * TILE, h0 = th * TILE;
-  WaveTile<128, 128> wt;
-  // K runs over the kcols (padded) columns of the chunk; W has V - vbase rows left.
-  mainloop<true, false, 128, 128>(wt, smem, p.dz + (long)m0 * p.ldz, p.ldz, p.M - m0, p.kcols,
-                                  p.W + (long)p.vbase * p.H + h0, p.H, p.H - h0, p.V - p.vbase,
-                                  p.kcols);
+  f32x16 acc[4][4];
+  // the chunk's kcols (padded) columns of dzs; W has V - vbase rows left
+  const TileSrc A{p.dz + (long)m0 * p.ldz, p.ldz, p.M - m0, p.kcols,
+                  (long)(p.M - m0) * p.ldz};
+  const TileSrc B{p.W + (long)p.vbase * p.H + h0, p.H, p.H - h0, p.V - p.vbase,
+                  (long)(p.V - p.vbase) * p.H - h0};
+  mainloop<true, false>(acc, smem, A, B, p.kcols);
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
   const int lc = lane & 31;
+  if (p.mode == 0 || p.mode == 3) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int m = m0 + wr0 + 32 * mb + acc_row(lane, e);
-      if (m >= p.M) continue;
+      for (int e = 0; e < 16; ++e) {
+        const int rl = wr0 + 32 * mb + acc_row(lane, e);
+        const int m = m0 + rl;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int h = h0 + wc0 + 32 * nb + lc;
-        if (h >= p.H) continue;
-        const long o = (long)m * p.H + h;
-        float v = wt.acc[mb][nb][e];
-        if (p.mode >= 2) v += p.acc[o];
-        if (p.mode == 1 || p.mode == 2)
-          p.acc[o] = v;
-        else
-          p.dX[o] = f32_to_bf16_rne(v);
+        for (int nb = 0; nb < 4; ++nb) {
+          const int cl = wc0 + 32 * nb + lc;
+          float v = acc[mb][nb][e];
+          if (p.mode == 3 && m < p.M && h0 + cl < p.H) v += p.acc[(long)m * p.H + h0 + cl];
+          *out_slot(smem, smem + 128 * 512, rl, cl) = f32_to_bf16_rne(v);
+        }
       }
-    }
+    __syncthreads();
+    store_tile_bf16(smem, smem + 128 * 512, p.dX + (long)m0 * p.H + h0, p.H, p.M - m0, p.H - h0);
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wr0 + 32 * mb + acc_row(lane, e);
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int h = h0 + wc0 + 32 * nb + lc;
+          if (h >= p.H) continue;
+          const long o = (long)m * p.H + h;
+          p.acc[o] = p.mode == 2 ? p.acc[o] + acc[mb][nb][e] : acc[mb][nb][e];
+        }
+      }
+  }
 }
 
 __global__ void fill_u16_kernel(uint16_t* __restrict__ p, long n) {
@@ -555,10 +769,8 @@ __global__ void fill_u16_kernel(uint16_t* __restrict__ p, long n) {
 
 // ---------------------------------------------------------------------------
 // Launchers (host side).  Each returns the hipGetLastError() of its launch.
-static unsigned nblocks_of(long n) { return (unsigned)n; }
-
 hipError_t launch_fwd_tile(const FwdTileArgs& a, bool ent, hipStream_t s) {
-  const unsigned g = nblocks_of((long)a.n_mt * a.n_vt);
+  const unsigned g = (unsigned)((long)a.n_mt * a.n_vt);
   if (ent)
     fwd_tile_kernel<true><<<g, NTHREADS, 0, s>>>(a);
   else
@@ -576,7 +788,7 @@ hipError_t launch_fwd_merge(const FwdMergeArgs& a, bool ent, hipStream_t s) {
 }
 
 hipError_t launch_dlogits(const DlogitsArgs& a, bool entgrad, hipStream_t s) {
-  const unsigned g = nblocks_of((long)a.n_mt * a.n_vt);
+  const unsigned g = (unsigned)((long)a.n_mt * a.n_vt);
   if (entgrad)
     bwd_dlogits_kernel<true><<<g, NTHREADS, 0, s>>>(a);
   else
@@ -585,12 +797,12 @@ hipError_t launch_dlogits(const DlogitsArgs& a, bool entgrad, hipStream_t s) {
 }
 
 hipError_t launch_gemm_dw(const GemmDwArgs& a, hipStream_t s) {
-  gemm_dw_kernel<<<nblocks_of((long)a.n_i * a.n_h), NTHREADS, 0, s>>>(a);
+  gemm_dw_kernel<<<(unsigned)((long)a.n_i * a.n_h), NTHREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_dx(const GemmDxArgs& a, hipStream_t s) {
-  gemm_dx_kernel<<<nblocks_of((long)a.n_m * a.n_h), NTHREADS, 0, s>>>(a);
+  gemm_dx_kernel<<<(unsigned)((long)a.n_m * a.n_h), NTHREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 
