@@ -161,43 +161,77 @@ __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
 // Direct-to-LDS loads of one 256 x BKS operand tile for K offset k0.  The tile is
 // filled by 4 waves x DMA_PER_TILE loads; load j of wave w fills LDS bytes
 // [(w DMA_PER_TILE + j) KiB, + 1 KiB) of the tile, lane i the 16 bytes at i * 16.
+// Each lane's byte offsets relative to the K step's base address do not change from
+// step to step, so they are computed once (DmaPlan); only a K step that runs past
+// the end of K re-derives the mask (a uniform branch, taken at most once).
+template <bool KC>
+struct DmaPlan {
+  uint32_t voff[DMA_PER_TILE];
+  int wave;
+
+  __device__ __forceinline__ void granule(int j, int& a, int& b) const {
+    const int lane = threadIdx.x & 63;
+    const int G = (wave * DMA_PER_TILE + j) * 64 + lane;  // 16-byte granule of the tile
+    if constexpr (KC) {
+      a = G / KC_CHUNKS;                              // tile row
+      b = (G % KC_CHUNKS) ^ kc_swz(a);                // 16-byte chunk of K in the row
+    } else {
+      a = G >> 5;                                     // K row
+      b = (G & 31) ^ ((a & 7) << 1);                  // 16-byte chunk of columns
+    }
+  }
+
+  __device__ __forceinline__ void init(const TileSrc& s, int wave_id) {
+    wave = wave_id;
+#pragma unroll
+    for (int j = 0; j < DMA_PER_TILE; ++j) {
+      int a, b;
+      granule(j, a, b);
+      const bool ok = KC ? a < s.valid : 8 * b < s.valid;
+      voff[j] = ok ? (uint32_t)(((long)a * s.ld + 8 * b) * 2) : OOB_OFFSET;
+    }
+  }
+
+  // offset of load j for the K step at k0; `tail` (uniform) says the step runs past kvalid
+  __device__ __forceinline__ uint32_t at(const TileSrc& s, int k0, int j, bool tail) const {
+    uint32_t v = voff[j];
+    if (tail) {
+      int a, b;
+      granule(j, a, b);
+      const int k = KC ? k0 + 8 * b : k0 + a;
+      if (k >= s.kvalid) v = OOB_OFFSET;
+    }
+    return v;
+  }
+};
+
 struct TileDma {
   i32x4 rsrc;
-  uint32_t lds0;
+  uint32_t lds0;  // LDS byte address of this wave's first 1 KiB block of the tile
+  bool tail;      // the K step runs past kvalid
 };
 
 template <bool KC>
-__device__ __forceinline__ TileDma tile_dma(const TileSrc& s, int k0, const char* lds_tile) {
+__device__ __forceinline__ TileDma tile_dma(const TileSrc& s, const DmaPlan<KC>& plan, int k0,
+                                            const char* lds_tile) {
   const long koff = KC ? (long)k0 : (long)k0 * s.ld;
-  return TileDma{make_rsrc(s.base + koff, (s.span - koff) * 2), lds_addr_of(lds_tile)};
+  return TileDma{make_rsrc(s.base + koff, (s.span - koff) * 2),
+                 lds_addr_of(lds_tile) + (uint32_t)(plan.wave * DMA_PER_TILE * 1024),
+                 k0 + BKS > s.kvalid};
 }
 
 template <bool KC>
-__device__ __forceinline__ void tile_dma_issue(const TileDma& d, const TileSrc& s, int k0, int j) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int blk = wave * DMA_PER_TILE + j;
-  const int G = blk * 64 + lane;  // 16-byte granule of the tile this lane fills
-  uint32_t voff;
-  if constexpr (KC) {
-    const int r = G / KC_CHUNKS;
-    const int c = (G % KC_CHUNKS) ^ kc_swz(r);
-    const bool ok = r < s.valid && k0 + 8 * c < s.kvalid;
-    voff = ok ? (uint32_t)(((long)r * s.ld + 8 * c) * 2) : OOB_OFFSET;
-  } else {
-    const int k = G >> 5;
-    const int q = (G & 31) ^ ((k & 7) << 1);
-    const bool ok = k0 + k < s.kvalid && 8 * q < s.valid;
-    voff = ok ? (uint32_t)(((long)k * s.ld + 8 * q) * 2) : OOB_OFFSET;
-  }
-  dma16(d.rsrc, voff, d.lds0 + blk * 1024);
+__device__ __forceinline__ void tile_dma_issue(const TileDma& d, const DmaPlan<KC>& plan,
+                                               const TileSrc& s, int k0, int j) {
+  dma16(d.rsrc, plan.at(s, k0, j, d.tail), d.lds0 + j * 1024);
 }
 
 template <bool KC>
-__device__ __forceinline__ void load_tile_async(const TileSrc& s, int k0, const char* lds_tile) {
-  const TileDma d = tile_dma<KC>(s, k0, lds_tile);
+__device__ __forceinline__ void load_tile_async(const TileSrc& s, const DmaPlan<KC>& plan, int k0,
+                                                const char* lds_tile) {
+  const TileDma d = tile_dma<KC>(s, plan, k0, lds_tile);
 #pragma unroll
-  for (int j = 0; j < DMA_PER_TILE; ++j) tile_dma_issue<KC>(d, s, k0, j);
+  for (int j = 0; j < DMA_PER_TILE; ++j) tile_dma_issue<KC>(d, plan, s, k0, j);
 }
 
 // The loads of one whole stage (A then B), issued piece by piece between MFMA groups.
@@ -206,6 +240,8 @@ struct StageDma {
   TileDma a, b;
   const TileSrc* A;
   const TileSrc* B;
+  const DmaPlan<A_KC>* pa;
+  const DmaPlan<B_KC>* pb;
   int k0;
   bool active;
   __device__ __forceinline__ void issue_piece(int piece) {
@@ -215,53 +251,69 @@ struct StageDma {
     for (int q = 0; q < PER; ++q) {
       const int j = piece * PER + q;
       if (j < DMA_PER_TILE)
-        tile_dma_issue<A_KC>(a, *A, k0, j);
+        tile_dma_issue<A_KC>(a, *pa, *A, k0, j);
       else if (j < DMA_PER_STAGE)
-        tile_dma_issue<B_KC>(b, *B, k0, j - DMA_PER_TILE);
+        tile_dma_issue<B_KC>(b, *pb, *B, k0, j - DMA_PER_TILE);
     }
   }
 };
 
-// MFMA fragment (8 consecutive K values 16 kk + 8 (lane / 32) + 0..7 of tile row or
-// column `idx0 + lane % 32`) from a KC tile.
-__device__ __forceinline__ bf16x8 frag_kc(const char* tile, int idx0, int kk, int lane) {
-  const int r = idx0 + (lane & 31);
-  const int c = 2 * kk + (lane >> 5);
-  return *reinterpret_cast<const bf16x8*>(tile + r * KC_ROW_BYTES + ((c ^ kc_swz(r)) << 4));
-}
-
-// The same fragment from an MN tile, with two transposing reads.  In each 16-lane
-// group, lane i reads 4 columns (4 (i % 4) .. + 3 of the group's 16) of K row i / 4;
-// the read hands lane j of the group column j of those 4 K rows.
-__device__ __forceinline__ bf16x8 frag_mn(const char* tile, int idx0, int kk, int lane) {
-  const int g = lane >> 4, i = lane & 15;
-  const int c0 = idx0 + 16 * (g & 1) + 4 * (i & 3);
-  i16x4 h[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int k = 16 * kk + 8 * (g >> 1) + 4 * hh + (i >> 2);
-    const int off = (k << 9) + ((((c0 >> 4) ^ (k & 7))) << 5) + ((c0 & 15) << 1);
-    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(tile + off));
-  }
-  const i16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
+// Per-lane LDS byte offsets of the MFMA fragments a wave reads from one operand
+// tile, for sub-step kk = 0; sub-step kk adds a constant (folded into the LDS
+// instruction's immediate offset where the layout allows).
+//  KC tile: fragment of rows idx0 + lane % 32, K chunk 2 kk + lane / 32 (ds_read_b128).
+//  MN tile: the same fragment with two transposing reads; in each 16-lane group,
+//  lane i reads 4 columns (4 (i % 4) .. + 3 of the group's 16) of K row i / 4 and
+//  the read hands lane j of the group column j of those 4 K rows.
 template <bool KC>
-__device__ __forceinline__ bf16x8 frag(const char* tile, int idx0, int kk, int lane) {
-  if constexpr (KC)
-    return frag_kc(tile, idx0, kk, lane);
-  else
-    return frag_mn(tile, idx0, kk, lane);
-}
+struct FragPlan {
+  uint32_t off[4][KC ? BKS / 16 : 2];  // [block][kk] for KC, [block][half] for MN
+
+  __device__ __forceinline__ void init(int idx_base, int lane) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int idx0 = idx_base + 32 * blk;
+      if constexpr (KC) {
+        const int r = idx0 + (lane & 31);
+#pragma unroll
+        for (int kk = 0; kk < BKS / 16; ++kk) {
+          const int c = 2 * kk + (lane >> 5);
+          off[blk][kk] = r * KC_ROW_BYTES + ((c ^ kc_swz(r)) << 4);
+        }
+      } else {
+        const int g = lane >> 4, i = lane & 15;
+        const int c0 = idx0 + 16 * (g & 1) + 4 * (i & 3);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = 8 * (g >> 1) + 4 * hh + (i >> 2);   // kk adds 16 rows: k & 7 unchanged
+          off[blk][hh] = (k << 9) + ((((c0 >> 4) ^ (k & 7))) << 5) + ((c0 & 15) << 1);
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ bf16x8 read(const char* tile, int blk, int kk) const {
+    if constexpr (KC) {
+      return *reinterpret_cast<const bf16x8*>(tile + off[blk][kk]);
+    } else {
+      const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS i16x4*)(tile + off[blk][0] + kk * 16 * 512));
+      const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS i16x4*)(tile + off[blk][1] + kk * 16 * 512));
+      const i16x8 v = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      return __builtin_bit_cast(bf16x8, v);
+    }
+  }
+};
 
 template <bool A_KC, bool B_KC>
 __device__ __forceinline__ void read_frags(bf16x8 (&af)[4], bf16x8 (&bfr)[4], const char* stage,
-                                           int wr0, int wc0, int kk, int lane) {
+                                           const FragPlan<A_KC>& fa, const FragPlan<B_KC>& fb,
+                                           int kk) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) af[mb] = frag<A_KC>(stage, wr0 + 32 * mb, kk, lane);
+  for (int mb = 0; mb < 4; ++mb) af[mb] = fa.read(stage, mb, kk);
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) bfr[nb] = frag<B_KC>(stage + TILE_BYTES, wc0 + 32 * nb, kk, lane);
+  for (int nb = 0; nb < 4; ++nb) bfr[nb] = fb.read(stage + TILE_BYTES, nb, kk);
 }
 
 __device__ __forceinline__ void mfma_4x4(f32x16 (&acc)[4][4], const bf16x8 (&af)[4],
@@ -279,17 +331,17 @@ __device__ __forceinline__ void mfma_4x4(f32x16 (&acc)[4][4], const bf16x8 (&af)
 // later stage are issued in DMA_SPREAD pieces between the MFMA groups, so the
 // address FIFO never holds up the matrix pipe for long.
 template <bool A_KC, bool B_KC>
-__device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const char* stage, int wr0,
-                                              int wc0, int lane, StageDma<A_KC, B_KC>& dma) {
+__device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const char* stage,
+                                              const FragPlan<A_KC>& fa, const FragPlan<B_KC>& fb,
+                                              StageDma<A_KC, B_KC>& dma) {
   constexpr int KK = BKS / 16;
   static_assert(DMA_SPREAD >= 1 && DMA_SPREAD <= KK, "DMA_SPREAD must be 1 .. BKS / 16");
   if constexpr (FRAG_PREFETCH) {
     bf16x8 af[2][4], bfr[2][4];
-    read_frags<A_KC, B_KC>(af[0], bfr[0], stage, wr0, wc0, 0, lane);
+    read_frags<A_KC, B_KC>(af[0], bfr[0], stage, fa, fb, 0);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK)
-        read_frags<A_KC, B_KC>(af[(kk + 1) & 1], bfr[(kk + 1) & 1], stage, wr0, wc0, kk + 1, lane);
+      if (kk + 1 < KK) read_frags<A_KC, B_KC>(af[(kk + 1) & 1], bfr[(kk + 1) & 1], stage, fa, fb, kk + 1);
       if (kk < DMA_SPREAD) dma.issue_piece(kk);
       mfma_4x4(acc, af[kk & 1], bfr[kk & 1]);
     }
@@ -297,7 +349,7 @@ __device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const char* s
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       bf16x8 af[4], bfr[4];
-      read_frags<A_KC, B_KC>(af, bfr, stage, wr0, wc0, kk, lane);
+      read_frags<A_KC, B_KC>(af, bfr, stage, fa, fb, kk);
       if (kk < DMA_SPREAD) dma.issue_piece(kk);
       mfma_4x4(acc, af, bfr);
     }
@@ -350,11 +402,20 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, const 
   // K step processed at loop position i: (kt0 + i) mod nk
   const int kt0 = STAGGER > 1 ? (int)(((long)(blockIdx.x % (STAGGER > 1 ? STAGGER : 1)) * nk) / (STAGGER > 1 ? STAGGER : 1)) : 0;
   auto kstep = [&](int i) { const int t = kt0 + i; return t >= nk ? t - nk : t; };
+  DmaPlan<A_KC> plan_a;
+  DmaPlan<B_KC> plan_b;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  plan_a.init(A, wave_u);
+  plan_b.init(B, wave_u);
+  FragPlan<A_KC> frag_a;
+  FragPlan<B_KC> frag_b;
+  frag_a.init(wr0, lane);
+  frag_b.init(wc0, lane);
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st) {
     if (st < nk) {
-      load_tile_async<A_KC>(A, kstep(st) * BKS, smem + st * STAGE_BYTES);
-      load_tile_async<B_KC>(B, kstep(st) * BKS, smem + st * STAGE_BYTES + TILE_BYTES);
+      load_tile_async<A_KC>(A, plan_a, kstep(st) * BKS, smem + st * STAGE_BYTES);
+      load_tile_async<B_KC>(B, plan_b, kstep(st) * BKS, smem + st * STAGE_BYTES + TILE_BYTES);
     }
   }
   wait_stage(min(nk - 1, NST - 2));
@@ -366,12 +427,14 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, const 
     dma.active = ahead_kt < nk;
     dma.A = &A;
     dma.B = &B;
+    dma.pa = &plan_a;
+    dma.pb = &plan_b;
     dma.k0 = kstep(ahead_kt < nk ? ahead_kt : 0) * BKS;
     if (dma.active) {
-      dma.a = tile_dma<A_KC>(A, dma.k0, dst);
-      dma.b = tile_dma<B_KC>(B, dma.k0, dst + TILE_BYTES);
+      dma.a = tile_dma<A_KC>(A, plan_a, dma.k0, dst);
+      dma.b = tile_dma<B_KC>(B, plan_b, dma.k0, dst + TILE_BYTES);
     }
-    compute_stage<A_KC, B_KC>(acc, smem + (kt % NST) * STAGE_BYTES, wr0, wc0, lane, dma);
+    compute_stage<A_KC, B_KC>(acc, smem + (kt % NST) * STAGE_BYTES, frag_a, frag_b, dma);
     // stages issued after step kt + 1 that may still be in flight
     wait_stage(min(max(nk - 1 - (kt + 1), 0), NST - 2));
     __syncthreads();
