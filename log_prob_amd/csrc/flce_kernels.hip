@@ -59,6 +59,12 @@ constexpr int NTHREADS = 256;    // 4 waves of 64
 #ifndef FLCE_STAGGER
 #define FLCE_STAGGER 0
 #endif
+#ifndef FLCE_DMA_INTERLEAVE
+#define FLCE_DMA_INTERLEAVE 0
+#endif
+#ifndef FLCE_SCHED_PIPE
+#define FLCE_SCHED_PIPE 1
+#endif
 constexpr int BKS = FLCE_BKS;    // K per LDS stage
 constexpr int NST = FLCE_NST;    // LDS stages (loads run NST - 1 stages ahead)
 constexpr bool FRAG_PREFETCH = FLCE_FRAG_PREFETCH != 0;  // read kk + 1 before kk's MFMAs
@@ -68,6 +74,15 @@ constexpr int DMA_SPREAD = FLCE_DMA_SPREAD;  // MFMA sub-steps a stage's loads a
 // offset every row of every tile falls on the same few L2 channels; rotating the
 // start spreads the concurrent workgroups over all channels.
 constexpr int STAGGER = FLCE_STAGGER;
+// Issue the next stage's loads one at a time between MFMAs (one per
+// 16 * (BKS / 16) / DMA_PER_STAGE MFMAs) instead of in DMA_SPREAD pieces.
+constexpr bool DMA_INTERLEAVE = FLCE_DMA_INTERLEAVE != 0;
+// Pin the instruction order of a sub-step: the fragment reads of sub-step kk + 1
+// alternate with the first MFMAs of sub-step kk, so each read is issued a whole
+// sub-step (16 MFMAs) before its first use.  Left to itself the scheduler reuses
+// fragment registers right after their last MFMA and issues each read only one
+// MFMA group ahead, exposing the LDS latency.
+constexpr int SCHED_PIPE = FLCE_SCHED_PIPE;
 constexpr int TILE_BYTES = TILE * BKS * 2;            // one operand tile: 16 KiB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;           // A and B
 constexpr int LDS_MAIN = NST * STAGE_BYTES > 2 * TILE * TILE ? NST * STAGE_BYTES
@@ -136,20 +151,35 @@ __device__ __forceinline__ int kc_swz(int r) {
 // it; the mainloop waits for these loads itself (s_waitcnt vmcnt) before the
 // barrier that publishes a stage.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+template <int IMM>
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  static_assert(IMM >= 0 && IMM < 4096, "buffer instruction offset range");
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%4 lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(lds_addr)
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr), "i"(IMM)
                : "memory");
 }
 
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, long bytes) {
+// The same without rewriting m0: the LDS destination is the m0 of the previous
+// dma16 plus IMM (the immediate offset applies to the LDS address as well as to the
+// global one, which the lane offsets pre-subtract).
+template <int IMM>
+__device__ __forceinline__ void dma16_same_m0(i32x4 rsrc, uint32_t voff, uint32_t soff) {
+  static_assert(IMM >= 0 && IMM < 4096, "buffer instruction offset range");
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "i"(IMM)
+               : "memory");
+}
+
+// Buffer descriptor with a fixed record count: every lane that must not load
+// already carries an offset >= OOB_OFFSET, which the buffer unit turns into zeros.
+__device__ __forceinline__ i32x4 make_rsrc_fixed(const void* base) {
   const unsigned long a = (unsigned long)base;
-  const uint32_t nrec = bytes <= 0 ? 0u : (bytes >= 0x7fffffffL ? 0x7fffffffu : (uint32_t)bytes);
   i32x4 r;
   r.x = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
   r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
-  r.z = __builtin_amdgcn_readfirstlane((int)nrec);
+  r.z = 0x7fffffff;
   r.w = (int)RSRC_WORD3;
   return r;
 }
@@ -188,7 +218,8 @@ struct DmaPlan {
       int a, b;
       granule(j, a, b);
       const bool ok = KC ? a < s.valid : 8 * b < s.valid;
-      voff[j] = ok ? (uint32_t)(((long)a * s.ld + 8 * b) * 2) : OOB_OFFSET;
+      // the load's immediate offset (1 KiB x (j % 4)) is added back by the hardware
+      voff[j] = (ok ? (uint32_t)(((long)a * s.ld + 8 * b) * 2) : OOB_OFFSET) - 1024u * (j & 3);
     }
   }
 
@@ -199,14 +230,18 @@ struct DmaPlan {
       int a, b;
       granule(j, a, b);
       const int k = KC ? k0 + 8 * b : k0 + a;
-      if (k >= s.kvalid) v = OOB_OFFSET;
+      if (k >= s.kvalid) v = OOB_OFFSET - 1024u * (j & 3);
     }
     return v;
   }
 };
 
+// Per-stage state of one operand's loads.  A K-contiguous tile keeps one buffer
+// base for the whole K loop and moves with the scalar offset (k0 * 2 bytes stays far
+// below 2^31); an M/N-contiguous tile moves its base by k0 rows.
 struct TileDma {
   i32x4 rsrc;
+  uint32_t soff;
   uint32_t lds0;  // LDS byte address of this wave's first 1 KiB block of the tile
   bool tail;      // the K step runs past kvalid
 };
@@ -214,16 +249,34 @@ struct TileDma {
 template <bool KC>
 __device__ __forceinline__ TileDma tile_dma(const TileSrc& s, const DmaPlan<KC>& plan, int k0,
                                             const char* lds_tile) {
-  const long koff = KC ? (long)k0 : (long)k0 * s.ld;
-  return TileDma{make_rsrc(s.base + koff, (s.span - koff) * 2),
-                 lds_addr_of(lds_tile) + (uint32_t)(plan.wave * DMA_PER_TILE * 1024),
-                 k0 + BKS > s.kvalid};
+  TileDma d;
+  if constexpr (KC) {
+    d.rsrc = make_rsrc_fixed(s.base);
+    d.soff = (uint32_t)k0 * 2u;
+  } else {
+    d.rsrc = make_rsrc_fixed(s.base + (long)k0 * s.ld);
+    d.soff = 0u;
+  }
+  d.lds0 = lds_addr_of(lds_tile) + (uint32_t)(plan.wave * DMA_PER_TILE * 1024);
+  d.tail = k0 + BKS > s.kvalid;
+  return d;
+}
+
+template <bool KC>
+__device__ __forceinline__ void tile_dma_issue_v(const TileDma& d, uint32_t v, int j) {
+  // m0 is rewritten every 4 loads; the 1 KiB steps in between ride on the immediate
+  switch (j & 3) {
+    case 0: dma16<0>(d.rsrc, v, d.soff, d.lds0 + j * 1024); break;
+    case 1: dma16_same_m0<1024>(d.rsrc, v, d.soff); break;
+    case 2: dma16_same_m0<2048>(d.rsrc, v, d.soff); break;
+    default: dma16_same_m0<3072>(d.rsrc, v, d.soff); break;
+  }
 }
 
 template <bool KC>
 __device__ __forceinline__ void tile_dma_issue(const TileDma& d, const DmaPlan<KC>& plan,
                                                const TileSrc& s, int k0, int j) {
-  dma16(d.rsrc, plan.at(s, k0, j, d.tail), d.lds0 + j * 1024);
+  tile_dma_issue_v<KC>(d, plan.at(s, k0, j, d.tail), j);
 }
 
 template <bool KC>
@@ -244,16 +297,35 @@ struct StageDma {
   const DmaPlan<B_KC>* pb;
   int k0;
   bool active;
+  __device__ __forceinline__ void issue_one(int j) {
+    if (!active) return;
+    if (j < DMA_PER_TILE)
+      tile_dma_issue<A_KC>(a, *pa, *A, k0, j);
+    else if (j < DMA_PER_STAGE)
+      tile_dma_issue<B_KC>(b, *pb, *B, k0, j - DMA_PER_TILE);
+  }
   __device__ __forceinline__ void issue_piece(int piece) {
     constexpr int PER = (DMA_PER_STAGE + DMA_SPREAD - 1) / DMA_SPREAD;
     if (!active) return;
+    if (__builtin_expect(a.tail || b.tail, 0)) {
+      // the K step runs past the end of K: masks re-derived per load
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int j = piece * PER + q;
-      if (j < DMA_PER_TILE)
-        tile_dma_issue<A_KC>(a, *pa, *A, k0, j);
-      else if (j < DMA_PER_STAGE)
-        tile_dma_issue<B_KC>(b, *pb, *B, k0, j - DMA_PER_TILE);
+      for (int q = 0; q < PER; ++q) {
+        const int j = piece * PER + q;
+        if (j < DMA_PER_TILE)
+          tile_dma_issue<A_KC>(a, *pa, *A, k0, j);
+        else if (j < DMA_PER_STAGE)
+          tile_dma_issue<B_KC>(b, *pb, *B, k0, j - DMA_PER_TILE);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int j = piece * PER + q;
+        if (j < DMA_PER_TILE)
+          tile_dma_issue_v<A_KC>(a, pa->voff[j], j);
+        else if (j < DMA_PER_STAGE)
+          tile_dma_issue_v<B_KC>(b, pb->voff[j - DMA_PER_TILE], j - DMA_PER_TILE);
+      }
     }
   }
 };
@@ -325,6 +397,21 @@ __device__ __forceinline__ void mfma_4x4(f32x16 (&acc)[4][4], const bf16x8 (&af)
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
 }
 
+// The same 16 MFMAs with the stage's loads `first`, `first + 1`, ... issued one after
+// every EVERY MFMAs.
+template <int EVERY, class Dma>
+__device__ __forceinline__ void mfma_4x4_dma(f32x16 (&acc)[4][4], const bf16x8 (&af)[4],
+                                             const bf16x8 (&bfr)[4], Dma& dma, int first) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+      const int m = 4 * mb + nb;
+      if ((m % EVERY) == EVERY - 1) dma.issue_one(first + m / EVERY);
+    }
+}
+
 // The BKS / 16 MFMA sub-steps of one stage.  With FRAG_PREFETCH the fragments of
 // sub-step kk + 1 are read (into the other register set) before the 16 MFMAs of
 // sub-step kk are issued, so LDS latency hides under matrix work; the loads of a
@@ -342,8 +429,28 @@ __device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const char* s
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if (kk + 1 < KK) read_frags<A_KC, B_KC>(af[(kk + 1) & 1], bfr[(kk + 1) & 1], stage, fa, fb, kk + 1);
-      if (kk < DMA_SPREAD) dma.issue_piece(kk);
-      mfma_4x4(acc, af[kk & 1], bfr[kk & 1]);
+      if constexpr (DMA_INTERLEAVE) {
+        constexpr int EVERY = 16 * KK / DMA_PER_STAGE;
+        mfma_4x4_dma<EVERY>(acc, af[kk & 1], bfr[kk & 1], dma, kk * (16 / EVERY));
+      } else {
+        if (kk < DMA_SPREAD) dma.issue_piece(kk);
+        mfma_4x4(acc, af[kk & 1], bfr[kk & 1]);
+      }
+      if constexpr (SCHED_PIPE == 1) {
+        if (kk + 1 < KK) {
+          // (ds_read, MFMA) x 8, then the remaining 8 MFMAs of this sub-step
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        }
+      } else if constexpr (SCHED_PIPE == 2) {
+        __builtin_amdgcn_iglp_opt(0);
+      }
     }
   } else {
 #pragma unroll
