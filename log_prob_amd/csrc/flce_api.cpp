@@ -54,7 +54,8 @@ flce_status_t check_shape(int64_t M, int64_t H, int64_t V) {
   if (H % 8 != 0)
     return fail(FLCE_ERR_UNSUPPORTED, "H must be a multiple of 8 (got %lld)", (long long)H);
   const int64_t n_mt = cdiv(M, kTile), n_vt = cdiv(V, kTile), n_ht = cdiv(H, kTile);
-  if (n_mt * n_vt > kMaxGrid || n_vt * n_ht > kMaxGrid)
+  if (cdiv(M, flce::kFwdTileM) * cdiv(V, flce::kFwdTileN) > kMaxGrid || n_mt * n_vt > kMaxGrid ||
+      n_vt * n_ht > kMaxGrid)
     return fail(FLCE_ERR_UNSUPPORTED, "shape needs more than 2^31 - 1 workgroups");
   return FLCE_OK;
 }
@@ -66,9 +67,9 @@ struct FwdLayout {
 
 FwdLayout fwd_layout(int64_t M, int64_t V, bool ent) {
   FwdLayout L;
-  L.n_mt = cdiv(M, kTile);
-  L.n_vt = cdiv(V, kTile);
-  L.Mpad = L.n_mt * kTile;
+  L.n_mt = cdiv(M, flce::kFwdTileM);
+  L.n_vt = cdiv(V, flce::kFwdTileN);
+  L.Mpad = cdiv(M, kTile) * kTile;
   const size_t part = align_up(size_t(L.n_vt) * size_t(L.Mpad) * sizeof(float));
   L.off_m = 0;
   L.off_s = part;

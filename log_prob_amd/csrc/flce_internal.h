@@ -7,7 +7,15 @@
 
 namespace flce {
 
-constexpr int kTile = 256;  // workgroup tile edge used by every kernel
+constexpr int kTile = 256;  // backward workgroup tile edge; row padding of every buffer
+// Forward workgroup tile (rows of X x columns of W); kTile is a multiple of both.
+#ifdef FLCE_FWD_PAIR
+constexpr int kFwdTileM = 128;
+#else
+constexpr int kFwdTileM = 256;
+#endif
+constexpr int kFwdTileN = 256;
+static_assert(kTile % kFwdTileM == 0 && kTile % kFwdTileN == 0, "forward tiles pad to kTile");
 
 struct FwdTileArgs {
   const uint16_t* X;        // bf16 [M, H]
@@ -16,8 +24,8 @@ struct FwdTileArgs {
   int M, H, V;
   int64_t ignore_index;
   float scale;
-  int n_mt, n_vt;           // tiles along M and V
-  int Mpad;                 // n_mt * 256: row stride of the partial arrays
+  int n_mt, n_vt;           // forward tiles along M and V
+  int Mpad;                 // M rounded up to kTile: row stride of the partial arrays
   float* part_m;            // [n_vt, Mpad] tile row max of z
   float* part_s;            // [n_vt, Mpad] sum exp(z - m)
   float* part_u;            // [n_vt, Mpad] sum exp(z - m) (z - m)   (entropy only)

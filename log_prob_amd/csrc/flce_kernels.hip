@@ -41,66 +41,83 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TILE = 256;        // rows and columns of a workgroup tile
-constexpr int NTHREADS = 256;    // 4 waves of 64
-// Pipeline shape (tuning builds may override the defaults).
-#ifndef FLCE_BKS
-#define FLCE_BKS 64
-#endif
-#ifndef FLCE_NST
-#define FLCE_NST 2
-#endif
-#ifndef FLCE_FRAG_PREFETCH
-#define FLCE_FRAG_PREFETCH 1
-#endif
+constexpr int NTHREADS = 256;    // 4 waves of 64 in a 2 x 2 grid over the workgroup tile
+// Pipeline options (tuning builds may override the defaults).
 #ifndef FLCE_DMA_SPREAD
 #define FLCE_DMA_SPREAD 1
-#endif
-#ifndef FLCE_STAGGER
-#define FLCE_STAGGER 0
-#endif
-#ifndef FLCE_DMA_INTERLEAVE
-#define FLCE_DMA_INTERLEAVE 0
 #endif
 #ifndef FLCE_SCHED_PIPE
 #define FLCE_SCHED_PIPE 1
 #endif
-constexpr int BKS = FLCE_BKS;    // K per LDS stage
-constexpr int NST = FLCE_NST;    // LDS stages (loads run NST - 1 stages ahead)
-constexpr bool FRAG_PREFETCH = FLCE_FRAG_PREFETCH != 0;  // read kk + 1 before kk's MFMAs
-constexpr int DMA_SPREAD = FLCE_DMA_SPREAD;  // MFMA sub-steps a stage's loads are spread over
-// Workgroups start their K loop at one of STAGGER evenly spaced K steps (and wrap
-// around).  Operand rows are a power-of-two number of bytes apart, so at a fixed K
-// offset every row of every tile falls on the same few L2 channels; rotating the
-// start spreads the concurrent workgroups over all channels.
-constexpr int STAGGER = FLCE_STAGGER;
-// Issue the next stage's loads one at a time between MFMAs (one per
-// 16 * (BKS / 16) / DMA_PER_STAGE MFMAs) instead of in DMA_SPREAD pieces.
-constexpr bool DMA_INTERLEAVE = FLCE_DMA_INTERLEAVE != 0;
+#ifndef FLCE_FENCE_BARRIER
+#define FLCE_FENCE_BARRIER 1
+#endif
+
+// MFMA sub-steps over which a stage's loads are spread (1 = all issued at once).
+constexpr int DMA_SPREAD = FLCE_DMA_SPREAD;
 // Pin the instruction order of a sub-step: the fragment reads of sub-step kk + 1
 // alternate with the first MFMAs of sub-step kk, so each read is issued a whole
-// sub-step (16 MFMAs) before its first use.  Left to itself the scheduler reuses
-// fragment registers right after their last MFMA and issues each read only one
-// MFMA group ahead, exposing the LDS latency.
-constexpr int SCHED_PIPE = FLCE_SCHED_PIPE;
-constexpr int TILE_BYTES = TILE * BKS * 2;            // one operand tile: 16 KiB
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;           // A and B
-constexpr int LDS_MAIN = NST * STAGE_BYTES > 2 * TILE * TILE ? NST * STAGE_BYTES
-                                                             : 2 * TILE * TILE;  // 128 KiB
-constexpr int DMA_PER_TILE = TILE_BYTES / 1024 / 4;   // 16-byte x 64-lane loads per wave
-constexpr int DMA_PER_STAGE = 2 * DMA_PER_TILE;
-static_assert(LDS_MAIN >= 2 * TILE * TILE, "LDS must also hold a 256 x 256 bf16 output tile");
-static_assert(LDS_MAIN <= 128 * 1024, "LDS budget");
+// sub-step before its first use.  Left to itself the scheduler reuses fragment
+// registers right after their last MFMA and issues each read only one MFMA group
+// ahead, exposing the LDS latency.
+constexpr bool SCHED_PIPE = FLCE_SCHED_PIPE != 0;
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // beyond every descriptor's num_records
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+// Shape of a workgroup's mainloop: a TM x TN output tile computed by 4 waves of
+// (TM / 2) x (TN / 2), K staged BK at a time through NST LDS stages.  WAVES_PER_EU
+// is the occupancy the register budget is sized for: 2 lets two workgroups share a
+// CU, so one workgroup's barrier and load-issue stalls hide under the other's
+// matrix work (their LDS footprints must then fit 160 KiB together).
+template <int TM_, int TN_, int BK_, int NST_, int WAVES_PER_EU_>
+struct Shape {
+  static constexpr int TM = TM_, TN = TN_, BK = BK_, NST = NST_;
+  static constexpr int WAVES_PER_EU = WAVES_PER_EU_;
+  static constexpr int WM = TM / 2, WN = TN / 2;      // wave tile
+  static constexpr int MB = WM / 32, NB = WN / 32;    // 32 x 32 MFMA blocks per wave
+  static constexpr int KK = BK / 16;                  // MFMA sub-steps per stage
+  static constexpr int A_BYTES = TM * BK * 2, B_BYTES = TN * BK * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int PIPE_BYTES = NST * STAGE_BYTES;
+  static constexpr int DMA_A = A_BYTES / 4096, DMA_B = B_BYTES / 4096;  // 1 KiB loads per wave
+  static constexpr int DMA_STAGE = DMA_A + DMA_B;
+  static_assert(MB >= 2 && MB % 2 == 0 && NB >= 1, "wave tile");
+  static_assert(BK == 32 || BK == 64, "K per stage");
+  static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole loads per wave");
+  static_assert(NST >= 2 && NST <= 3, "stages");
+  static_assert(DMA_SPREAD >= 1 && DMA_SPREAD < KK, "DMA_SPREAD must be 1 .. BK / 16 - 1");
+};
+// One workgroup per CU: 256 x 256 tiles, waves of 128 x 128, 2 x 64 KiB of LDS.
+using BigShape = Shape<256, 256, 64, 2, 1>;
+// Two workgroups per CU: 128 x 256 tiles, waves of 64 x 128, 3 x 24 KiB of LDS.
+using PairShape = Shape<128, 256, 32, 3, 2>;
+
+// The forward runs BigShape: PairShape raises MFMA utilisation per cycle only a
+// little and its extra LDS and L2 traffic lowers the power-limited clock more.
+#ifdef FLCE_FWD_PAIR
+using FwdShape = PairShape;
+#else
+using FwdShape = BigShape;
+#endif
+static_assert(FwdShape::TM == kFwdTileM && FwdShape::TN == kFwdTileN, "host and kernel tile");
+#ifndef FLCE_FWD_GROUP_M
+#define FLCE_FWD_GROUP_M (2048 / kFwdTileM)
+#endif
+constexpr int FWD_GROUP_M = FLCE_FWD_GROUP_M;  // forward tile rows per L2 group
+
+// The backward kernels run BigShape; their epilogues stage a 256 x 256 bf16 output
+// tile in the LDS the pipeline stages used.
+constexpr int TILE = BigShape::TM;
+constexpr int LDS_BIG = 2 * TILE * TILE;
+static_assert(BigShape::TN == TILE && BigShape::PIPE_BYTES <= LDS_BIG, "backward LDS");
+
 // ---------------------------------------------------------------------------
 // Tile coordinates.  Workgroups are handed to the 8 XCDs round robin, so id b runs
 // on XCD b % 8.  Ids are renumbered so each XCD receives a contiguous range of
-// logical ids, walked in groups of `group_m` tile rows (tile row fastest): the ~32
+// logical ids, walked in groups of `group_m` tile rows (tile row fastest): the
 // workgroups resident on one XCD then share a few operand tiles in its L2.
 __device__ __forceinline__ void tile_coords(int bid, int nblocks, int n_m, int n_n, int group_m,
                                             int& tm, int& tn) {
@@ -132,18 +149,17 @@ struct TileSrc {
   long span;
 };
 
-// LDS layout of a KC tile: 256 rows of BKS bf16 (BKS / 8 chunks of 16 bytes);
-// chunk c of row r sits at chunk position c ^ kc_swz(r).  The 16 consecutive rows
-// one ds_read_b128 cycle serves land on distinct (bank-row, chunk) positions.
-constexpr int KC_ROW_BYTES = BKS * 2;
-constexpr int KC_CHUNKS = BKS / 8;
+// LDS layout of a KC tile: rows of BK bf16 (BK / 8 chunks of 16 bytes); chunk c of
+// row r sits at chunk position c ^ kc_swz(r).  The 16 rows one ds_read_b128 cycle
+// serves land on 16 distinct 16-byte bank groups.
+template <int CHUNKS>
 __device__ __forceinline__ int kc_swz(int r) {
-  return KC_CHUNKS == 8 ? ((r ^ (r >> 3)) & 7) : ((r >> 2) & (KC_CHUNKS - 1));
+  return CHUNKS == 8 ? ((r ^ (r >> 3)) & 7) : ((r >> 2) & 3);
 }
 
-// LDS layout of an MN tile: BKS K rows of 256 bf16 (16 blocks of 32 bytes); block b
-// of K row k sits at block position b ^ (k & 7).  The 4 consecutive K rows one
-// transposing read touches land on distinct blocks.
+// LDS layout of an MN tile of `cols` columns: BK K rows of 2 cols bytes (cols / 16
+// blocks of 32 bytes); block b of K row k sits at block position b ^ (k & 7).  The
+// 4 consecutive K rows one transposing read touches land on distinct blocks.
 
 // One 64-lane direct-to-LDS load: lane i's 16 bytes from byte offset voff of the
 // buffer go to LDS address lds_addr + 16 i.  Issued as inline assembly so that the
@@ -188,33 +204,36 @@ __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
   return (uint32_t)(uintptr_t)(LDS_AS const char*)p;
 }
 
-// Direct-to-LDS loads of one 256 x BKS operand tile for K offset k0.  The tile is
-// filled by 4 waves x DMA_PER_TILE loads; load j of wave w fills LDS bytes
-// [(w DMA_PER_TILE + j) KiB, + 1 KiB) of the tile, lane i the 16 bytes at i * 16.
-// Each lane's byte offsets relative to the K step's base address do not change from
-// step to step, so they are computed once (DmaPlan); only a K step that runs past
-// the end of K re-derives the mask (a uniform branch, taken at most once).
-template <bool KC>
+// Direct-to-LDS loads of one ROWS x BK operand tile (ROWS rows of a KC operand, or
+// ROWS columns of an MN operand).  The tile is filled by 4 waves x N loads; load j
+// of wave w fills LDS bytes [(w N + j) KiB, + 1 KiB) of the tile, lane i the 16
+// bytes at i * 16.  Each lane's byte offsets relative to the K step's base address
+// do not change from step to step, so they are computed once; only a K step that
+// runs past the end of K re-derives the mask (a uniform branch, taken at most once).
+template <bool KC, int ROWS, int BK>
 struct DmaPlan {
-  uint32_t voff[DMA_PER_TILE];
+  static constexpr int N = ROWS * BK * 2 / 4096;  // loads per wave
+  static constexpr int CHUNKS = BK / 8;           // KC: 16-byte chunks per tile row
+  static constexpr int GPR = ROWS / 8;            // MN: 16-byte granules per K row
+  uint32_t voff[N];
   int wave;
 
   __device__ __forceinline__ void granule(int j, int& a, int& b) const {
     const int lane = threadIdx.x & 63;
-    const int G = (wave * DMA_PER_TILE + j) * 64 + lane;  // 16-byte granule of the tile
+    const int G = (wave * N + j) * 64 + lane;  // 16-byte granule of the tile
     if constexpr (KC) {
-      a = G / KC_CHUNKS;                              // tile row
-      b = (G % KC_CHUNKS) ^ kc_swz(a);                // 16-byte chunk of K in the row
+      a = G / CHUNKS;                          // tile row
+      b = (G % CHUNKS) ^ kc_swz<CHUNKS>(a);    // 16-byte chunk of K in the row
     } else {
-      a = G >> 5;                                     // K row
-      b = (G & 31) ^ ((a & 7) << 1);                  // 16-byte chunk of columns
+      a = G / GPR;                             // K row
+      b = (G % GPR) ^ ((a & 7) << 1);          // 16-byte chunk of columns
     }
   }
 
   __device__ __forceinline__ void init(const TileSrc& s, int wave_id) {
     wave = wave_id;
 #pragma unroll
-    for (int j = 0; j < DMA_PER_TILE; ++j) {
+    for (int j = 0; j < N; ++j) {
       int a, b;
       granule(j, a, b);
       const bool ok = KC ? a < s.valid : 8 * b < s.valid;
@@ -246,9 +265,9 @@ struct TileDma {
   bool tail;      // the K step runs past kvalid
 };
 
-template <bool KC>
-__device__ __forceinline__ TileDma tile_dma(const TileSrc& s, const DmaPlan<KC>& plan, int k0,
-                                            const char* lds_tile) {
+template <bool KC, int ROWS, int BK>
+__device__ __forceinline__ TileDma tile_dma(const TileSrc& s, const DmaPlan<KC, ROWS, BK>& plan,
+                                            int k0, const char* lds_tile) {
   TileDma d;
   if constexpr (KC) {
     d.rsrc = make_rsrc_fixed(s.base);
@@ -257,12 +276,11 @@ __device__ __forceinline__ TileDma tile_dma(const TileSrc& s, const DmaPlan<KC>&
     d.rsrc = make_rsrc_fixed(s.base + (long)k0 * s.ld);
     d.soff = 0u;
   }
-  d.lds0 = lds_addr_of(lds_tile) + (uint32_t)(plan.wave * DMA_PER_TILE * 1024);
-  d.tail = k0 + BKS > s.kvalid;
+  d.lds0 = lds_addr_of(lds_tile) + (uint32_t)(plan.wave * plan.N * 1024);
+  d.tail = k0 + BK > s.kvalid;
   return d;
 }
 
-template <bool KC>
 __device__ __forceinline__ void tile_dma_issue_v(const TileDma& d, uint32_t v, int j) {
   // m0 is rewritten every 4 loads; the 1 KiB steps in between ride on the immediate
   switch (j & 3) {
@@ -273,58 +291,48 @@ __device__ __forceinline__ void tile_dma_issue_v(const TileDma& d, uint32_t v, i
   }
 }
 
-template <bool KC>
-__device__ __forceinline__ void tile_dma_issue(const TileDma& d, const DmaPlan<KC>& plan,
-                                               const TileSrc& s, int k0, int j) {
-  tile_dma_issue_v<KC>(d, plan.at(s, k0, j, d.tail), j);
-}
-
-template <bool KC>
-__device__ __forceinline__ void load_tile_async(const TileSrc& s, const DmaPlan<KC>& plan, int k0,
-                                                const char* lds_tile) {
-  const TileDma d = tile_dma<KC>(s, plan, k0, lds_tile);
+template <bool KC, int ROWS, int BK>
+__device__ __forceinline__ void load_tile_async(const TileSrc& s, const DmaPlan<KC, ROWS, BK>& plan,
+                                                int k0, const char* lds_tile) {
+  const TileDma d = tile_dma(s, plan, k0, lds_tile);
 #pragma unroll
-  for (int j = 0; j < DMA_PER_TILE; ++j) tile_dma_issue<KC>(d, plan, s, k0, j);
+  for (int j = 0; j < plan.N; ++j) tile_dma_issue_v(d, plan.at(s, k0, j, d.tail), j);
 }
 
-// The loads of one whole stage (A then B), issued piece by piece between MFMA groups.
-template <bool A_KC, bool B_KC>
+// The loads of one whole stage (A then B), issued in DMA_SPREAD pieces between
+// MFMA groups.
+template <class S, bool A_KC, bool B_KC>
 struct StageDma {
+  using PA = DmaPlan<A_KC, S::TM, S::BK>;
+  using PB = DmaPlan<B_KC, S::TN, S::BK>;
   TileDma a, b;
   const TileSrc* A;
   const TileSrc* B;
-  const DmaPlan<A_KC>* pa;
-  const DmaPlan<B_KC>* pb;
+  const PA* pa;
+  const PB* pb;
   int k0;
   bool active;
-  __device__ __forceinline__ void issue_one(int j) {
-    if (!active) return;
-    if (j < DMA_PER_TILE)
-      tile_dma_issue<A_KC>(a, *pa, *A, k0, j);
-    else if (j < DMA_PER_STAGE)
-      tile_dma_issue<B_KC>(b, *pb, *B, k0, j - DMA_PER_TILE);
-  }
   __device__ __forceinline__ void issue_piece(int piece) {
-    constexpr int PER = (DMA_PER_STAGE + DMA_SPREAD - 1) / DMA_SPREAD;
+    constexpr int PER = (S::DMA_STAGE + DMA_SPREAD - 1) / DMA_SPREAD;
     if (!active) return;
     if (__builtin_expect(a.tail || b.tail, 0)) {
       // the K step runs past the end of K: masks re-derived per load
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const int j = piece * PER + q;
-        if (j < DMA_PER_TILE)
-          tile_dma_issue<A_KC>(a, *pa, *A, k0, j);
-        else if (j < DMA_PER_STAGE)
-          tile_dma_issue<B_KC>(b, *pb, *B, k0, j - DMA_PER_TILE);
+        if (j < S::DMA_A)
+          tile_dma_issue_v(a, pa->at(*A, k0, j, true), j);
+        else if (j < S::DMA_STAGE)
+          tile_dma_issue_v(b, pb->at(*B, k0, j - S::DMA_A, true), j - S::DMA_A);
       }
     } else {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const int j = piece * PER + q;
-        if (j < DMA_PER_TILE)
-          tile_dma_issue_v<A_KC>(a, pa->voff[j], j);
-        else if (j < DMA_PER_STAGE)
-          tile_dma_issue_v<B_KC>(b, pb->voff[j - DMA_PER_TILE], j - DMA_PER_TILE);
+        if (j < S::DMA_A)
+          tile_dma_issue_v(a, pa->voff[j], j);
+        else if (j < S::DMA_STAGE)
+          tile_dma_issue_v(b, pb->voff[j - S::DMA_A], j - S::DMA_A);
       }
     }
   }
@@ -337,20 +345,21 @@ struct StageDma {
 //  MN tile: the same fragment with two transposing reads; in each 16-lane group,
 //  lane i reads 4 columns (4 (i % 4) .. + 3 of the group's 16) of K row i / 4 and
 //  the read hands lane j of the group column j of those 4 K rows.
-template <bool KC>
+template <bool KC, int NBLK, int ROWS, int BK>
 struct FragPlan {
-  uint32_t off[4][KC ? BKS / 16 : 2];  // [block][kk] for KC, [block][half] for MN
+  static constexpr int ROW_BYTES = KC ? BK * 2 : ROWS * 2;  // bytes per LDS row
+  uint32_t off[NBLK][KC ? BK / 16 : 2];  // [block][kk] for KC, [block][half] for MN
 
   __device__ __forceinline__ void init(int idx_base, int lane) {
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
+    for (int blk = 0; blk < NBLK; ++blk) {
       const int idx0 = idx_base + 32 * blk;
       if constexpr (KC) {
         const int r = idx0 + (lane & 31);
 #pragma unroll
-        for (int kk = 0; kk < BKS / 16; ++kk) {
+        for (int kk = 0; kk < BK / 16; ++kk) {
           const int c = 2 * kk + (lane >> 5);
-          off[blk][kk] = r * KC_ROW_BYTES + ((c ^ kc_swz(r)) << 4);
+          off[blk][kk] = r * ROW_BYTES + ((c ^ kc_swz<BK / 8>(r)) << 4);
         }
       } else {
         const int g = lane >> 4, i = lane & 15;
@@ -358,7 +367,7 @@ struct FragPlan {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int k = 8 * (g >> 1) + 4 * hh + (i >> 2);   // kk adds 16 rows: k & 7 unchanged
-          off[blk][hh] = (k << 9) + ((((c0 >> 4) ^ (k & 7))) << 5) + ((c0 & 15) << 1);
+          off[blk][hh] = k * ROW_BYTES + ((((c0 >> 4) ^ (k & 7))) << 5) + ((c0 & 15) << 1);
         }
       }
     }
@@ -369,98 +378,39 @@ struct FragPlan {
       return *reinterpret_cast<const bf16x8*>(tile + off[blk][kk]);
     } else {
       const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (LDS_AS i16x4*)(tile + off[blk][0] + kk * 16 * 512));
+          (LDS_AS i16x4*)(tile + off[blk][0] + kk * 16 * ROW_BYTES));
       const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (LDS_AS i16x4*)(tile + off[blk][1] + kk * 16 * 512));
+          (LDS_AS i16x4*)(tile + off[blk][1] + kk * 16 * ROW_BYTES));
       const i16x8 v = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
       return __builtin_bit_cast(bf16x8, v);
     }
   }
 };
 
-template <bool A_KC, bool B_KC>
-__device__ __forceinline__ void read_frags(bf16x8 (&af)[4], bf16x8 (&bfr)[4], const char* stage,
-                                           const FragPlan<A_KC>& fa, const FragPlan<B_KC>& fb,
+template <class S, bool A_KC, bool B_KC>
+struct Frags {
+  FragPlan<A_KC, S::MB, S::TM, S::BK> a;
+  FragPlan<B_KC, S::NB, S::TN, S::BK> b;
+};
+
+template <class S, bool A_KC, bool B_KC>
+__device__ __forceinline__ void read_frags(bf16x8 (&af)[S::MB], bf16x8 (&bfr)[S::NB],
+                                           const char* stage, const Frags<S, A_KC, B_KC>& f,
                                            int kk) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) af[mb] = fa.read(stage, mb, kk);
+  for (int mb = 0; mb < S::MB; ++mb) af[mb] = f.a.read(stage, mb, kk);
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) bfr[nb] = fb.read(stage + TILE_BYTES, nb, kk);
+  for (int nb = 0; nb < S::NB; ++nb) bfr[nb] = f.b.read(stage + S::A_BYTES, nb, kk);
 }
 
-__device__ __forceinline__ void mfma_4x4(f32x16 (&acc)[4][4], const bf16x8 (&af)[4],
-                                         const bf16x8 (&bfr)[4]) {
+template <int MB, int NB>
+__device__ __forceinline__ void mfma_block(f32x16 (&acc)[MB][NB], const bf16x8 (&af)[MB],
+                                           const bf16x8 (&bfr)[NB]) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-}
-
-// The same 16 MFMAs with the stage's loads `first`, `first + 1`, ... issued one after
-// every EVERY MFMAs.
-template <int EVERY, class Dma>
-__device__ __forceinline__ void mfma_4x4_dma(f32x16 (&acc)[4][4], const bf16x8 (&af)[4],
-                                             const bf16x8 (&bfr)[4], Dma& dma, int first) {
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-      const int m = 4 * mb + nb;
-      if ((m % EVERY) == EVERY - 1) dma.issue_one(first + m / EVERY);
-    }
-}
-
-// The BKS / 16 MFMA sub-steps of one stage.  With FRAG_PREFETCH the fragments of
-// sub-step kk + 1 are read (into the other register set) before the 16 MFMAs of
-// sub-step kk are issued, so LDS latency hides under matrix work; the loads of a
-// later stage are issued in DMA_SPREAD pieces between the MFMA groups, so the
-// address FIFO never holds up the matrix pipe for long.
-template <bool A_KC, bool B_KC>
-__device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const char* stage,
-                                              const FragPlan<A_KC>& fa, const FragPlan<B_KC>& fb,
-                                              StageDma<A_KC, B_KC>& dma) {
-  constexpr int KK = BKS / 16;
-  static_assert(DMA_SPREAD >= 1 && DMA_SPREAD <= KK, "DMA_SPREAD must be 1 .. BKS / 16");
-  if constexpr (FRAG_PREFETCH) {
-    bf16x8 af[2][4], bfr[2][4];
-    read_frags<A_KC, B_KC>(af[0], bfr[0], stage, fa, fb, 0);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) read_frags<A_KC, B_KC>(af[(kk + 1) & 1], bfr[(kk + 1) & 1], stage, fa, fb, kk + 1);
-      if constexpr (DMA_INTERLEAVE) {
-        constexpr int EVERY = 16 * KK / DMA_PER_STAGE;
-        mfma_4x4_dma<EVERY>(acc, af[kk & 1], bfr[kk & 1], dma, kk * (16 / EVERY));
-      } else {
-        if (kk < DMA_SPREAD) dma.issue_piece(kk);
-        mfma_4x4(acc, af[kk & 1], bfr[kk & 1]);
-      }
-      if constexpr (SCHED_PIPE == 1) {
-        if (kk + 1 < KK) {
-          // (ds_read, MFMA) x 8, then the remaining 8 MFMAs of this sub-step
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-        }
-      } else if constexpr (SCHED_PIPE == 2) {
-        __builtin_amdgcn_iglp_opt(0);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      bf16x8 af[4], bfr[4];
-      read_frags<A_KC, B_KC>(af, bfr, stage, fa, fb, kk);
-      if (kk < DMA_SPREAD) dma.issue_piece(kk);
-      mfma_4x4(acc, af, bfr);
-    }
-  }
 }
 
 // s_waitcnt until at most n of this wave's vector-memory operations are outstanding
@@ -473,78 +423,115 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Wait until the loads of the stage after the one just computed have landed, given
 // that `ahead` later stages (0 .. NST - 2) may still be in flight.
+template <class S>
 __device__ __forceinline__ void wait_stage(int ahead) {
-  if constexpr (NST >= 4) {
-    if (ahead >= 2) { wait_vmcnt<2 * DMA_PER_STAGE>(); return; }
-  }
-  if constexpr (NST >= 3) {
-    if (ahead >= 1) { wait_vmcnt<DMA_PER_STAGE>(); return; }
+  if constexpr (S::NST >= 3) {
+    if (ahead >= 1) { wait_vmcnt<S::DMA_STAGE>(); return; }
   }
   wait_vmcnt<0>();
 }
 
+// Pin the instruction order of one MFMA sub-step whose successor's fragments are
+// read during it: (ds_read, MFMA) x R, then the remaining MFMAs.
+template <class S, bool READS>
+__device__ __forceinline__ void sched_substep() {
+  constexpr int F = S::MB * S::NB;                          // MFMAs per sub-step
+  constexpr int R = S::MB + S::NB < F ? S::MB + S::NB : F;  // reads paired with MFMAs
+  if constexpr (SCHED_PIPE) {
+    if constexpr (READS) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      if constexpr (F > R) __builtin_amdgcn_sched_group_barrier(0x008, F - R, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, F, 0);
+    }
+  }
+}
+
 // The MFMA mainloop shared by every kernel: D = A B^T over K for the workgroup's
-// 256 x 256 tile, as 4 waves of 128 x 128 (wave w at rows 128 (w / 2), columns
-// 128 (w % 2)).  acc[mb][nb] is the 32 x 32 block at (32 mb, 32 nb) of the wave
+// TM x TN tile, as 4 waves of WM x WN (wave w at rows WM (w / 2), columns
+// WN (w % 2)).  acc[mb][nb] is the 32 x 32 block at (32 mb, 32 nb) of the wave
 // tile in the v_mfma_f32_32x32x16 layout: lane l, element e holds row
 // 8 (e / 4) + 4 (l / 32) + e % 4 and column l % 32.
 //
 // Pipeline: NST LDS stages; at step kt the loads of step kt + NST - 1 are issued
-// into the stage computed at step kt - 1 (released by the barrier that ended that
-// step), the fragments of stage kt are read and multiplied, then the wave waits for
-// its own loads of step kt + 1 and the barrier publishes that stage to all waves.
-template <bool A_KC, bool B_KC>
-__device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], char* smem, const TileSrc& A,
-                                         const TileSrc& B, int K) {
+// into the stage computed at step kt - 1, and the KK MFMA sub-steps of stage kt
+// run with the fragments of sub-step kk + 1 read (into the other register set)
+// while the MFMAs of sub-step kk are issued.  Before the last sub-step the wave
+// waits for its own loads of step kt + 1 and the barrier publishes that stage (and
+// releases stage kt, whose reads have all returned); the first fragments of step
+// kt + 1 are then read under the last sub-step's MFMAs, so no step starts with an
+// LDS-latency bubble.
+template <class S, bool A_KC, bool B_KC>
+__device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem,
+                                         const TileSrc& A, const TileSrc& B, int K) {
+  constexpr int KK = S::KK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
+  const int wr0 = (wave >> 1) * S::WM, wc0 = (wave & 1) * S::WN;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < S::MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < S::NB; ++nb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
 
-  const int nk = (K + BKS - 1) / BKS;
-  // K step processed at loop position i: (kt0 + i) mod nk
-  const int kt0 = STAGGER > 1 ? (int)(((long)(blockIdx.x % (STAGGER > 1 ? STAGGER : 1)) * nk) / (STAGGER > 1 ? STAGGER : 1)) : 0;
-  auto kstep = [&](int i) { const int t = kt0 + i; return t >= nk ? t - nk : t; };
-  DmaPlan<A_KC> plan_a;
-  DmaPlan<B_KC> plan_b;
+  const int nk = (K + S::BK - 1) / S::BK;
+  typename StageDma<S, A_KC, B_KC>::PA plan_a;
+  typename StageDma<S, A_KC, B_KC>::PB plan_b;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   plan_a.init(A, wave_u);
   plan_b.init(B, wave_u);
-  FragPlan<A_KC> frag_a;
-  FragPlan<B_KC> frag_b;
-  frag_a.init(wr0, lane);
-  frag_b.init(wc0, lane);
+  Frags<S, A_KC, B_KC> frags;
+  frags.a.init(wr0, lane);
+  frags.b.init(wc0, lane);
 #pragma unroll
-  for (int st = 0; st < NST - 1; ++st) {
+  for (int st = 0; st < S::NST - 1; ++st) {
     if (st < nk) {
-      load_tile_async<A_KC>(A, plan_a, kstep(st) * BKS, smem + st * STAGE_BYTES);
-      load_tile_async<B_KC>(B, plan_b, kstep(st) * BKS, smem + st * STAGE_BYTES + TILE_BYTES);
+      load_tile_async(A, plan_a, st * S::BK, smem + st * S::STAGE_BYTES);
+      load_tile_async(B, plan_b, st * S::BK, smem + st * S::STAGE_BYTES + S::A_BYTES);
     }
   }
-  wait_stage(min(nk - 1, NST - 2));
+  wait_stage<S>(min(nk - 1, S::NST - 2));
   __syncthreads();
+  static_assert(KK % 2 == 0, "sub-step 0 of every stage uses register set 0");
+  bf16x8 af[2][S::MB], bfr[2][S::NB];
+  read_frags<S>(af[0], bfr[0], smem, frags, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int ahead_kt = kt + NST - 1;
-    char* dst = smem + (ahead_kt % NST) * STAGE_BYTES;
-    StageDma<A_KC, B_KC> dma;
+    const int ahead_kt = kt + S::NST - 1;
+    char* dst = smem + (ahead_kt % S::NST) * S::STAGE_BYTES;
+    const char* cur = smem + (kt % S::NST) * S::STAGE_BYTES;
+    StageDma<S, A_KC, B_KC> dma;
     dma.active = ahead_kt < nk;
     dma.A = &A;
     dma.B = &B;
     dma.pa = &plan_a;
     dma.pb = &plan_b;
-    dma.k0 = kstep(ahead_kt < nk ? ahead_kt : 0) * BKS;
+    dma.k0 = (ahead_kt < nk ? ahead_kt : 0) * S::BK;
     if (dma.active) {
-      dma.a = tile_dma<A_KC>(A, plan_a, dma.k0, dst);
-      dma.b = tile_dma<B_KC>(B, plan_b, dma.k0, dst + TILE_BYTES);
+      dma.a = tile_dma(A, plan_a, dma.k0, dst);
+      dma.b = tile_dma(B, plan_b, dma.k0, dst + S::A_BYTES);
     }
-    compute_stage<A_KC, B_KC>(acc, smem + (kt % NST) * STAGE_BYTES, frag_a, frag_b, dma);
+#pragma unroll
+    for (int kk = 0; kk < KK - 1; ++kk) {
+      read_frags<S>(af[(kk + 1) & 1], bfr[(kk + 1) & 1], cur, frags, kk + 1);
+      if (kk < DMA_SPREAD) dma.issue_piece(kk);
+      mfma_block<S::MB, S::NB>(acc, af[kk & 1], bfr[kk & 1]);
+      sched_substep<S, true>();
+    }
+#if FLCE_FENCE_BARRIER
+    // keep the barrier after every MFMA issued so far (the compiler would hoist it)
+    __builtin_amdgcn_sched_barrier(0);
+#endif
     // stages issued after step kt + 1 that may still be in flight
-    wait_stage(min(max(nk - 1 - (kt + 1), 0), NST - 2));
+    wait_stage<S>(min(max(nk - 1 - (kt + 1), 0), S::NST - 2));
     __syncthreads();
+    // (after the last step this reads a stale stage; the values are never used)
+    read_frags<S>(af[0], bfr[0], smem + ((kt + 1) % S::NST) * S::STAGE_BYTES, frags, 0);
+    mfma_block<S::MB, S::NB>(acc, af[1], bfr[1]);
+    sched_substep<S, true>();
   }
 }
 
@@ -623,92 +610,99 @@ __device__ __forceinline__ uint16_t* out_slot(char* lo, char* hi, int rl, int cl
 }
 
 // ---------------------------------------------------------------------------
-// Forward tile kernel.  Per wave: lane l holds, for row slot q = 16 mb + e (64 of
-// them), the 4 columns 32 nb + l % 32 of its wave tile.  The wave reduces its 128
+// Forward tile kernel.  Per wave: lane l holds, for row slot q = 16 mb + e (16 MB of
+// them), the NB columns 32 nb + l % 32 of its wave tile.  The wave reduces its WN
 // columns per row (max, then shifted sums); the two waves sharing rows are merged
-// through LDS and thread t writes the partials of tile row t.
-template <bool ENT>
-__global__ __launch_bounds__(NTHREADS) void fwd_tile_kernel(FwdTileArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_MAIN];
-  __shared__ int t_local[TILE];
+// through LDS and thread t < TM writes the partials of tile row t.
+template <class S, bool ENT>
+__global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(FwdTileArgs p) {
+  constexpr int TM = S::TM, TN = S::TN, MB = S::MB, NB = S::NB, WN = S::WN;
+  constexpr int P = MB / 2;  // groups of 32 row slots per lane
+  __shared__ __attribute__((aligned(1024))) char smem[S::PIPE_BYTES];
+  __shared__ int t_local[TM];
+  static_assert(6 * TM * 4 <= S::PIPE_BYTES, "row merge buffer");
   int mt, vt;
-  tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, 8, mt, vt);
-  const int row0 = mt * TILE, col0 = vt * TILE;
+  tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, FWD_GROUP_M, mt, vt);
+  const int row0 = mt * TM, col0 = vt * TN;
   const int tid = threadIdx.x;
-  {
+  if (tid < TM) {
     // target column relative to this tile, or -1 if no valid target lies in it
     const int r = row0 + tid;
     int tl = -1;
     if (r < p.M) {
       const int64_t t = p.targets[r];
-      if (t != p.ignore_index && t >= col0 && t < min<int64_t>(col0 + TILE, p.V))
+      if (t != p.ignore_index && t >= col0 && t < min<int64_t>(col0 + TN, p.V))
         tl = (int)(t - col0);
     }
     t_local[tid] = tl;
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[MB][NB];
   const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, (long)(p.M - row0) * p.H};
   const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, (long)(p.V - col0) * p.H};
-  mainloop<true, true>(acc, smem, A, B, p.H);
+  mainloop<S, true, true>(acc, smem, A, B, p.H);
 
   const int lane = tid & 63, wave = tid >> 6;
-  const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
+  const int wr0 = (wave >> 1) * S::WM, wc0 = (wave & 1) * WN;
   const int lc = lane & 31;
   const float c1 = p.scale * LOG2E;  // logits in log2 units: z2 = acc * c1
-  const bool ragged = col0 + TILE > p.V;
+  const bool ragged = col0 + TN > p.V;
 
   // scale into log2 units; columns past V become -inf (only the last V tile has any)
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const bool colok = !ragged || (col0 + wc0 + 32 * nb + lc < p.V);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mb][nb][e] = colok ? acc[mb][nb][e] * c1 : -INFINITY;
   }
 
   // target logit: the unique lane holding column t[row] writes z[row, t]
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int rl = wr0 + 32 * mb + acc_row(lane, e);
       const int d = t_local[rl] - wc0 - lc;
-      if (d >= 0 && d < 128 && (d & 31) == 0) {
+      if (d >= 0 && d < WN && (d & 31) == 0) {
         float z = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
           if ((d >> 5) == nb) z = acc[mb][nb][e];
         p.zt[row0 + rl] = z * LN2;
       }
     }
 
-  // row maxima of the wave's 128 columns
-  float mx[64];
+  // row maxima of the wave's WN columns
+  float mx[32 * P];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float m = fmaxf(fmaxf(acc[mb][0][e], acc[mb][1][e]), fmaxf(acc[mb][2][e], acc[mb][3][e]));
+      float m = acc[mb][0][e];
+#pragma unroll
+      for (int nb = 1; nb < NB; ++nb) m = fmaxf(m, acc[mb][nb][e]);
       mx[16 * mb + e] = m;
     }
-  reduce_scatter32<2>(mx, lane, [](float a, float b) { return fmaxf(a, b); });
-  const float my_max0 = mx[0], my_max1 = mx[32];
-  all_gather32<2>(mx, lane);
+  reduce_scatter32<P>(mx, lane, [](float a, float b) { return fmaxf(a, b); });
+  float my_max[P];
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp) my_max[pp] = mx[32 * pp];
+  all_gather32<P>(mx, lane);
 
   // shifted sums s = sum exp2(z2 - m2) and u = sum exp2(z2 - m2) (z2 - m2); a row
   // with no column in this wave (ragged tile) keeps m = -inf, s = u = 0
-  float sv[64], uv[ENT ? 64 : 1];
+  float sv[32 * P], uv[ENT ? 32 * P : 1];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float m = mx[16 * mb + e];
       const float mref = m == -INFINITY ? 0.f : m;
       float s = 0.f, u = 0.f;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         const float d = acc[mb][nb][e] - mref;
         const float pe = __builtin_amdgcn_exp2f(d);
         s += pe;
@@ -717,25 +711,25 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tile_kernel(FwdTileArgs p) {
       sv[16 * mb + e] = s;
       if constexpr (ENT) uv[16 * mb + e] = u;
     }
-  reduce_scatter32<2>(sv, lane, [](float a, float b) { return a + b; });
-  if constexpr (ENT) reduce_scatter32<2>(uv, lane, [](float a, float b) { return a + b; });
+  reduce_scatter32<P>(sv, lane, [](float a, float b) { return a + b; });
+  if constexpr (ENT) reduce_scatter32<P>(uv, lane, [](float a, float b) { return a + b; });
 
   // merge the two column halves of each row through LDS (the stages are free now)
-  float* comb = reinterpret_cast<float*>(smem);  // [2 halves][3 stats][256 rows]
+  float* comb = reinterpret_cast<float*>(smem);  // [2 halves][3 stats][TM rows]
   const int wn = wave & 1;
 #pragma unroll
-  for (int pp = 0; pp < 2; ++pp) {
+  for (int pp = 0; pp < P; ++pp) {
     const int j = lc;
     const int mb = 2 * pp + (j >> 4), e = j & 15;
     const int rl = wr0 + 32 * mb + acc_row(lane, e);
-    comb[(wn * 3 + 0) * TILE + rl] = (pp ? my_max1 : my_max0) * LN2;
-    comb[(wn * 3 + 1) * TILE + rl] = sv[32 * pp];
-    comb[(wn * 3 + 2) * TILE + rl] = ENT ? uv[ENT ? 32 * pp : 0] * LN2 : 0.f;
+    comb[(wn * 3 + 0) * TM + rl] = my_max[pp] * LN2;
+    comb[(wn * 3 + 1) * TM + rl] = sv[32 * pp];
+    comb[(wn * 3 + 2) * TM + rl] = ENT ? uv[ENT ? 32 * pp : 0] * LN2 : 0.f;
   }
   __syncthreads();
-  {
-    const float m0 = comb[0 * TILE + tid], s0 = comb[1 * TILE + tid], u0 = comb[2 * TILE + tid];
-    const float m1 = comb[3 * TILE + tid], s1 = comb[4 * TILE + tid], u1 = comb[5 * TILE + tid];
+  if (tid < TM) {
+    const float m0 = comb[0 * TM + tid], s0 = comb[1 * TM + tid], u0 = comb[2 * TM + tid];
+    const float m1 = comb[3 * TM + tid], s1 = comb[4 * TM + tid], u1 = comb[5 * TM + tid];
     float m, s, u;
     if (s1 == 0.f) {
       m = m0; s = s0; u = u0;
@@ -785,7 +779,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdMergeArgs p) {
 // V and rows past M are written as zero.
 template <bool ENTGRAD>
 __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_MAIN];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
   __shared__ float r_lse2[TILE], r_a[TILE], r_b[TILE], r_E[TILE];
   __shared__ int t_local[TILE];
   int mt, vt;
@@ -819,7 +813,7 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
   f32x16 acc[4][4];
   const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, (long)(p.M - row0) * p.H};
   const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, (long)(p.V - col0) * p.H};
-  mainloop<true, true>(acc, smem, A, B, p.H);
+  mainloop<BigShape, true, true>(acc, smem, A, B, p.H);
 
   const int lane = tid & 63, wave = tid >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
@@ -851,7 +845,7 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
 // ---------------------------------------------------------------------------
 // dW[vbase + i, h] = sum_m dzs[m, i] X[m, h]: A = dzs^T (MN), B = X^T (MN), K = Mpad.
 __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_MAIN];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
   int ti, th;
   tile_coords(blockIdx.x, gridDim.x, p.n_i, p.n_h, 8, ti, th);
   const int i0 = ti * TILE, h0 = th * TILE;
@@ -859,7 +853,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
   // dzs has Mpad rows (rows past M hold zeros); X has only M rows.
   const TileSrc A{p.dz + i0, p.ldz, p.chunk_cols - i0, p.Mpad, (long)p.Mpad * p.ldz - i0};
   const TileSrc B{p.X + h0, p.H, p.H - h0, p.M, (long)p.M * p.H - h0};
-  mainloop<false, false>(acc, smem, A, B, p.Mpad);
+  mainloop<BigShape, false, false>(acc, smem, A, B, p.Mpad);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
@@ -881,7 +875,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
 // dX[m, h] (+)= sum_i dzs[m, i] W[vbase + i, h]: A = dzs (KC), B = W^T (MN), K = kcols.
 // mode 0: write bf16; 1: write fp32 accumulator; 2: accumulate fp32; 3: accumulate and write bf16.
 __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_MAIN];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
   int tm, th;
   tile_coords(blockIdx.x, gridDim.x, p.n_m, p.n_h, 8, tm, th);
   const int m0 = tm * TILE, h0 = th * TILE;
@@ -891,7 +885,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
                   (long)(p.M - m0) * p.ldz};
   const TileSrc B{p.W + (long)p.vbase * p.H + h0, p.H, p.H - h0, p.V - p.vbase,
                   (long)(p.V - p.vbase) * p.H - h0};
-  mainloop<true, false>(acc, smem, A, B, p.kcols);
+  mainloop<BigShape, true, false>(acc, smem, A, B, p.kcols);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
@@ -942,9 +936,9 @@ __global__ void fill_u16_kernel(uint16_t* __restrict__ p, long n) {
 hipError_t launch_fwd_tile(const FwdTileArgs& a, bool ent, hipStream_t s) {
   const unsigned g = (unsigned)((long)a.n_mt * a.n_vt);
   if (ent)
-    fwd_tile_kernel<true><<<g, NTHREADS, 0, s>>>(a);
+    fwd_tile_kernel<FwdShape, true><<<g, NTHREADS, 0, s>>>(a);
   else
-    fwd_tile_kernel<false><<<g, NTHREADS, 0, s>>>(a);
+    fwd_tile_kernel<FwdShape, false><<<g, NTHREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 
