@@ -43,9 +43,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NTHREADS = 256;    // 4 waves of 64 in a 2 x 2 grid over the workgroup tile
 // Pipeline options (tuning builds may override the defaults).
-#ifndef FLCE_DMA_SPREAD
-#define FLCE_DMA_SPREAD 1
-#endif
 #ifndef FLCE_SCHED_PIPE
 #define FLCE_SCHED_PIPE 1
 #endif
@@ -53,8 +50,6 @@ constexpr int NTHREADS = 256;    // 4 waves of 64 in a 2 x 2 grid over the workg
 #define FLCE_FENCE_BARRIER 1
 #endif
 
-// MFMA sub-steps over which a stage's loads are spread (1 = all issued at once).
-constexpr int DMA_SPREAD = FLCE_DMA_SPREAD;
 // Pin the instruction order of a sub-step: the fragment reads of sub-step kk + 1
 // alternate with the first MFMAs of sub-step kk, so each read is issued a whole
 // sub-step before its first use.  Left to itself the scheduler reuses fragment
@@ -88,7 +83,6 @@ struct Shape {
   static_assert(BK == 32 || BK == 64, "K per stage");
   static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole loads per wave");
   static_assert(NST >= 2 && NST <= 3, "stages");
-  static_assert(DMA_SPREAD >= 1 && DMA_SPREAD < KK, "DMA_SPREAD must be 1 .. BK / 16 - 1");
 };
 // One workgroup per CU: 256 x 256 tiles, waves of 128 x 128, 2 x 64 KiB of LDS.
 using BigShape = Shape<256, 256, 64, 2, 1>;
@@ -208,66 +202,65 @@ __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
 // ROWS columns of an MN operand).  The tile is filled by 4 waves x N loads; load j
 // of wave w fills LDS bytes [(w N + j) KiB, + 1 KiB) of the tile, lane i the 16
 // bytes at i * 16.  Each lane's byte offsets relative to the K step's base address
-// do not change from step to step, so they are computed once; only a K step that
-// runs past the end of K re-derives the mask (a uniform branch, taken at most once).
+// do not change from step to step, so they are computed once, together with the K
+// position of the lane's 16 bytes within the step (in 8-element chunks for KC, in
+// K rows for MN, one byte per load).  A step keeps the loads whose K position lies
+// below a uniform limit and turns the others into zero fills, without branches.
 template <bool KC, int ROWS, int BK>
 struct DmaPlan {
   static constexpr int N = ROWS * BK * 2 / 4096;  // loads per wave
   static constexpr int CHUNKS = BK / 8;           // KC: 16-byte chunks per tile row
   static constexpr int GPR = ROWS / 8;            // MN: 16-byte granules per K row
+  static constexpr int KPOS_MAX = KC ? CHUNKS : BK;
   uint32_t voff[N];
+  uint32_t kpos[(N + 3) / 4];
   int wave;
-
-  __device__ __forceinline__ void granule(int j, int& a, int& b) const {
-    const int lane = threadIdx.x & 63;
-    const int G = (wave * N + j) * 64 + lane;  // 16-byte granule of the tile
-    if constexpr (KC) {
-      a = G / CHUNKS;                          // tile row
-      b = (G % CHUNKS) ^ kc_swz<CHUNKS>(a);    // 16-byte chunk of K in the row
-    } else {
-      a = G / GPR;                             // K row
-      b = (G % GPR) ^ ((a & 7) << 1);          // 16-byte chunk of columns
-    }
-  }
 
   __device__ __forceinline__ void init(const TileSrc& s, int wave_id) {
     wave = wave_id;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < (N + 3) / 4; ++q) kpos[q] = 0;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
+      const int G = (wave * N + j) * 64 + lane;  // 16-byte granule of the tile
       int a, b;
-      granule(j, a, b);
+      if constexpr (KC) {
+        a = G / CHUNKS;                          // tile row
+        b = (G % CHUNKS) ^ kc_swz<CHUNKS>(a);    // 16-byte chunk of K in the row
+      } else {
+        a = G / GPR;                             // K row
+        b = (G % GPR) ^ ((a & 7) << 1);          // 16-byte chunk of columns
+      }
       const bool ok = KC ? a < s.valid : 8 * b < s.valid;
       // the load's immediate offset (1 KiB x (j % 4)) is added back by the hardware
       voff[j] = (ok ? (uint32_t)(((long)a * s.ld + 8 * b) * 2) : OOB_OFFSET) - 1024u * (j & 3);
+      kpos[j >> 2] |= (uint32_t)(KC ? b : a) << (8 * (j & 3));
     }
   }
 
-  // offset of load j for the K step at k0; `tail` (uniform) says the step runs past kvalid
-  __device__ __forceinline__ uint32_t at(const TileSrc& s, int k0, int j, bool tail) const {
-    uint32_t v = voff[j];
-    if (tail) {
-      int a, b;
-      granule(j, a, b);
-      const int k = KC ? k0 + 8 * b : k0 + a;
-      if (k >= s.kvalid) v = OOB_OFFSET - 1024u * (j & 3);
-    }
-    return v;
+  // offset of load j in a step of which `lim` K positions exist
+  __device__ __forceinline__ uint32_t off(int j, int lim) const {
+    const uint32_t kp = (kpos[j >> 2] >> (8 * (j & 3))) & 0xffu;
+    return kp < (uint32_t)lim ? voff[j] : OOB_OFFSET - 1024u * (j & 3);
   }
 };
 
-// Per-stage state of one operand's loads.  A K-contiguous tile keeps one buffer
-// base for the whole K loop and moves with the scalar offset (k0 * 2 bytes stays far
-// below 2^31); an M/N-contiguous tile moves its base by k0 rows.
+// Per-step state of one operand's loads.  A K-contiguous tile keeps one buffer base
+// for the whole K loop and moves with the scalar offset (k0 * 2 bytes stays far below
+// 2^31); an M/N-contiguous tile moves its base by k0 rows.  `lim` (uniform) is the
+// number of the step's K positions that exist: 0 for a step past the end of K, whose
+// loads then only zero-fill a free stage.
 struct TileDma {
   i32x4 rsrc;
   uint32_t soff;
   uint32_t lds0;  // LDS byte address of this wave's first 1 KiB block of the tile
-  bool tail;      // the K step runs past kvalid
+  int lim;
 };
 
 template <bool KC, int ROWS, int BK>
 __device__ __forceinline__ TileDma tile_dma(const TileSrc& s, const DmaPlan<KC, ROWS, BK>& plan,
-                                            int k0, const char* lds_tile) {
+                                            int k0, bool active, const char* lds_tile) {
   TileDma d;
   if constexpr (KC) {
     d.rsrc = make_rsrc_fixed(s.base);
@@ -277,63 +270,52 @@ __device__ __forceinline__ TileDma tile_dma(const TileSrc& s, const DmaPlan<KC, 
     d.soff = 0u;
   }
   d.lds0 = lds_addr_of(lds_tile) + (uint32_t)(plan.wave * plan.N * 1024);
-  d.tail = k0 + BK > s.kvalid;
+  const int rem = s.kvalid - k0;  // K extent left from k0 (a multiple of 8 for KC)
+  d.lim = !active ? 0 : KC ? min(max((rem + 7) >> 3, 0), plan.CHUNKS) : min(max(rem, 0), BK);
   return d;
 }
 
-__device__ __forceinline__ void tile_dma_issue_v(const TileDma& d, uint32_t v, int j) {
-  // m0 is rewritten every 4 loads; the 1 KiB steps in between ride on the immediate
+// Load j of a tile.  m0 holds the LDS base of a group of 4 loads; `set_m0` rewrites
+// it (required for the first load issued after any other code that may touch m0 is
+// scheduled in between), the other loads of the group ride on the immediate offset.
+template <bool KC, int ROWS, int BK>
+__device__ __forceinline__ void tile_load(const TileDma& d, const DmaPlan<KC, ROWS, BK>& plan, int j,
+                                          bool set_m0) {
+  const uint32_t v = plan.off(j, d.lim);
+  const uint32_t m0 = d.lds0 + (uint32_t)(j & ~3) * 1024u;
   switch (j & 3) {
-    case 0: dma16<0>(d.rsrc, v, d.soff, d.lds0 + j * 1024); break;
-    case 1: dma16_same_m0<1024>(d.rsrc, v, d.soff); break;
-    case 2: dma16_same_m0<2048>(d.rsrc, v, d.soff); break;
-    default: dma16_same_m0<3072>(d.rsrc, v, d.soff); break;
+    case 0: dma16<0>(d.rsrc, v, d.soff, m0); break;
+    case 1: if (set_m0) dma16<1024>(d.rsrc, v, d.soff, m0); else dma16_same_m0<1024>(d.rsrc, v, d.soff); break;
+    case 2: if (set_m0) dma16<2048>(d.rsrc, v, d.soff, m0); else dma16_same_m0<2048>(d.rsrc, v, d.soff); break;
+    default: if (set_m0) dma16<3072>(d.rsrc, v, d.soff, m0); else dma16_same_m0<3072>(d.rsrc, v, d.soff); break;
   }
 }
 
 template <bool KC, int ROWS, int BK>
 __device__ __forceinline__ void load_tile_async(const TileSrc& s, const DmaPlan<KC, ROWS, BK>& plan,
                                                 int k0, const char* lds_tile) {
-  const TileDma d = tile_dma(s, plan, k0, lds_tile);
+  const TileDma d = tile_dma(s, plan, k0, true, lds_tile);
 #pragma unroll
-  for (int j = 0; j < plan.N; ++j) tile_dma_issue_v(d, plan.at(s, k0, j, d.tail), j);
+  for (int j = 0; j < plan.N; ++j) tile_load(d, plan, j, false);
 }
 
-// The loads of one whole stage (A then B), issued in DMA_SPREAD pieces between
-// MFMA groups.
+// The loads of one whole stage: stage load j < DMA_A is load j of the A tile, the
+// rest are the B tile's.
 template <class S, bool A_KC, bool B_KC>
 struct StageDma {
   using PA = DmaPlan<A_KC, S::TM, S::BK>;
   using PB = DmaPlan<B_KC, S::TN, S::BK>;
   TileDma a, b;
-  const TileSrc* A;
-  const TileSrc* B;
   const PA* pa;
   const PB* pb;
-  int k0;
-  bool active;
-  __device__ __forceinline__ void issue_piece(int piece) {
-    constexpr int PER = (S::DMA_STAGE + DMA_SPREAD - 1) / DMA_SPREAD;
-    if (!active) return;
-    if (__builtin_expect(a.tail || b.tail, 0)) {
-      // the K step runs past the end of K: masks re-derived per load
+  // issue stage loads [j0, j1) back to back
+  __device__ __forceinline__ void issue(int j0, int j1) const {
 #pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const int j = piece * PER + q;
-        if (j < S::DMA_A)
-          tile_dma_issue_v(a, pa->at(*A, k0, j, true), j);
-        else if (j < S::DMA_STAGE)
-          tile_dma_issue_v(b, pb->at(*B, k0, j - S::DMA_A, true), j - S::DMA_A);
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const int j = piece * PER + q;
-        if (j < S::DMA_A)
-          tile_dma_issue_v(a, pa->voff[j], j);
-        else if (j < S::DMA_STAGE)
-          tile_dma_issue_v(b, pb->voff[j - S::DMA_A], j - S::DMA_A);
-      }
+    for (int j = j0; j < j1; ++j) {
+      if (j < S::DMA_A)
+        tile_load(a, *pa, j, j == j0);
+      else
+        tile_load(b, *pb, j - S::DMA_A, j == j0 || j == S::DMA_A);
     }
   }
 };
@@ -431,6 +413,61 @@ __device__ __forceinline__ void wait_stage(int ahead) {
   wait_vmcnt<0>();
 }
 
+// Fragment i of sub-step kk: i < MB is A block i, the others B block i - MB.
+template <class S, bool A_KC, bool B_KC>
+__device__ __forceinline__ void read_frag(bf16x8 (&af)[S::MB], bf16x8 (&bfr)[S::NB],
+                                          const char* stage, const Frags<S, A_KC, B_KC>& f,
+                                          int kk, int i) {
+  if (i < S::MB)
+    af[i] = f.a.read(stage, i, kk);
+  else
+    bfr[i - S::MB] = f.b.read(stage + S::A_BYTES, i - S::MB, kk);
+}
+
+// LDS read instructions of fragments [i0, i1) (a transposing fragment takes two).
+template <class S, bool A_KC, bool B_KC>
+constexpr int frag_read_instrs(int i0, int i1) {
+  int n = 0;
+  for (int i = i0; i < i1; ++i) n += (i < S::MB ? A_KC : B_KC) ? 1 : 2;
+  return n;
+}
+
+// Group g of sub-step 0 of a stage: a share of the fragment reads of sub-step 1,
+// each paired with one of the group's MFMAs, the group's other MFMAs, then a share
+// of the stage's loads.  Scheduling fences keep the loads between the MFMA groups,
+// so the matrix pipe never waits behind a long burst of load issue.
+template <int g, int GROUPS, class S, bool A_KC, bool B_KC>
+__device__ __forceinline__ void substep0_group(f32x16 (&acc)[S::MB][S::NB],
+                                               const bf16x8 (&af)[S::MB], const bf16x8 (&bfr)[S::NB],
+                                               bf16x8 (&af_n)[S::MB], bf16x8 (&bfr_n)[S::NB],
+                                               const char* stage, const Frags<S, A_KC, B_KC>& f,
+                                               const StageDma<S, A_KC, B_KC>& dma) {
+  constexpr int NF = S::MB + S::NB, F = S::MB * S::NB, D = S::DMA_STAGE;
+  constexpr int i0 = g * NF / GROUPS, i1 = (g + 1) * NF / GROUPS;
+  constexpr int m0 = g * F / GROUPS, m1 = (g + 1) * F / GROUPS;
+  constexpr int R = frag_read_instrs<S, A_KC, B_KC>(i0, i1);
+  constexpr int P = R < m1 - m0 ? R : m1 - m0;
+#pragma unroll
+  for (int i = i0; i < i1; ++i) read_frag<S>(af_n, bfr_n, stage, f, 1, i);
+#pragma unroll
+  for (int m = m0; m < m1; ++m) {
+    const int mb = m / S::NB, nb = m % S::NB;
+    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+  }
+  if constexpr (SCHED_PIPE) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    if constexpr (m1 - m0 > P) __builtin_amdgcn_sched_group_barrier(0x008, m1 - m0 - P, 0);
+    if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  dma.issue(g * D / GROUPS, (g + 1) * D / GROUPS);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Pin the instruction order of one MFMA sub-step whose successor's fragments are
 // read during it: (ds_read, MFMA) x R, then the remaining MFMAs.
 template <class S, bool READS>
@@ -457,10 +494,10 @@ __device__ __forceinline__ void sched_substep() {
 // tile in the v_mfma_f32_32x32x16 layout: lane l, element e holds row
 // 8 (e / 4) + 4 (l / 32) + e % 4 and column l % 32.
 //
-// Pipeline: NST LDS stages; at step kt the loads of step kt + NST - 1 are issued
-// into the stage computed at step kt - 1, and the KK MFMA sub-steps of stage kt
-// run with the fragments of sub-step kk + 1 read (into the other register set)
-// while the MFMAs of sub-step kk are issued.  Before the last sub-step the wave
+// Pipeline: NST LDS stages; at step kt the loads of step kt + NST - 1 are issued,
+// between the MFMA groups of sub-step 0, into the stage computed at step kt - 1,
+// and the KK MFMA sub-steps of stage kt run with the fragments of sub-step kk + 1
+// read (into the other register set) while the MFMAs of sub-step kk are issued.  Before the last sub-step the wave
 // waits for its own loads of step kt + 1 and the barrier publishes that stage (and
 // releases stage kt, whose reads have all returned); the first fragments of step
 // kt + 1 are then read under the last sub-step's MFMAs, so no step starts with an
@@ -503,21 +540,20 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
     const int ahead_kt = kt + S::NST - 1;
     char* dst = smem + (ahead_kt % S::NST) * S::STAGE_BYTES;
     const char* cur = smem + (kt % S::NST) * S::STAGE_BYTES;
+    const bool active = ahead_kt < nk;  // a step past K only zero-fills a free stage
+    const int k0n = (active ? ahead_kt : 0) * S::BK;
     StageDma<S, A_KC, B_KC> dma;
-    dma.active = ahead_kt < nk;
-    dma.A = &A;
-    dma.B = &B;
     dma.pa = &plan_a;
     dma.pb = &plan_b;
-    dma.k0 = (ahead_kt < nk ? ahead_kt : 0) * S::BK;
-    if (dma.active) {
-      dma.a = tile_dma(A, plan_a, dma.k0, dst);
-      dma.b = tile_dma(B, plan_b, dma.k0, dst + S::A_BYTES);
-    }
+    dma.a = tile_dma(A, plan_a, k0n, active, dst);
+    dma.b = tile_dma(B, plan_b, k0n, active, dst + S::A_BYTES);
+    substep0_group<0, 4, S>(acc, af[0], bfr[0], af[1], bfr[1], cur, frags, dma);
+    substep0_group<1, 4, S>(acc, af[0], bfr[0], af[1], bfr[1], cur, frags, dma);
+    substep0_group<2, 4, S>(acc, af[0], bfr[0], af[1], bfr[1], cur, frags, dma);
+    substep0_group<3, 4, S>(acc, af[0], bfr[0], af[1], bfr[1], cur, frags, dma);
 #pragma unroll
-    for (int kk = 0; kk < KK - 1; ++kk) {
+    for (int kk = 1; kk < KK - 1; ++kk) {
       read_frags<S>(af[(kk + 1) & 1], bfr[(kk + 1) & 1], cur, frags, kk + 1);
-      if (kk < DMA_SPREAD) dma.issue_piece(kk);
       mfma_block<S::MB, S::NB>(acc, af[kk & 1], bfr[kk & 1]);
       sched_substep<S, true>();
     }
