@@ -8,7 +8,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/flce.h"
+#include "flce.h"
 #include "flce_internal.h"
 
 namespace {

@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "flce_internal.h"
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -49,6 +51,12 @@ constexpr int NTHREADS = 256;    // 4 waves of 64 in a 2 x 2 grid over the workg
 #ifndef FLCE_FENCE_BARRIER
 #define FLCE_FENCE_BARRIER 1
 #endif
+#ifndef FLCE_LOAD_GROUPS
+#define FLCE_LOAD_GROUPS 16
+#endif
+#ifndef FLCE_LOAD_EARLY
+#define FLCE_LOAD_EARLY 8
+#endif
 
 // Pin the instruction order of a sub-step: the fragment reads of sub-step kk + 1
 // alternate with the first MFMAs of sub-step kk, so each read is issued a whole
@@ -56,6 +64,11 @@ constexpr int NTHREADS = 256;    // 4 waves of 64 in a 2 x 2 grid over the workg
 // registers right after their last MFMA and issues each read only one MFMA group
 // ahead, exposing the LDS latency.
 constexpr bool SCHED_PIPE = FLCE_SCHED_PIPE != 0;
+// A stage's loads are issued in LOAD_GROUPS groups per MFMA sub-step, placed
+// between the sub-step's MFMA groups; with two stages, LOAD_EARLY of them under the
+// last sub-step of the step before, the others under sub-step 0.
+constexpr int LOAD_GROUPS = FLCE_LOAD_GROUPS;
+constexpr int LOAD_EARLY = FLCE_LOAD_EARLY;
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // beyond every descriptor's num_records
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format
 
@@ -432,23 +445,24 @@ constexpr int frag_read_instrs(int i0, int i1) {
   return n;
 }
 
-// Group g of sub-step 0 of a stage: a share of the fragment reads of sub-step 1,
-// each paired with one of the group's MFMAs, the group's other MFMAs, then a share
-// of the stage's loads.  Scheduling fences keep the loads between the MFMA groups,
-// so the matrix pipe never waits behind a long burst of load issue.
-template <int g, int GROUPS, class S, bool A_KC, bool B_KC>
-__device__ __forceinline__ void substep0_group(f32x16 (&acc)[S::MB][S::NB],
-                                               const bf16x8 (&af)[S::MB], const bf16x8 (&bfr)[S::NB],
-                                               bf16x8 (&af_n)[S::MB], bf16x8 (&bfr_n)[S::NB],
-                                               const char* stage, const Frags<S, A_KC, B_KC>& f,
-                                               const StageDma<S, A_KC, B_KC>& dma) {
-  constexpr int NF = S::MB + S::NB, F = S::MB * S::NB, D = S::DMA_STAGE;
+// Group g (of GROUPS) of one MFMA sub-step: a share of the fragment reads of
+// sub-step RKK of the stage at `rstage` (the next sub-step), each paired with one
+// of the group's MFMAs, the group's other MFMAs, then a share of the stage loads
+// [JB, JE) of `dma`.  Scheduling fences keep the loads between the MFMA groups, so
+// the matrix pipe never waits behind a long burst of load issue.
+template <int RKK, int g, int GROUPS, int JB, int JE, class S, bool A_KC, bool B_KC>
+__device__ __forceinline__ void substep_group(f32x16 (&acc)[S::MB][S::NB],
+                                              const bf16x8 (&af)[S::MB], const bf16x8 (&bfr)[S::NB],
+                                              bf16x8 (&af_n)[S::MB], bf16x8 (&bfr_n)[S::NB],
+                                              const char* rstage, const Frags<S, A_KC, B_KC>& f,
+                                              const StageDma<S, A_KC, B_KC>& dma) {
+  constexpr int NF = S::MB + S::NB, F = S::MB * S::NB, D = JE - JB;
   constexpr int i0 = g * NF / GROUPS, i1 = (g + 1) * NF / GROUPS;
   constexpr int m0 = g * F / GROUPS, m1 = (g + 1) * F / GROUPS;
   constexpr int R = frag_read_instrs<S, A_KC, B_KC>(i0, i1);
   constexpr int P = R < m1 - m0 ? R : m1 - m0;
 #pragma unroll
-  for (int i = i0; i < i1; ++i) read_frag<S>(af_n, bfr_n, stage, f, 1, i);
+  for (int i = i0; i < i1; ++i) read_frag<S>(af_n, bfr_n, rstage, f, RKK, i);
 #pragma unroll
   for (int m = m0; m < m1; ++m) {
     const int mb = m / S::NB, nb = m % S::NB;
@@ -463,9 +477,23 @@ __device__ __forceinline__ void substep0_group(f32x16 (&acc)[S::MB][S::NB],
     if constexpr (m1 - m0 > P) __builtin_amdgcn_sched_group_barrier(0x008, m1 - m0 - P, 0);
     if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, 0);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  dma.issue(g * D / GROUPS, (g + 1) * D / GROUPS);
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (D > 0) {
+    __builtin_amdgcn_sched_barrier(0);
+    dma.issue(JB + g * D / GROUPS, JB + (g + 1) * D / GROUPS);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Sub-step kk (MFMAs on register set kk % 2) with the reads of sub-step RKK of
+// `rstage` into the other set and stage loads [JB, JE) spread over GROUPS groups.
+template <int kk, int RKK, int GROUPS, int JB, int JE, class S, bool A_KC, bool B_KC, int... G>
+__device__ __forceinline__ void substep_with_loads(f32x16 (&acc)[S::MB][S::NB],
+                                                   bf16x8 (&af)[2][S::MB], bf16x8 (&bfr)[2][S::NB],
+                                                   const char* rstage, const Frags<S, A_KC, B_KC>& f,
+                                                   const StageDma<S, A_KC, B_KC>& dma,
+                                                   std::integer_sequence<int, G...>) {
+  (substep_group<RKK, G, GROUPS, JB, JE, S>(acc, af[kk & 1], bfr[kk & 1], af[(kk + 1) & 1],
+                                            bfr[(kk + 1) & 1], rstage, f, dma), ...);
 }
 
 // Pin the instruction order of one MFMA sub-step whose successor's fragments are
@@ -494,18 +522,20 @@ __device__ __forceinline__ void sched_substep() {
 // tile in the v_mfma_f32_32x32x16 layout: lane l, element e holds row
 // 8 (e / 4) + 4 (l / 32) + e % 4 and column l % 32.
 //
-// Pipeline: NST LDS stages; at step kt the loads of step kt + NST - 1 are issued,
-// between the MFMA groups of sub-step 0, into the stage computed at step kt - 1,
-// and the KK MFMA sub-steps of stage kt run with the fragments of sub-step kk + 1
-// read (into the other register set) while the MFMAs of sub-step kk are issued.  Before the last sub-step the wave
-// waits for its own loads of step kt + 1 and the barrier publishes that stage (and
-// releases stage kt, whose reads have all returned); the first fragments of step
-// kt + 1 are then read under the last sub-step's MFMAs, so no step starts with an
-// LDS-latency bubble.
+// Pipeline: NST LDS stages.  The KK MFMA sub-steps of stage kt run with the
+// fragments of sub-step kk + 1 read (into the other register set) while the MFMAs
+// of sub-step kk are issued.  Before the last sub-step the wave waits for its own
+// loads of step kt + 1 and the barrier publishes that stage and releases stage kt
+// (all of whose reads have returned); the first fragments of step kt + 1 are then
+// read under the last sub-step's MFMAs, so no step starts with an LDS-latency
+// bubble.  The loads of step kt + NST - 1 go out in groups between MFMA groups: with
+// two stages, the first EARLY of them already under the last sub-step of step
+// kt - 1 (right after the barrier freed their stage), the rest under sub-step 0.
 template <class S, bool A_KC, bool B_KC>
 __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem,
                                          const TileSrc& A, const TileSrc& B, int K) {
-  constexpr int KK = S::KK;
+  constexpr int KK = S::KK, D = S::DMA_STAGE;
+  constexpr int EARLY = S::NST == 2 ? (LOAD_EARLY < D ? LOAD_EARLY : D) : 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * S::WM, wc0 = (wave & 1) * S::WN;
 #pragma unroll
@@ -524,33 +554,38 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
   Frags<S, A_KC, B_KC> frags;
   frags.a.init(wr0, lane);
   frags.b.init(wc0, lane);
+  // loads of step st into stage buffer `dst`; a step past K only zero-fills it
+  auto stage_dma = [&](int st, char* dst) {
+    StageDma<S, A_KC, B_KC> d;
+    d.pa = &plan_a;
+    d.pb = &plan_b;
+    const bool active = st < nk;
+    const int k0 = (active ? st : 0) * S::BK;
+    d.a = tile_dma(A, plan_a, k0, active, dst);
+    d.b = tile_dma(B, plan_b, k0, active, dst + S::A_BYTES);
+    return d;
+  };
+  // prologue: steps 0 .. NST - 2, and the early loads of step NST - 1
 #pragma unroll
-  for (int st = 0; st < S::NST - 1; ++st) {
-    if (st < nk) {
-      load_tile_async(A, plan_a, st * S::BK, smem + st * S::STAGE_BYTES);
-      load_tile_async(B, plan_b, st * S::BK, smem + st * S::STAGE_BYTES + S::A_BYTES);
-    }
+  for (int st = 0; st < S::NST - 1; ++st) stage_dma(st, smem + st * S::STAGE_BYTES).issue(0, D);
+  if constexpr (EARLY > 0) {
+    stage_dma(S::NST - 1, smem + (S::NST - 1) * S::STAGE_BYTES).issue(0, EARLY);
+    wait_vmcnt<EARLY>();
+  } else {
+    wait_stage<S>(min(nk - 1, S::NST - 2));
   }
-  wait_stage<S>(min(nk - 1, S::NST - 2));
   __syncthreads();
   static_assert(KK % 2 == 0, "sub-step 0 of every stage uses register set 0");
   bf16x8 af[2][S::MB], bfr[2][S::NB];
   read_frags<S>(af[0], bfr[0], smem, frags, 0);
+  constexpr auto groups = std::make_integer_sequence<int, LOAD_GROUPS>();
   for (int kt = 0; kt < nk; ++kt) {
+    char* cur = smem + (kt % S::NST) * S::STAGE_BYTES;
     const int ahead_kt = kt + S::NST - 1;
-    char* dst = smem + (ahead_kt % S::NST) * S::STAGE_BYTES;
-    const char* cur = smem + (kt % S::NST) * S::STAGE_BYTES;
-    const bool active = ahead_kt < nk;  // a step past K only zero-fills a free stage
-    const int k0n = (active ? ahead_kt : 0) * S::BK;
-    StageDma<S, A_KC, B_KC> dma;
-    dma.pa = &plan_a;
-    dma.pb = &plan_b;
-    dma.a = tile_dma(A, plan_a, k0n, active, dst);
-    dma.b = tile_dma(B, plan_b, k0n, active, dst + S::A_BYTES);
-    substep0_group<0, 4, S>(acc, af[0], bfr[0], af[1], bfr[1], cur, frags, dma);
-    substep0_group<1, 4, S>(acc, af[0], bfr[0], af[1], bfr[1], cur, frags, dma);
-    substep0_group<2, 4, S>(acc, af[0], bfr[0], af[1], bfr[1], cur, frags, dma);
-    substep0_group<3, 4, S>(acc, af[0], bfr[0], af[1], bfr[1], cur, frags, dma);
+    {
+      const StageDma<S, A_KC, B_KC> dma = stage_dma(ahead_kt, smem + (ahead_kt % S::NST) * S::STAGE_BYTES);
+      substep_with_loads<0, 1, LOAD_GROUPS, EARLY, D, S>(acc, af, bfr, cur, frags, dma, groups);
+    }
 #pragma unroll
     for (int kk = 1; kk < KK - 1; ++kk) {
       read_frags<S>(af[(kk + 1) & 1], bfr[(kk + 1) & 1], cur, frags, kk + 1);
@@ -565,9 +600,21 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
     wait_stage<S>(min(max(nk - 1 - (kt + 1), 0), S::NST - 2));
     __syncthreads();
     // (after the last step this reads a stale stage; the values are never used)
-    read_frags<S>(af[0], bfr[0], smem + ((kt + 1) % S::NST) * S::STAGE_BYTES, frags, 0);
-    mfma_block<S::MB, S::NB>(acc, af[1], bfr[1]);
-    sched_substep<S, true>();
+    const char* next = smem + ((kt + 1) % S::NST) * S::STAGE_BYTES;
+    if constexpr (EARLY > 0) {
+      // stage kt is free now: it receives step kt + 2
+      const StageDma<S, A_KC, B_KC> dma = stage_dma(kt + 2, cur);
+      substep_with_loads<KK - 1, 0, LOAD_GROUPS, 0, EARLY, S>(acc, af, bfr, next, frags, dma, groups);
+    } else {
+      read_frags<S>(af[0], bfr[0], next, frags, 0);
+      mfma_block<S::MB, S::NB>(acc, af[1], bfr[1]);
+      sched_substep<S, true>();
+    }
+  }
+  if constexpr (EARLY > 0) {
+    // the zero fills issued under the last step must land before the caller reuses LDS
+    wait_vmcnt<0>();
+    __syncthreads();
   }
 }
 
