@@ -95,10 +95,16 @@ struct Shape {
   static_assert(MB >= 2 && MB % 2 == 0 && NB >= 1, "wave tile");
   static_assert(BK == 32 || BK == 64, "K per stage");
   static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole loads per wave");
-  static_assert(NST >= 2 && NST <= 3, "stages");
+  static_assert(NST >= 2 && NST <= 4, "stages");
 };
-// One workgroup per CU: 256 x 256 tiles, waves of 128 x 128, 2 x 64 KiB of LDS.
-using BigShape = Shape<256, 256, 64, 2, 1>;
+#ifndef FLCE_BIG_BK
+#define FLCE_BIG_BK 64
+#endif
+#ifndef FLCE_BIG_NST
+#define FLCE_BIG_NST 2
+#endif
+// One workgroup per CU: 256 x 256 tiles, waves of 128 x 128, 128 KiB of LDS stages.
+using BigShape = Shape<256, 256, FLCE_BIG_BK, FLCE_BIG_NST, 1>;
 // Two workgroups per CU: 128 x 256 tiles, waves of 64 x 128, 3 x 24 KiB of LDS.
 using PairShape = Shape<128, 256, 32, 3, 2>;
 
@@ -416,16 +422,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-// Wait until the loads of the stage after the one just computed have landed, given
-// that `ahead` later stages (0 .. NST - 2) may still be in flight.
-template <class S>
-__device__ __forceinline__ void wait_stage(int ahead) {
-  if constexpr (S::NST >= 3) {
-    if (ahead >= 1) { wait_vmcnt<S::DMA_STAGE>(); return; }
-  }
-  wait_vmcnt<0>();
-}
-
 // Fragment i of sub-step kk: i < MB is A block i, the others B block i - MB.
 template <class S, bool A_KC, bool B_KC>
 __device__ __forceinline__ void read_frag(bf16x8 (&af)[S::MB], bf16x8 (&bfr)[S::NB],
@@ -528,14 +524,17 @@ __device__ __forceinline__ void sched_substep() {
 // loads of step kt + 1 and the barrier publishes that stage and releases stage kt
 // (all of whose reads have returned); the first fragments of step kt + 1 are then
 // read under the last sub-step's MFMAs, so no step starts with an LDS-latency
-// bubble.  The loads of step kt + NST - 1 go out in groups between MFMA groups: with
-// two stages, the first EARLY of them already under the last sub-step of step
-// kt - 1 (right after the barrier freed their stage), the rest under sub-step 0.
+// bubble.  The loads of step kt + NST go out in groups between MFMA groups: the
+// first EARLY of them under the last sub-step of step kt, right after the barrier
+// freed their stage, the rest under sub-step 0 of step kt + 1.  Every step issues
+// the same number of loads (steps past K only zero-fill their stage), so the wait
+// before each barrier is a fixed count.
 template <class S, bool A_KC, bool B_KC>
 __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem,
                                          const TileSrc& A, const TileSrc& B, int K) {
-  constexpr int KK = S::KK, D = S::DMA_STAGE;
-  constexpr int EARLY = S::NST == 2 ? (LOAD_EARLY < D ? LOAD_EARLY : D) : 0;
+  constexpr int KK = S::KK, D = S::DMA_STAGE, NST = S::NST;
+  constexpr int EARLY = LOAD_EARLY < D ? LOAD_EARLY : D;
+  static_assert((NST - 2) * D + EARLY < 64, "vmcnt range");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * S::WM, wc0 = (wave & 1) * S::WN;
 #pragma unroll
@@ -565,25 +564,21 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
     d.b = tile_dma(B, plan_b, k0, active, dst + S::A_BYTES);
     return d;
   };
+  auto stage_at = [&](int st) { return smem + (st % NST) * S::STAGE_BYTES; };
   // prologue: steps 0 .. NST - 2, and the early loads of step NST - 1
 #pragma unroll
-  for (int st = 0; st < S::NST - 1; ++st) stage_dma(st, smem + st * S::STAGE_BYTES).issue(0, D);
-  if constexpr (EARLY > 0) {
-    stage_dma(S::NST - 1, smem + (S::NST - 1) * S::STAGE_BYTES).issue(0, EARLY);
-    wait_vmcnt<EARLY>();
-  } else {
-    wait_stage<S>(min(nk - 1, S::NST - 2));
-  }
+  for (int st = 0; st < NST - 1; ++st) stage_dma(st, stage_at(st)).issue(0, D);
+  if constexpr (EARLY > 0) stage_dma(NST - 1, stage_at(NST - 1)).issue(0, EARLY);
+  wait_vmcnt<(NST - 2) * D + EARLY>();  // step 0 has landed
   __syncthreads();
   static_assert(KK % 2 == 0, "sub-step 0 of every stage uses register set 0");
   bf16x8 af[2][S::MB], bfr[2][S::NB];
   read_frags<S>(af[0], bfr[0], smem, frags, 0);
   constexpr auto groups = std::make_integer_sequence<int, LOAD_GROUPS>();
   for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt % S::NST) * S::STAGE_BYTES;
-    const int ahead_kt = kt + S::NST - 1;
+    char* cur = stage_at(kt);
     {
-      const StageDma<S, A_KC, B_KC> dma = stage_dma(ahead_kt, smem + (ahead_kt % S::NST) * S::STAGE_BYTES);
+      const StageDma<S, A_KC, B_KC> dma = stage_dma(kt + NST - 1, stage_at(kt + NST - 1));
       substep_with_loads<0, 1, LOAD_GROUPS, EARLY, D, S>(acc, af, bfr, cur, frags, dma, groups);
     }
 #pragma unroll
@@ -596,14 +591,14 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
     // keep the barrier after every MFMA issued so far (the compiler would hoist it)
     __builtin_amdgcn_sched_barrier(0);
 #endif
-    // stages issued after step kt + 1 that may still be in flight
-    wait_stage<S>(min(max(nk - 1 - (kt + 1), 0), S::NST - 2));
+    // the loads of steps kt + 2 .. kt + NST - 1 may still be in flight
+    wait_vmcnt<(NST - 2) * D>();
     __syncthreads();
     // (after the last step this reads a stale stage; the values are never used)
-    const char* next = smem + ((kt + 1) % S::NST) * S::STAGE_BYTES;
+    const char* next = stage_at(kt + 1);
     if constexpr (EARLY > 0) {
-      // stage kt is free now: it receives step kt + 2
-      const StageDma<S, A_KC, B_KC> dma = stage_dma(kt + 2, cur);
+      // stage kt is free now: it receives step kt + NST
+      const StageDma<S, A_KC, B_KC> dma = stage_dma(kt + NST, cur);
       substep_with_loads<KK - 1, 0, LOAD_GROUPS, 0, EARLY, S>(acc, af, bfr, next, frags, dma, groups);
     } else {
       read_frags<S>(af[0], bfr[0], next, frags, 0);
@@ -611,11 +606,9 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
       sched_substep<S, true>();
     }
   }
-  if constexpr (EARLY > 0) {
-    // the zero fills issued under the last step must land before the caller reuses LDS
-    wait_vmcnt<0>();
-    __syncthreads();
-  }
+  // the zero fills issued under the last steps must land before the caller reuses LDS
+  wait_vmcnt<0>();
+  __syncthreads();
 }
 
 // Row of the wave tile held by lane `lane` in element e of a 32 x 32 block.
@@ -623,45 +616,57 @@ __device__ __forceinline__ int acc_row(int lane, int e) {
   return ((e >> 2) << 3) + ((lane >> 5) << 2) + (e & 3);
 }
 
-__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+// DPP move within rows of 16 lanes: row_shl:N (CTRL 0x100 + N) gives lane i the value
+// of lane i + N, row_shr:N (CTRL 0x110 + N) that of lane i - N; a lane whose source
+// lies outside its row reads 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+
+// v_permlane16_swap_b32: rows 1 and 3 of a (lanes 16-31, 48-63) trade places with
+// rows 0 and 2 of b, so that afterwards a holds (own a | b of lane - 16) and b holds
+// (a of lane + 16 | own b).  Issued as inline assembly because the compiler builtin
+// hands back only the first register; the s_nop pads cover the VALU hazards around it.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+// One butterfly level of the reduce-scatter for lane distance s < 16: a lane with bit
+// s clear keeps the low half of each pair and combines it with its partner's
+// (lane + s, a row_shl), a lane with bit s set the high half (lane - s, a row_shr).
+template <int s, int P, class Op>
+__device__ __forceinline__ void rs_level(float (&v)[32 * P], bool upper, Op op) {
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int i = 0; i < s; ++i) {
+      const float lo = v[32 * p + i], hi = v[32 * p + i + s];
+      const float tl = op(lo, dpp_mov<0x100 + s>(lo));
+      const float th = op(hi, dpp_mov<0x110 + s>(hi));
+      v[32 * p + i] = upper ? th : tl;
+    }
+}
 
 // Reduce-scatter over the 32 lanes of a half-wave.  v holds 32 P values, entry
 // 32 p + j being slot j of group p.  On exit v[32 p] holds the reduction over the
-// half-wave of slot (lane % 32) of group p.
+// half-wave of slot (lane % 32) of group p.  Lanes l and l ^ 16 meet through the
+// row swap, the closer pairs through DPP row shifts; no LDS traffic.
 template <int P, class Op>
 __device__ __forceinline__ void reduce_scatter32(float (&v)[32 * P], int lane, Op op) {
 #pragma unroll
-  for (int s = 16; s >= 1; s >>= 1) {
-    const bool upper = (lane & s) != 0;
+  for (int p = 0; p < P; ++p)
 #pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-      for (int i = 0; i < s; ++i) {
-        const float lo = v[32 * p + i], hi = v[32 * p + i + s];
-        const float send = upper ? lo : hi;
-        const float keep = upper ? hi : lo;
-        v[32 * p + i] = op(keep, shfl_xor(send, s));
-      }
-  }
-}
-
-// Inverse distribution: v[32 p] holds slot (lane % 32) of group p; on exit every
-// lane holds all 32 slots of every group.
-template <int P>
-__device__ __forceinline__ void all_gather32(float (&v)[32 * P], int lane) {
-#pragma unroll
-  for (int s = 1; s <= 16; s <<= 1) {
-    const bool upper = (lane & s) != 0;
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-      for (int i = 0; i < s; ++i) {
-        const float mine = v[32 * p + i];
-        const float other = shfl_xor(mine, s);
-        v[32 * p + i] = upper ? other : mine;
-        v[32 * p + i + s] = upper ? mine : other;
-      }
-  }
+    for (int i = 0; i < 16; ++i) {
+      float a = v[32 * p + i], b = v[32 * p + i + 16];
+      swap16(a, b);
+      v[32 * p + i] = op(a, b);
+    }
+  rs_level<8, P>(v, (lane & 8) != 0, op);
+  rs_level<4, P>(v, (lane & 4) != 0, op);
+  rs_level<2, P>(v, (lane & 2) != 0, op);
+  rs_level<1, P>(v, (lane & 1) != 0, op);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -693,140 +698,189 @@ __device__ __forceinline__ uint16_t* out_slot(char* lo, char* hi, int rl, int cl
 }
 
 // ---------------------------------------------------------------------------
-// Forward tile kernel.  Per wave: lane l holds, for row slot q = 16 mb + e (16 MB of
-// them), the NB columns 32 nb + l % 32 of its wave tile.  The wave reduces its WN
-// columns per row (max, then shifted sums); the two waves sharing rows are merged
-// through LDS and thread t < TM writes the partials of tile row t.
+// Forward tile kernel.
+//
+// Per-lane extreme of each row slot q = 16 mb + e over the lane's NB columns, on
+// sgn * acc (sgn = -1 if NEG): the row maximum of z = scale * acc is |scale| times
+// the maximum of sgn(scale) * acc.  In a RAGGED tile columns past V are skipped
+// (bit nb of colmask: column 32 nb + lane % 32 of the wave tile exists).
+template <bool NEG, bool RAGGED, class S>
+__device__ __forceinline__ void lane_row_max(const f32x16 (&acc)[S::MB][S::NB],
+                                             float (&mx)[16 * S::MB], unsigned colmask) {
+#pragma unroll
+  for (int mb = 0; mb < S::MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb) {
+        const float a = NEG ? -acc[mb][nb][e] : acc[mb][nb][e];
+        m = fmaxf(m, RAGGED && !((colmask >> nb) & 1u) ? -INFINITY : a);
+      }
+      mx[16 * mb + e] = m;
+    }
+}
+
+// Shifted sums of each row slot over the lane's NB columns, in log2 units:
+// s = sum 2^d and u = sum 2^d d with d = c1 acc - m2 (c1 = scale log2 e, m2 = the
+// row maximum of c1 acc, read for both column halves from `red`).
+template <bool ENT, bool RAGGED, class S>
+__device__ __forceinline__ void lane_row_sums(const f32x16 (&acc)[S::MB][S::NB], const float* red,
+                                              int wr0, int lane, float c1, unsigned colmask,
+                                              float (&sv)[16 * S::MB],
+                                              float (&uv)[ENT ? 16 * S::MB : 1]) {
+  const float ac1 = fabsf(c1);
+#pragma unroll
+  for (int mb = 0; mb < S::MB; ++mb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // rows 8 q + 4 (lane / 32) + 0..3 of block mb: slots e = 4 q + 0..3
+      const int rb = wr0 + 32 * mb + 8 * q + 4 * (lane >> 5);
+      const float4 h0 = *reinterpret_cast<const float4*>(red + rb);
+      const float4 h1 = *reinterpret_cast<const float4*>(red + S::TM + rb);
+      const float mh[4] = {fmaxf(h0.x, h1.x), fmaxf(h0.y, h1.y), fmaxf(h0.z, h1.z), fmaxf(h0.w, h1.w)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = 4 * q + j;
+        const float nm2 = -ac1 * mh[j];
+        float s = 0.f, u = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < S::NB; ++nb) {
+          float d = fmaf(acc[mb][nb][e], c1, nm2);
+          if constexpr (RAGGED) d = ((colmask >> nb) & 1u) ? d : -INFINITY;
+          const float pe = __builtin_amdgcn_exp2f(d);
+          s += pe;
+          if constexpr (ENT) u = fmaf(pe, RAGGED ? fmaxf(d, -3.0e38f) : d, u);
+        }
+        sv[16 * mb + e] = s;
+        if constexpr (ENT) uv[16 * mb + e] = u;
+      }
+    }
+}
+
+// One workgroup per (TM-row, TN-column) tile of the logits.  Per wave, lane l holds
+// for row slot q = 16 mb + e (16 MB of them) the NB columns 32 nb + l % 32 of its
+// wave tile.  The row maximum over the tile's TN columns is formed first (lane, then
+// half-wave, then the two waves sharing the rows through LDS), so both column halves
+// sum against the same shift and their partials simply add; thread t < TM writes the
+// partials of tile row t.
 template <class S, bool ENT>
 __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(FwdTileArgs p) {
-  constexpr int TM = S::TM, TN = S::TN, MB = S::MB, NB = S::NB, WN = S::WN;
+  constexpr int TM = S::TM, TN = S::TN, MB = S::MB, NB = S::NB, WM = S::WM, WN = S::WN;
   constexpr int P = MB / 2;  // groups of 32 row slots per lane
+  constexpr int NW = NTHREADS / 64;
   __shared__ __attribute__((aligned(1024))) char smem[S::PIPE_BYTES];
-  __shared__ int t_local[TM];
-  static_assert(6 * TM * 4 <= S::PIPE_BYTES, "row merge buffer");
+  __shared__ __attribute__((aligned(16))) int t_col[TM];  // tile column of the row's target, or -1
+  __shared__ unsigned t_hits[NW];  // bit w: wave w's rectangle holds a target (per producer wave)
+  static_assert(6 * TM * 4 <= S::PIPE_BYTES, "epilogue buffers");
+  static_assert(NW == 4 && TM / WM * (TN / WN) == NW, "one bit per wave rectangle");
   int mt, vt;
   tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, FWD_GROUP_M, mt, vt);
   const int row0 = mt * TM, col0 = vt * TN;
-  const int tid = threadIdx.x;
-  if (tid < TM) {
-    // target column relative to this tile, or -1 if no valid target lies in it
-    const int r = row0 + tid;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  {
     int tl = -1;
-    if (r < p.M) {
+    const int r = row0 + tid;
+    if (tid < TM && r < p.M) {
       const int64_t t = p.targets[r];
-      if (t != p.ignore_index && t >= col0 && t < min<int64_t>(col0 + TN, p.V))
-        tl = (int)(t - col0);
+      const int64_t hi = col0 + TN < p.V ? col0 + TN : p.V;
+      if (t != p.ignore_index && t >= col0 && t < hi) tl = (int)(t - col0);
     }
-    t_local[tid] = tl;
+    if (tid < TM) t_col[tid] = tl;
+    // the wave rectangle (rows of half tid / WM, columns of half tl / WN) holding it
+    const int owner = tl >= 0 ? 2 * (tid / WM) + tl / WN : -1;
+    unsigned bits = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) bits |= (__ballot(owner == w) != 0ull ? 1u : 0u) << w;
+    if (lane == 0) t_hits[wave] = bits;
   }
 
   f32x16 acc[MB][NB];
   const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, (long)(p.M - row0) * p.H};
   const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, (long)(p.V - col0) * p.H};
   mainloop<S, true, true>(acc, smem, A, B, p.H);
+  // (the mainloop ends with a barrier: t_list is complete and the LDS stages are free)
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wr0 = (wave >> 1) * S::WM, wc0 = (wave & 1) * WN;
+  const int wr0 = (wave >> 1) * WM, wc0 = (wave & 1) * WN, wn = wave & 1;
   const int lc = lane & 31;
-  const float c1 = p.scale * LOG2E;  // logits in log2 units: z2 = acc * c1
-  const bool ragged = col0 + TN > p.V;
+  const float c1 = p.scale * LOG2E;  // logits in log2 units: z2 = c1 acc
 
-  // scale into log2 units; columns past V become -inf (only the last V tile has any)
+  // target logits: in a wave whose rectangle holds one, the lane holding (row,
+  // target column) writes z = scale * acc
+  unsigned hits = 0;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const bool colok = !ragged || (col0 + wc0 + 32 * nb + lc < p.V);
+  for (int w = 0; w < NW; ++w) hits |= t_hits[w];
+  if ((__builtin_amdgcn_readfirstlane(hits) >> wave) & 1u) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[mb][nb][e] = colok ? acc[mb][nb][e] * c1 : -INFINITY;
+      for (int q = 0; q < 4; ++q) {
+        const int rb = wr0 + 32 * mb + 8 * q + 4 * (lane >> 5);
+        const int4 tc = *reinterpret_cast<const int4*>(t_col + rb);
+        const int tcs[4] = {tc.x, tc.y, tc.z, tc.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int dd = tcs[j] - wc0 - lc;  // 32 nb if this lane holds the target column
+          if ((unsigned)dd < (unsigned)WN && (dd & 31) == 0) {
+            float z = acc[mb][0][4 * q + j];
+#pragma unroll
+            for (int nb = 1; nb < NB; ++nb) z = (dd >> 5) == nb ? acc[mb][nb][4 * q + j] : z;
+            p.zt[row0 + rb + j] = z * p.scale;
+          }
+        }
+      }
   }
 
-  // target logit: the unique lane holding column t[row] writes z[row, t]
+  const bool ragged = col0 + TN > p.V;
+  unsigned colmask = 0;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rl = wr0 + 32 * mb + acc_row(lane, e);
-      const int d = t_local[rl] - wc0 - lc;
-      if (d >= 0 && d < WN && (d & 31) == 0) {
-        float z = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          if ((d >> 5) == nb) z = acc[mb][nb][e];
-        p.zt[row0 + rl] = z * LN2;
-      }
-    }
+  for (int nb = 0; nb < NB; ++nb) colmask |= (col0 + wc0 + 32 * nb + lc < p.V ? 1u : 0u) << nb;
 
-  // row maxima of the wave's WN columns
-  float mx[32 * P];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float m = acc[mb][0][e];
-#pragma unroll
-      for (int nb = 1; nb < NB; ++nb) m = fmaxf(m, acc[mb][nb][e]);
-      mx[16 * mb + e] = m;
+  // row maxima of sgn(c1) acc: lane, half-wave, then both column halves via LDS
+  float* red = reinterpret_cast<float*>(smem);  // [2 halves][TM]
+  {
+    float mx[32 * P];
+    if (!ragged) {
+      if (c1 >= 0.f) lane_row_max<false, false, S>(acc, mx, colmask);
+      else lane_row_max<true, false, S>(acc, mx, colmask);
+    } else {
+      if (c1 >= 0.f) lane_row_max<false, true, S>(acc, mx, colmask);
+      else lane_row_max<true, true, S>(acc, mx, colmask);
     }
-  reduce_scatter32<P>(mx, lane, [](float a, float b) { return fmaxf(a, b); });
-  float my_max[P];
+    reduce_scatter32<P>(mx, lane, [](float a, float b) { return fmaxf(a, b); });
 #pragma unroll
-  for (int pp = 0; pp < P; ++pp) my_max[pp] = mx[32 * pp];
-  all_gather32<P>(mx, lane);
+    for (int pp = 0; pp < P; ++pp) {
+      const int mb = 2 * pp + (lc >> 4), e = lc & 15;
+      red[wn * TM + wr0 + 32 * mb + acc_row(lane, e)] = mx[32 * pp];
+    }
+  }
+  __syncthreads();
 
-  // shifted sums s = sum exp2(z2 - m2) and u = sum exp2(z2 - m2) (z2 - m2); a row
-  // with no column in this wave (ragged tile) keeps m = -inf, s = u = 0
+  // shifted sums against the full-row maximum
   float sv[32 * P], uv[ENT ? 32 * P : 1];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float m = mx[16 * mb + e];
-      const float mref = m == -INFINITY ? 0.f : m;
-      float s = 0.f, u = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float d = acc[mb][nb][e] - mref;
-        const float pe = __builtin_amdgcn_exp2f(d);
-        s += pe;
-        if constexpr (ENT) u += pe * fmaxf(d, -3.0e38f);
-      }
-      sv[16 * mb + e] = s;
-      if constexpr (ENT) uv[16 * mb + e] = u;
-    }
+  if (!ragged)
+    lane_row_sums<ENT, false, S>(acc, red, wr0, lane, c1, colmask, sv, uv);
+  else
+    lane_row_sums<ENT, true, S>(acc, red, wr0, lane, c1, colmask, sv, uv);
   reduce_scatter32<P>(sv, lane, [](float a, float b) { return a + b; });
   if constexpr (ENT) reduce_scatter32<P>(uv, lane, [](float a, float b) { return a + b; });
 
-  // merge the two column halves of each row through LDS (the stages are free now)
-  float* comb = reinterpret_cast<float*>(smem);  // [2 halves][3 stats][TM rows]
-  const int wn = wave & 1;
+  float* comb = red + 2 * TM;  // [2 halves][2 stats][TM]
 #pragma unroll
   for (int pp = 0; pp < P; ++pp) {
-    const int j = lc;
-    const int mb = 2 * pp + (j >> 4), e = j & 15;
+    const int mb = 2 * pp + (lc >> 4), e = lc & 15;
     const int rl = wr0 + 32 * mb + acc_row(lane, e);
-    comb[(wn * 3 + 0) * TM + rl] = my_max[pp] * LN2;
-    comb[(wn * 3 + 1) * TM + rl] = sv[32 * pp];
-    comb[(wn * 3 + 2) * TM + rl] = ENT ? uv[ENT ? 32 * pp : 0] * LN2 : 0.f;
+    comb[(wn * 2 + 0) * TM + rl] = sv[32 * pp];
+    if constexpr (ENT) comb[(wn * 2 + 1) * TM + rl] = uv[32 * pp];
   }
   __syncthreads();
   if (tid < TM) {
-    const float m0 = comb[0 * TM + tid], s0 = comb[1 * TM + tid], u0 = comb[2 * TM + tid];
-    const float m1 = comb[3 * TM + tid], s1 = comb[4 * TM + tid], u1 = comb[5 * TM + tid];
-    float m, s, u;
-    if (s1 == 0.f) {
-      m = m0; s = s0; u = u0;
-    } else {
-      m = fmaxf(m0, m1);
-      const float d0 = m0 - m, d1 = m1 - m;
-      const float a0 = __expf(d0), a1 = __expf(d1);
-      s = s0 * a0 + s1 * a1;
-      u = a0 * (u0 + d0 * s0) + a1 * (u1 + d1 * s1);
-    }
+    const float m2 = fabsf(c1) * fmaxf(red[tid], red[TM + tid]);
     const long off = (long)vt * p.Mpad + row0 + tid;
-    p.part_m[off] = m;
-    p.part_s[off] = s;
-    if constexpr (ENT) p.part_u[off] = u;
+    p.part_m[off] = m2 * LN2;
+    p.part_s[off] = comb[0 * TM + tid] + comb[2 * TM + tid];
+    if constexpr (ENT) p.part_u[off] = (comb[1 * TM + tid] + comb[3 * TM + tid]) * LN2;
   }
 }
 
