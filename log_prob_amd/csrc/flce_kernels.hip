@@ -122,10 +122,11 @@ static_assert(FwdShape::TM == kFwdTileM && FwdShape::TN == kFwdTileN, "host and 
 constexpr int FWD_GROUP_M = FLCE_FWD_GROUP_M;  // forward tile rows per L2 group
 
 // The backward kernels run BigShape; their epilogues stage a 256 x 256 bf16 output
-// tile in the LDS the pipeline stages used.
+// tile (128 KiB) in the LDS the pipeline used.
 constexpr int TILE = BigShape::TM;
-constexpr int LDS_BIG = 2 * TILE * TILE;
-static_assert(BigShape::TN == TILE && BigShape::PIPE_BYTES <= LDS_BIG, "backward LDS");
+constexpr int LDS_OUT = 2 * TILE * TILE;
+constexpr int LDS_BIG = BigShape::PIPE_BYTES > LDS_OUT ? BigShape::PIPE_BYTES : LDS_OUT;
+static_assert(BigShape::TN == TILE, "backward tile");
 
 // ---------------------------------------------------------------------------
 // Tile coordinates.  Workgroups are handed to the 8 XCDs round robin, so id b runs
@@ -394,14 +395,19 @@ struct Frags {
   FragPlan<B_KC, S::NB, S::TN, S::BK> b;
 };
 
+// The LDS tiles of one K step: A and B operand tiles.
+struct StagePtr {
+  const char* a;
+  const char* b;
+};
+
 template <class S, bool A_KC, bool B_KC>
 __device__ __forceinline__ void read_frags(bf16x8 (&af)[S::MB], bf16x8 (&bfr)[S::NB],
-                                           const char* stage, const Frags<S, A_KC, B_KC>& f,
-                                           int kk) {
+                                           StagePtr stage, const Frags<S, A_KC, B_KC>& f, int kk) {
 #pragma unroll
-  for (int mb = 0; mb < S::MB; ++mb) af[mb] = f.a.read(stage, mb, kk);
+  for (int mb = 0; mb < S::MB; ++mb) af[mb] = f.a.read(stage.a, mb, kk);
 #pragma unroll
-  for (int nb = 0; nb < S::NB; ++nb) bfr[nb] = f.b.read(stage + S::A_BYTES, nb, kk);
+  for (int nb = 0; nb < S::NB; ++nb) bfr[nb] = f.b.read(stage.b, nb, kk);
 }
 
 template <int MB, int NB>
@@ -425,12 +431,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Fragment i of sub-step kk: i < MB is A block i, the others B block i - MB.
 template <class S, bool A_KC, bool B_KC>
 __device__ __forceinline__ void read_frag(bf16x8 (&af)[S::MB], bf16x8 (&bfr)[S::NB],
-                                          const char* stage, const Frags<S, A_KC, B_KC>& f,
-                                          int kk, int i) {
+                                          StagePtr stage, const Frags<S, A_KC, B_KC>& f, int kk,
+                                          int i) {
   if (i < S::MB)
-    af[i] = f.a.read(stage, i, kk);
+    af[i] = f.a.read(stage.a, i, kk);
   else
-    bfr[i - S::MB] = f.b.read(stage + S::A_BYTES, i - S::MB, kk);
+    bfr[i - S::MB] = f.b.read(stage.b, i - S::MB, kk);
 }
 
 // LDS read instructions of fragments [i0, i1) (a transposing fragment takes two).
@@ -446,12 +452,12 @@ constexpr int frag_read_instrs(int i0, int i1) {
 // of the group's MFMAs, the group's other MFMAs, then a share of the stage loads
 // [JB, JE) of `dma`.  Scheduling fences keep the loads between the MFMA groups, so
 // the matrix pipe never waits behind a long burst of load issue.
-template <int RKK, int g, int GROUPS, int JB, int JE, class S, bool A_KC, bool B_KC>
+template <int RKK, int g, int GROUPS, int JB, int JE, class S, bool A_KC, bool B_KC, class Ops>
 __device__ __forceinline__ void substep_group(f32x16 (&acc)[S::MB][S::NB],
                                               const bf16x8 (&af)[S::MB], const bf16x8 (&bfr)[S::NB],
                                               bf16x8 (&af_n)[S::MB], bf16x8 (&bfr_n)[S::NB],
-                                              const char* rstage, const Frags<S, A_KC, B_KC>& f,
-                                              const StageDma<S, A_KC, B_KC>& dma) {
+                                              StagePtr rstage, const Frags<S, A_KC, B_KC>& f,
+                                              Ops& dma) {
   constexpr int NF = S::MB + S::NB, F = S::MB * S::NB, D = JE - JB;
   constexpr int i0 = g * NF / GROUPS, i1 = (g + 1) * NF / GROUPS;
   constexpr int m0 = g * F / GROUPS, m1 = (g + 1) * F / GROUPS;
@@ -482,11 +488,12 @@ __device__ __forceinline__ void substep_group(f32x16 (&acc)[S::MB][S::NB],
 
 // Sub-step kk (MFMAs on register set kk % 2) with the reads of sub-step RKK of
 // `rstage` into the other set and stage loads [JB, JE) spread over GROUPS groups.
-template <int kk, int RKK, int GROUPS, int JB, int JE, class S, bool A_KC, bool B_KC, int... G>
+template <int kk, int RKK, int GROUPS, int JB, int JE, class S, bool A_KC, bool B_KC, class Ops,
+          int... G>
 __device__ __forceinline__ void substep_with_loads(f32x16 (&acc)[S::MB][S::NB],
                                                    bf16x8 (&af)[2][S::MB], bf16x8 (&bfr)[2][S::NB],
-                                                   const char* rstage, const Frags<S, A_KC, B_KC>& f,
-                                                   const StageDma<S, A_KC, B_KC>& dma,
+                                                   StagePtr rstage, const Frags<S, A_KC, B_KC>& f,
+                                                   Ops& dma,
                                                    std::integer_sequence<int, G...>) {
   (substep_group<RKK, G, GROUPS, JB, JE, S>(acc, af[kk & 1], bfr[kk & 1], af[(kk + 1) & 1],
                                             bfr[(kk + 1) & 1], rstage, f, dma), ...);
@@ -565,6 +572,7 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
     return d;
   };
   auto stage_at = [&](int st) { return smem + (st % NST) * S::STAGE_BYTES; };
+  auto tiles_at = [&](int st) { return StagePtr{stage_at(st), stage_at(st) + S::A_BYTES}; };
   // prologue: steps 0 .. NST - 2, and the early loads of step NST - 1
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st) stage_dma(st, stage_at(st)).issue(0, D);
@@ -573,12 +581,12 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
   __syncthreads();
   static_assert(KK % 2 == 0, "sub-step 0 of every stage uses register set 0");
   bf16x8 af[2][S::MB], bfr[2][S::NB];
-  read_frags<S>(af[0], bfr[0], smem, frags, 0);
+  read_frags<S>(af[0], bfr[0], tiles_at(0), frags, 0);
   constexpr auto groups = std::make_integer_sequence<int, LOAD_GROUPS>();
   for (int kt = 0; kt < nk; ++kt) {
-    char* cur = stage_at(kt);
+    const StagePtr cur = tiles_at(kt);
     {
-      const StageDma<S, A_KC, B_KC> dma = stage_dma(kt + NST - 1, stage_at(kt + NST - 1));
+      StageDma<S, A_KC, B_KC> dma = stage_dma(kt + NST - 1, stage_at(kt + NST - 1));
       substep_with_loads<0, 1, LOAD_GROUPS, EARLY, D, S>(acc, af, bfr, cur, frags, dma, groups);
     }
 #pragma unroll
@@ -595,10 +603,10 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
     wait_vmcnt<(NST - 2) * D>();
     __syncthreads();
     // (after the last step this reads a stale stage; the values are never used)
-    const char* next = stage_at(kt + 1);
+    const StagePtr next = tiles_at(kt + 1);
     if constexpr (EARLY > 0) {
       // stage kt is free now: it receives step kt + NST
-      const StageDma<S, A_KC, B_KC> dma = stage_dma(kt + NST, cur);
+      StageDma<S, A_KC, B_KC> dma = stage_dma(kt + NST, stage_at(kt));
       substep_with_loads<KK - 1, 0, LOAD_GROUPS, 0, EARLY, S>(acc, af, bfr, next, frags, dma, groups);
     } else {
       read_frags<S>(af[0], bfr[0], next, frags, 0);
@@ -610,6 +618,7 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
   wait_vmcnt<0>();
   __syncthreads();
 }
+
 
 // Row of the wave tile held by lane `lane` in element e of a 32 x 32 block.
 __device__ __forceinline__ int acc_row(int lane, int e) {
@@ -669,32 +678,63 @@ __device__ __forceinline__ void reduce_scatter32(float (&v)[32 * P], int lane, O
   rs_level<1, P>(v, (lane & 1) != 0, op);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  unsigned u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// ---------------------------------------------------------------------------
+// bf16 output tiles of the backward kernels are staged in LDS before 16-byte
+// coalesced stores.  Staging layout of a 256 x 256 tile: row r at byte 512 r, its
+// 16-byte chunk c (columns 8 c .. 8 c + 7) at chunk position c ^ out_swz(r).  The
+// swizzle sends the four rows one pair write touches (r0, r0 + 1, r0 + 4, r0 + 5,
+// r0 even within its group of 8) to four different 64-byte bank groups.
+__device__ __forceinline__ int out_swz(int r) { return ((r & 1) | ((r >> 1) & 2)) << 2; }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Stage two elements per lane as one packed bf16 pair.  In the MFMA layout, lanes 2i
+// and 2i + 1 hold adjacent columns (cl even, cl + 1) of the same rows; v0 is this
+// lane's element in row r0, v1 the one in row r0 + 1.  One DPP swap within each lane
+// pair lets the even lane write (r0, cl .. cl + 1) and the odd lane (r0 + 1, cl - 1 .. cl);
+// the conversion rounds to nearest even.
+__device__ __forceinline__ void stage_pair_bf16(char* tile, int lane, int r0, int cl, float v0,
+                                                float v1) {
+  const bool odd = (lane & 1) != 0;
+  const float recv = dpp_mov<0xB1>(odd ? v0 : v1);  // quad_perm [1, 0, 3, 2]
+  const f32x2 pr = {odd ? recv : v0, odd ? v1 : recv};
+  const int r = odd ? r0 + 1 : r0, c = cl & ~1;
+  *reinterpret_cast<uint32_t*>(tile + (r << 9) + ((((c >> 3) ^ out_swz(r))) << 4) + ((c & 7) << 1)) =
+      __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
 }
 
-// Copy a 256 x 256 bf16 tile staged row-major in LDS (512 bytes per row; rows
-// 0..127 in `lo`, 128..255 in `hi`) to rows [row0, row0 + nrows) and columns
-// [col0, col0 + ncols) of a row-major matrix with leading dimension ld; ncols is a
-// multiple of 8.  16-byte stores, 32 lanes per row.
-__device__ __forceinline__ void store_tile_bf16(const char* lo, const char* hi, uint16_t* dst,
-                                                long ld, int nrows, int ncols) {
+// Stage a wave's 128 x 128 block of values f(mb, nb, e) (the accumulator layout:
+// element e of block (mb, nb) is row wr0 + 32 mb + acc_row(lane, e), column
+// wc0 + 32 nb + lane % 32) into a staged tile.
+template <class F>
+__device__ __forceinline__ void stage_wave_bf16(char* tile, int wr0, int wc0, int lane, F f) {
+  const int lc = lane & 31;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const int r0 = wr0 + 32 * mb + ((e >> 2) << 3) + ((lane >> 5) << 2) + (e & 3);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        stage_pair_bf16(tile, lane, r0, wc0 + 32 * nb + lc, f(mb, nb, e), f(mb, nb, e + 1));
+    }
+}
+
+// Copy a staged 256 x 256 bf16 tile to rows [0, nrows) and columns [0, ncols) of a
+// row-major matrix at dst with leading dimension ld; ncols is a multiple of 8.
+// 16-byte stores, 32 lanes per row.
+__device__ __forceinline__ void store_tile_bf16(const char* tile, uint16_t* dst, long ld, int nrows,
+                                                int ncols) {
   const int t = threadIdx.x;
 #pragma unroll 4
   for (int it = 0; it < 32; ++it) {
     const int G = it * NTHREADS + t;
-    const int r = G >> 5, c = (G & 31) << 3;
-    const char* src = (r < 128 ? lo : hi) + ((r & 127) << 9) + (c << 1);
-    if (r < nrows && c < ncols)
-      *reinterpret_cast<u32x4*>(dst + (long)r * ld + c) = *reinterpret_cast<const u32x4*>(src);
+    const int r = G >> 5, c = G & 31;
+    const char* src = tile + (r << 9) + ((c ^ out_swz(r)) << 4);
+    if (r < nrows && 8 * c < ncols)
+      *reinterpret_cast<u32x4*>(dst + (long)r * ld + 8 * c) = *reinterpret_cast<const u32x4*>(src);
   }
-}
-
-// Staging slot of tile element (rl, cl) for store_tile_bf16.
-__device__ __forceinline__ uint16_t* out_slot(char* lo, char* hi, int rl, int cl) {
-  return reinterpret_cast<uint16_t*>((rl < 128 ? lo : hi) + ((rl & 127) << 9) + (cl << 1));
 }
 
 // ---------------------------------------------------------------------------
@@ -770,24 +810,43 @@ __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(Fwd
   constexpr int P = MB / 2;  // groups of 32 row slots per lane
   constexpr int NW = NTHREADS / 64;
   __shared__ __attribute__((aligned(1024))) char smem[S::PIPE_BYTES];
-  __shared__ __attribute__((aligned(16))) int t_col[TM];  // tile column of the row's target, or -1
-  __shared__ unsigned t_hits[NW];  // bit w: wave w's rectangle holds a target (per producer wave)
-  static_assert(6 * TM * 4 <= S::PIPE_BYTES, "epilogue buffers");
+  static_assert(7 * TM * 4 + 4 * NW <= S::PIPE_BYTES, "epilogue buffers");
   static_assert(NW == 4 && TM / WM * (TN / WN) == NW, "one bit per wave rectangle");
   int mt, vt;
   tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, FWD_GROUP_M, mt, vt);
   const int row0 = mt * TM, col0 = vt * TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  // tile column of the target of row tid, or -1 (kept in a register over the mainloop,
+  // which needs all of the LDS)
+  int tl = -1;
   {
-    int tl = -1;
     const int r = row0 + tid;
     if (tid < TM && r < p.M) {
       const int64_t t = p.targets[r];
       const int64_t hi = col0 + TN < p.V ? col0 + TN : p.V;
       if (t != p.ignore_index && t >= col0 && t < hi) tl = (int)(t - col0);
     }
-    if (tid < TM) t_col[tid] = tl;
+  }
+
+  f32x16 acc[MB][NB];
+  const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, (long)(p.M - row0) * p.H};
+  const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, (long)(p.V - col0) * p.H};
+  mainloop<S, true, true>(acc, smem, A, B, p.H);
+  // (the mainloop ends with a barrier: the LDS is free)
+
+  const int wr0 = (wave >> 1) * WM, wc0 = (wave & 1) * WN, wn = wave & 1;
+  const int lc = lane & 31;
+  const float c1 = p.scale * LOG2E;  // logits in log2 units: z2 = c1 acc
+
+  // epilogue LDS: half-row maxima [2][TM], sums [2][2][TM], target columns [TM] and
+  // per producer wave the rectangles (bit w: wave w's) that hold a target
+  float* red = reinterpret_cast<float*>(smem);
+  float* comb = red + 2 * TM;
+  int* t_col = reinterpret_cast<int*>(comb + 4 * TM);
+  unsigned* t_hits = reinterpret_cast<unsigned*>(t_col + TM);
+  if (tid < TM) t_col[tid] = tl;
+  {
     // the wave rectangle (rows of half tid / WM, columns of half tl / WN) holding it
     const int owner = tl >= 0 ? 2 * (tid / WM) + tl / WN : -1;
     unsigned bits = 0;
@@ -796,15 +855,29 @@ __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(Fwd
     if (lane == 0) t_hits[wave] = bits;
   }
 
-  f32x16 acc[MB][NB];
-  const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, (long)(p.M - row0) * p.H};
-  const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, (long)(p.V - col0) * p.H};
-  mainloop<S, true, true>(acc, smem, A, B, p.H);
-  // (the mainloop ends with a barrier: t_list is complete and the LDS stages are free)
+  const bool ragged = col0 + TN > p.V;
+  unsigned colmask = 0;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) colmask |= (col0 + wc0 + 32 * nb + lc < p.V ? 1u : 0u) << nb;
 
-  const int wr0 = (wave >> 1) * WM, wc0 = (wave & 1) * WN, wn = wave & 1;
-  const int lc = lane & 31;
-  const float c1 = p.scale * LOG2E;  // logits in log2 units: z2 = c1 acc
+  // row maxima of sgn(c1) acc: lane, half-wave, then both column halves via LDS
+  {
+    float mx[32 * P];
+    if (!ragged) {
+      if (c1 >= 0.f) lane_row_max<false, false, S>(acc, mx, colmask);
+      else lane_row_max<true, false, S>(acc, mx, colmask);
+    } else {
+      if (c1 >= 0.f) lane_row_max<false, true, S>(acc, mx, colmask);
+      else lane_row_max<true, true, S>(acc, mx, colmask);
+    }
+    reduce_scatter32<P>(mx, lane, [](float a, float b) { return fmaxf(a, b); });
+#pragma unroll
+    for (int pp = 0; pp < P; ++pp) {
+      const int mb = 2 * pp + (lc >> 4), e = lc & 15;
+      red[wn * TM + wr0 + 32 * mb + acc_row(lane, e)] = mx[32 * pp];
+    }
+  }
+  __syncthreads();
 
   // target logits: in a wave whose rectangle holds one, the lane holding (row,
   // target column) writes z = scale * acc
@@ -832,31 +905,6 @@ __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(Fwd
       }
   }
 
-  const bool ragged = col0 + TN > p.V;
-  unsigned colmask = 0;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) colmask |= (col0 + wc0 + 32 * nb + lc < p.V ? 1u : 0u) << nb;
-
-  // row maxima of sgn(c1) acc: lane, half-wave, then both column halves via LDS
-  float* red = reinterpret_cast<float*>(smem);  // [2 halves][TM]
-  {
-    float mx[32 * P];
-    if (!ragged) {
-      if (c1 >= 0.f) lane_row_max<false, false, S>(acc, mx, colmask);
-      else lane_row_max<true, false, S>(acc, mx, colmask);
-    } else {
-      if (c1 >= 0.f) lane_row_max<false, true, S>(acc, mx, colmask);
-      else lane_row_max<true, true, S>(acc, mx, colmask);
-    }
-    reduce_scatter32<P>(mx, lane, [](float a, float b) { return fmaxf(a, b); });
-#pragma unroll
-    for (int pp = 0; pp < P; ++pp) {
-      const int mb = 2 * pp + (lc >> 4), e = lc & 15;
-      red[wn * TM + wr0 + 32 * mb + acc_row(lane, e)] = mx[32 * pp];
-    }
-  }
-  __syncthreads();
-
   // shifted sums against the full-row maximum
   float sv[32 * P], uv[ENT ? 32 * P : 1];
   if (!ragged)
@@ -866,7 +914,6 @@ __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(Fwd
   reduce_scatter32<P>(sv, lane, [](float a, float b) { return a + b; });
   if constexpr (ENT) reduce_scatter32<P>(uv, lane, [](float a, float b) { return a + b; });
 
-  float* comb = red + 2 * TM;  // [2 halves][2 stats][TM]
 #pragma unroll
   for (int pp = 0; pp < P; ++pp) {
     const int mb = 2 * pp + (lc >> 4), e = lc & 15;
@@ -914,37 +961,99 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdMergeArgs p) {
 // Backward d-logits for one vocabulary chunk: dzs = scale * dz in bf16, written to
 // a [Mpad, ldz] buffer (chunk column j = vocabulary column vbase + j).  Columns past
 // V and rows past M are written as zero.
+// Stage a wave's d-logits, d = 2^(c1 acc - lse2) (c0 + cb acc) + [column = target] sa
+// (per-row parameters in LDS, see bwd_dlogits_kernel).  TGT: the wave's rectangle holds
+// a target column; RAGGED: columns past V (colmask bit nb clear) become 0.
+template <bool ENTGRAD, bool RAGGED, bool TGT>
+__device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4][4],
+                                              const float* r_lse2, const float* r_c0,
+                                              const float* r_cb, const float* r_sa,
+                                              const int* t_local, int wr0, int wc0, int lane,
+                                              float c1, unsigned colmask) {
+  const int lc = lane & 31;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // rows rb .. rb + 3 are the lane's slots e = 4 q .. 4 q + 3 of block mb
+      const int rb = wr0 + 32 * mb + 8 * q + 4 * (lane >> 5);
+      const float4 L4 = *reinterpret_cast<const float4*>(r_lse2 + rb);
+      const float4 C4 = *reinterpret_cast<const float4*>(r_c0 + rb);
+      const float L[4] = {L4.x, L4.y, L4.z, L4.w}, C0[4] = {C4.x, C4.y, C4.z, C4.w};
+      float CB[4] = {0.f, 0.f, 0.f, 0.f}, SA[4] = {0.f, 0.f, 0.f, 0.f};
+      int DD[4] = {-1, -1, -1, -1};  // target column - first column of the lane
+      if constexpr (ENTGRAD) {
+        const float4 B4 = *reinterpret_cast<const float4*>(r_cb + rb);
+        CB[0] = B4.x; CB[1] = B4.y; CB[2] = B4.z; CB[3] = B4.w;
+      }
+      if constexpr (TGT) {
+        const float4 S4 = *reinterpret_cast<const float4*>(r_sa + rb);
+        const int4 T4 = *reinterpret_cast<const int4*>(t_local + rb);
+        SA[0] = S4.x; SA[1] = S4.y; SA[2] = S4.z; SA[3] = S4.w;
+        DD[0] = T4.x - wc0 - lc; DD[1] = T4.y - wc0 - lc; DD[2] = T4.z - wc0 - lc; DD[3] = T4.w - wc0 - lc;
+      }
+#pragma unroll
+      for (int jp = 0; jp < 4; jp += 2)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          float v[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int j = jp + h;
+            const float av = acc[mb][nb][4 * q + j];
+            const float pr = __builtin_amdgcn_exp2f(fmaf(av, c1, -L[j]));
+            float d = pr * (ENTGRAD ? fmaf(CB[j], av, C0[j]) : C0[j]);
+            if constexpr (TGT) d += DD[j] == 32 * nb ? SA[j] : 0.f;
+            if constexpr (RAGGED) d = ((colmask >> nb) & 1u) ? d : 0.f;
+            v[h] = d;
+          }
+          stage_pair_bf16(tile, lane, rb + jp, wc0 + 32 * nb + lc, v[0], v[1]);
+        }
+    }
+}
+
+// Backward d-logits for one vocabulary chunk: dzs = scale * dz in bf16, written to
+// a [Mpad, ldz] buffer (chunk column j = vocabulary column vbase + j).  Columns past
+// V and rows past M are written as zero.  With p = 2^(c1 acc - lse2) (c1 = scale log2 e)
+// and per-row a = grad_logprob, b = grad_entropy, E = lse - entropy (all 0 on ignored
+// rows):  scale dz = scale (a ([v = t] - p) + b p (E - scale acc))
+//                  = p (c0 + cb acc) + [v = t] sa,
+// c0 = scale (b E - a), cb = -scale^2 b, sa = scale a.
 template <bool ENTGRAD>
 __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
-  __shared__ float r_lse2[TILE], r_a[TILE], r_b[TILE], r_E[TILE];
-  __shared__ int t_local[TILE];
+  // the pipeline, then the bf16 output tile and the per-row arrays
+  constexpr int ROW_BYTES = 5 * TILE * 4 + 16;
+  constexpr int LDS_DLOGITS =
+      BigShape::PIPE_BYTES > LDS_OUT + ROW_BYTES ? BigShape::PIPE_BYTES : LDS_OUT + ROW_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_DLOGITS];
   int mt, vt;
   tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, 8, mt, vt);
   const int row0 = mt * TILE, ccol0 = vt * TILE, col0 = p.vbase + ccol0;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  // row tid's parameters, kept in registers over the mainloop (which may need all of
+  // the LDS) and published through LDS after it
+  float lse2 = 0.f, c0 = 0.f, cb = 0.f, sa = 0.f;
+  int tl = -1;
   {
     const int r = row0 + tid;
-    float lse = 0.f, a = 0.f, b = 0.f, E = 0.f;
-    int tl = -1;
     if (r < p.M) {
       const int64_t t = p.targets[r];
       const bool valid = t != p.ignore_index && t >= 0 && t < p.V;
-      lse = p.lse[r];
+      const float lse = p.lse[r];
+      lse2 = lse * LOG2E;
       if (valid) {
-        a = p.grad_logprob ? p.grad_logprob[r] : 0.f;
+        const float a = p.grad_logprob ? p.grad_logprob[r] : 0.f;
+        sa = p.scale * a;
+        c0 = -sa;
         if constexpr (ENTGRAD) {
-          b = p.grad_entropy[r];
-          E = lse - p.entropy[r];
+          const float b = p.grad_entropy[r];
+          c0 = p.scale * (b * (lse - p.entropy[r]) - a);
+          cb = -p.scale * p.scale * b;
         }
         if (t >= col0 && t < col0 + TILE) tl = (int)(t - col0);
       }
     }
-    r_lse2[tid] = lse * LOG2E;
-    r_a[tid] = a;
-    r_b[tid] = b;
-    r_E[tid] = E;
-    t_local[tid] = tl;
   }
 
   f32x16 acc[4][4];
@@ -952,31 +1061,43 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
   const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, (long)(p.V - col0) * p.H};
   mainloop<BigShape, true, true>(acc, smem, A, B, p.H);
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
-  const int lc = lane & 31;
-  const float c1 = p.scale * LOG2E;
+  float* r_lse2 = reinterpret_cast<float*>(smem + LDS_OUT);
+  float* r_c0 = r_lse2 + TILE;
+  float* r_cb = r_c0 + TILE;
+  float* r_sa = r_cb + TILE;
+  int* t_local = reinterpret_cast<int*>(r_sa + TILE);
+  unsigned* t_hits = reinterpret_cast<unsigned*>(t_local + TILE);
+  r_lse2[tid] = lse2;
+  r_c0[tid] = c0;
+  if constexpr (ENTGRAD) r_cb[tid] = cb;
+  r_sa[tid] = sa;
+  t_local[tid] = tl;
+  {
+    // bit w: wave w's 128 x 128 rectangle holds a target column
+    const int owner = tl >= 0 ? 2 * (tid >> 7) + (tl >> 7) : -1;
+    unsigned bits = 0;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rl = wr0 + 32 * mb + acc_row(lane, e);
-      const float lse2 = r_lse2[rl], a = r_a[rl], b = r_b[rl], E = r_E[rl];
-      const int tl = t_local[rl];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int cl = wc0 + 32 * nb + lc;
-        const float av = acc[mb][nb][e];
-        const float pr = __builtin_amdgcn_exp2f(av * c1 - lse2);
-        float d = (cl == tl ? a : 0.f) - a * pr;
-        if constexpr (ENTGRAD) d += b * pr * (E - av * p.scale);
-        d *= p.scale;
-        if (col0 + cl >= p.V) d = 0.f;
-        *out_slot(smem, smem + 128 * 512, rl, cl) = f32_to_bf16_rne(d);
-      }
-    }
+    for (int w = 0; w < 4; ++w) bits |= (__ballot(owner == w) != 0ull ? 1u : 0u) << w;
+    if (lane == 0) t_hits[wave] = bits;
+  }
   __syncthreads();
-  store_tile_bf16(smem, smem + 128 * 512, p.dz + (long)row0 * p.ldz + ccol0, p.ldz, TILE, TILE);
+
+  const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
+  const float c1 = p.scale * LOG2E;
+  const bool ragged = col0 + TILE > p.V;
+  const bool tgt = (__builtin_amdgcn_readfirstlane(t_hits[0] | t_hits[1] | t_hits[2] | t_hits[3]) >> wave) & 1u;
+  unsigned colmask = 0;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) colmask |= (col0 + wc0 + 32 * nb + (lane & 31) < p.V ? 1u : 0u) << nb;
+  if (!ragged) {
+    if (!tgt) stage_dlogits<ENTGRAD, false, false>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
+    else stage_dlogits<ENTGRAD, false, true>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
+  } else {
+    if (!tgt) stage_dlogits<ENTGRAD, true, false>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
+    else stage_dlogits<ENTGRAD, true, true>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
+  }
+  __syncthreads();
+  store_tile_bf16(smem, p.dz + (long)row0 * p.ldz + ccol0, p.ldz, TILE, TILE);
 }
 
 // ---------------------------------------------------------------------------
@@ -994,19 +1115,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
-  const int lc = lane & 31;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rl = wr0 + 32 * mb + acc_row(lane, e);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        *out_slot(smem, smem + 128 * 512, rl, wc0 + 32 * nb + lc) = f32_to_bf16_rne(acc[mb][nb][e]);
-    }
+  stage_wave_bf16(smem, wr0, wc0, lane, [&](int mb, int nb, int e) { return acc[mb][nb][e]; });
   __syncthreads();
   const int rows = min(min(TILE, p.chunk_cols - i0), p.V - (p.vbase + i0));
-  store_tile_bf16(smem, smem + 128 * 512, p.dW + (long)(p.vbase + i0) * p.H + h0, p.H, rows, p.H - h0);
+  store_tile_bf16(smem, p.dW + (long)(p.vbase + i0) * p.H + h0, p.H, rows, p.H - h0);
 }
 
 // dX[m, h] (+)= sum_i dzs[m, i] W[vbase + i, h]: A = dzs (KC), B = W^T (MN), K = kcols.
@@ -1027,23 +1139,17 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
   const int lc = lane & 31;
-  if (p.mode == 0 || p.mode == 3) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rl = wr0 + 32 * mb + acc_row(lane, e);
-        const int m = m0 + rl;
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int cl = wc0 + 32 * nb + lc;
-          float v = acc[mb][nb][e];
-          if (p.mode == 3 && m < p.M && h0 + cl < p.H) v += p.acc[(long)m * p.H + h0 + cl];
-          *out_slot(smem, smem + 128 * 512, rl, cl) = f32_to_bf16_rne(v);
-        }
-      }
+  if (p.mode == 0) {
+    stage_wave_bf16(smem, wr0, wc0, lane, [&](int mb, int nb, int e) { return acc[mb][nb][e]; });
     __syncthreads();
-    store_tile_bf16(smem, smem + 128 * 512, p.dX + (long)m0 * p.H + h0, p.H, p.M - m0, p.H - h0);
+    store_tile_bf16(smem, p.dX + (long)m0 * p.H + h0, p.H, p.M - m0, p.H - h0);
+  } else if (p.mode == 3) {
+    stage_wave_bf16(smem, wr0, wc0, lane, [&](int mb, int nb, int e) {
+      const int m = m0 + wr0 + 32 * mb + acc_row(lane, e), h = h0 + wc0 + 32 * nb + lc;
+      return acc[mb][nb][e] + (m < p.M && h < p.H ? p.acc[(long)m * p.H + h] : 0.f);
+    });
+    __syncthreads();
+    store_tile_bf16(smem, p.dX + (long)m0 * p.H + h0, p.H, p.M - m0, p.H - h0);
   } else {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
