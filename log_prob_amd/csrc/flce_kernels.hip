@@ -933,27 +933,50 @@ __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(Fwd
 
 // Merge of the per-tile partials of each row: m* = max m_j, S = sum s_j e^(m_j - m*),
 // U = sum e^(m_j - m*) (u_j + (m_j - m*) s_j); lse = m* + log S, entropy = log S - U / S.
+// A workgroup takes MERGE_ROWS rows; its MERGE_SLICES waves split each row's tiles
+// (lanes read consecutive rows of one tile, so every load is a coalesced 256 bytes)
+// and combine their maxima, then their sums, through LDS.
+constexpr int MERGE_ROWS = 64, MERGE_SLICES = 8;
 template <bool ENT>
-__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdMergeArgs p) {
-  const int row = blockIdx.x * 256 + threadIdx.x;
-  if (row >= p.M) return;
+__global__ __launch_bounds__(MERGE_ROWS * MERGE_SLICES) void fwd_merge_kernel(FwdMergeArgs p) {
+  __shared__ float sm[3][MERGE_SLICES][MERGE_ROWS];
+  const int lr = threadIdx.x % MERGE_ROWS, sl = threadIdx.x / MERGE_ROWS;
+  const int row = blockIdx.x * MERGE_ROWS + lr;
+  const bool live = row < p.M;
   float m = -INFINITY;
-  for (int j = 0; j < p.n_vt; ++j) m = fmaxf(m, p.part_m[(long)j * p.Mpad + row]);
+  if (live)
+    for (int j = sl; j < p.n_vt; j += MERGE_SLICES) m = fmaxf(m, p.part_m[(long)j * p.Mpad + row]);
+  sm[0][sl][lr] = m;
+  __syncthreads();
+  float ms = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < MERGE_SLICES; ++k) ms = fmaxf(ms, sm[0][k][lr]);
   float S = 0.f, U = 0.f;
-  for (int j = 0; j < p.n_vt; ++j) {
-    const long off = (long)j * p.Mpad + row;
-    const float dm = p.part_m[off] - m;
-    const float a = __expf(dm);
-    const float s = p.part_s[off];
-    S += s * a;
-    if constexpr (ENT) U += a * (p.part_u[off] + dm * s);
+  if (live)
+    for (int j = sl; j < p.n_vt; j += MERGE_SLICES) {
+      const long off = (long)j * p.Mpad + row;
+      const float dm = p.part_m[off] - ms;
+      const float a = __expf(dm);
+      const float s = p.part_s[off];
+      S += s * a;
+      if constexpr (ENT) U += a * (p.part_u[off] + dm * s);
+    }
+  sm[1][sl][lr] = S;
+  sm[2][sl][lr] = U;
+  __syncthreads();
+  if (sl != 0 || !live) return;
+  S = 0.f;
+  U = 0.f;
+#pragma unroll
+  for (int k = 0; k < MERGE_SLICES; ++k) {
+    S += sm[1][k][lr];
+    if constexpr (ENT) U += sm[2][k][lr];
   }
   const float logS = logf(S);
-  const float lse = m + logS;
   const int64_t t = p.targets[row];
   const bool valid = t != p.ignore_index && t >= 0 && t < p.V;
-  p.lse[row] = lse;
-  p.logprob[row] = valid ? p.zt[row] - lse : 0.f;
+  p.lse[row] = ms + logS;
+  p.logprob[row] = valid ? p.zt[row] - (ms + logS) : 0.f;
   if constexpr (ENT) p.entropy[row] = valid ? logS - U / S : 0.f;
 }
 
@@ -1186,11 +1209,11 @@ hipError_t launch_fwd_tile(const FwdTileArgs& a, bool ent, hipStream_t s) {
 }
 
 hipError_t launch_fwd_merge(const FwdMergeArgs& a, bool ent, hipStream_t s) {
-  const unsigned g = (unsigned)((a.M + 255) / 256);
+  const unsigned g = (unsigned)((a.M + MERGE_ROWS - 1) / MERGE_ROWS);
   if (ent)
-    fwd_merge_kernel<true><<<g, 256, 0, s>>>(a);
+    fwd_merge_kernel<true><<<g, MERGE_ROWS * MERGE_SLICES, 0, s>>>(a);
   else
-    fwd_merge_kernel<false><<<g, 256, 0, s>>>(a);
+    fwd_merge_kernel<false><<<g, MERGE_ROWS * MERGE_SLICES, 0, s>>>(a);
   return hipGetLastError();
 }
 
