@@ -808,10 +808,8 @@ template <class S, bool ENT>
 __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(FwdTileArgs p) {
   constexpr int TM = S::TM, TN = S::TN, MB = S::MB, NB = S::NB, WM = S::WM, WN = S::WN;
   constexpr int P = MB / 2;  // groups of 32 row slots per lane
-  constexpr int NW = NTHREADS / 64;
   __shared__ __attribute__((aligned(1024))) char smem[S::PIPE_BYTES];
-  static_assert(7 * TM * 4 + 4 * NW <= S::PIPE_BYTES, "epilogue buffers");
-  static_assert(NW == 4 && TM / WM * (TN / WN) == NW, "one bit per wave rectangle");
+  static_assert(7 * TM * 4 <= S::PIPE_BYTES, "epilogue buffers");
   int mt, vt;
   tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, FWD_GROUP_M, mt, vt);
   const int row0 = mt * TM, col0 = vt * TN;
@@ -839,21 +837,11 @@ __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(Fwd
   const int lc = lane & 31;
   const float c1 = p.scale * LOG2E;  // logits in log2 units: z2 = c1 acc
 
-  // epilogue LDS: half-row maxima [2][TM], sums [2][2][TM], target columns [TM] and
-  // per producer wave the rectangles (bit w: wave w's) that hold a target
+  // epilogue LDS: half-row maxima [2][TM], sums [2][2][TM], target columns [TM]
   float* red = reinterpret_cast<float*>(smem);
   float* comb = red + 2 * TM;
   int* t_col = reinterpret_cast<int*>(comb + 4 * TM);
-  unsigned* t_hits = reinterpret_cast<unsigned*>(t_col + TM);
   if (tid < TM) t_col[tid] = tl;
-  {
-    // the wave rectangle (rows of half tid / WM, columns of half tl / WN) holding it
-    const int owner = tl >= 0 ? 2 * (tid / WM) + tl / WN : -1;
-    unsigned bits = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) bits |= (__ballot(owner == w) != 0ull ? 1u : 0u) << w;
-    if (lane == 0) t_hits[wave] = bits;
-  }
 
   const bool ragged = col0 + TN > p.V;
   unsigned colmask = 0;
@@ -879,31 +867,28 @@ __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(Fwd
   }
   __syncthreads();
 
-  // target logits: in a wave whose rectangle holds one, the lane holding (row,
-  // target column) writes z = scale * acc
-  unsigned hits = 0;
+  // target logits: the lane holding (row, target column) writes z = scale * acc.
+  // Every wave scans its row slots, so that all tiles cost the same: the workgroups
+  // of an XCD then stay in step over K and share their operand tiles in L2 (a scan
+  // only where a target lies lets them drift apart and raises the L2 misses by half).
 #pragma unroll
-  for (int w = 0; w < NW; ++w) hits |= t_hits[w];
-  if ((__builtin_amdgcn_readfirstlane(hits) >> wave) & 1u) {
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int q = 0; q < 4; ++q) {
+      const int rb = wr0 + 32 * mb + 8 * q + 4 * (lane >> 5);
+      const int4 tc = *reinterpret_cast<const int4*>(t_col + rb);
+      const int tcs[4] = {tc.x, tc.y, tc.z, tc.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rb = wr0 + 32 * mb + 8 * q + 4 * (lane >> 5);
-        const int4 tc = *reinterpret_cast<const int4*>(t_col + rb);
-        const int tcs[4] = {tc.x, tc.y, tc.z, tc.w};
+      for (int j = 0; j < 4; ++j) {
+        const int dd = tcs[j] - wc0 - lc;  // 32 nb if this lane holds the target column
+        if ((unsigned)dd < (unsigned)WN && (dd & 31) == 0) {
+          float z = acc[mb][0][4 * q + j];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int dd = tcs[j] - wc0 - lc;  // 32 nb if this lane holds the target column
-          if ((unsigned)dd < (unsigned)WN && (dd & 31) == 0) {
-            float z = acc[mb][0][4 * q + j];
-#pragma unroll
-            for (int nb = 1; nb < NB; ++nb) z = (dd >> 5) == nb ? acc[mb][nb][4 * q + j] : z;
-            p.zt[row0 + rb + j] = z * p.scale;
-          }
+          for (int nb = 1; nb < NB; ++nb) z = (dd >> 5) == nb ? acc[mb][nb][4 * q + j] : z;
+          p.zt[row0 + rb + j] = z * p.scale;
         }
       }
-  }
+    }
 
   // shifted sums against the full-row maximum
   float sv[32 * P], uv[ENT ? 32 * P : 1];
@@ -985,6 +970,66 @@ __global__ __launch_bounds__(MERGE_ROWS * MERGE_SLICES) void fwd_merge_kernel(Fw
 // a [Mpad, ldz] buffer (chunk column j = vocabulary column vbase + j).  Columns past
 // V and rows past M are written as zero.
 // Stage a wave's d-logits, d = 2^(c1 acc - lse2) (c0 + cb acc) + [column = target] sa
+// (per-row parameters in LDS, see bwd_dlogits_kernel).  RAGGED: columns past V
+// (colmask bit nb clear) become 0.  Every wave runs the same instruction stream
+// whether or not it holds a target (the correction is a per-row-slot branch that
+// almost never has active lanes), which keeps the tiles of an XCD in step.
+template <bool ENTGRAD, bool RAGGED>
+__device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4][4],
+                                              const float* r_lse2, const float* r_c0,
+                                              const float* r_cb, const float* r_sa,
+                                              const int* t_local, int wr0, int wc0, int lane,
+                                              float c1, unsigned colmask) {
+  const int lc = lane & 31;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // rows rb .. rb + 3 are the lane's slots e = 4 q .. 4 q + 3 of block mb
+      const int rb = wr0 + 32 * mb + 8 * q + 4 * (lane >> 5);
+      const float4 L4 = *reinterpret_cast<const float4*>(r_lse2 + rb);
+      const float4 C4 = *reinterpret_cast<const float4*>(r_c0 + rb);
+      const float4 S4 = *reinterpret_cast<const float4*>(r_sa + rb);
+      const int4 T4 = *reinterpret_cast<const int4*>(t_local + rb);
+      const float L[4] = {L4.x, L4.y, L4.z, L4.w}, C0[4] = {C4.x, C4.y, C4.z, C4.w};
+      const float SA[4] = {S4.x, S4.y, S4.z, S4.w};
+      const int DD[4] = {T4.x - wc0 - lc, T4.y - wc0 - lc, T4.z - wc0 - lc, T4.w - wc0 - lc};
+      float CB[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (ENTGRAD) {
+        const float4 B4 = *reinterpret_cast<const float4*>(r_cb + rb);
+        CB[0] = B4.x; CB[1] = B4.y; CB[2] = B4.z; CB[3] = B4.w;
+      }
+#pragma unroll
+      for (int jp = 0; jp < 4; jp += 2) {
+        float v[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int j = jp + h;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const float av = acc[mb][nb][4 * q + j];
+            const float pr = __builtin_amdgcn_exp2f(fmaf(av, c1, -L[j]));
+            float d = pr * (ENTGRAD ? fmaf(CB[j], av, C0[j]) : C0[j]);
+            if constexpr (RAGGED) d = ((colmask >> nb) & 1u) ? d : 0.f;
+            v[h][nb] = d;
+          }
+          // DD = 32 nb: this lane holds the target column of the row (in block nb)
+          if ((unsigned)DD[j] < 128u && (DD[j] & 31) == 0) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) v[h][nb] += (DD[j] >> 5) == nb ? SA[j] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          stage_pair_bf16(tile, lane, rb + jp, wc0 + 32 * nb + lc, v[0][nb], v[1][nb]);
+      }
+    }
+}
+
+// Backward d-logits for one vocabulary chunk: dzs = scale * dz in bf16, written to
+// a [Mpad, ldz] buffer (chunk column j = vocabulary column vbase + j).  Columns past
+// V and rows past M are written as zero.
+// Stage a wave's d-logits, d = 2^(c1 acc - lse2) (c0 + cb acc) + [column = target] sa
 // (per-row parameters in LDS, see bwd_dlogits_kernel).  TGT: the wave's rectangle holds
 // a target column; RAGGED: columns past V (colmask bit nb clear) become 0.
 template <bool ENTGRAD, bool RAGGED, bool TGT>
@@ -1045,7 +1090,7 @@ __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4]
 template <bool ENTGRAD>
 __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
   // the pipeline, then the bf16 output tile and the per-row arrays
-  constexpr int ROW_BYTES = 5 * TILE * 4 + 16;
+  constexpr int ROW_BYTES = 5 * TILE * 4;
   constexpr int LDS_DLOGITS =
       BigShape::PIPE_BYTES > LDS_OUT + ROW_BYTES ? BigShape::PIPE_BYTES : LDS_OUT + ROW_BYTES;
   __shared__ __attribute__((aligned(1024))) char smem[LDS_DLOGITS];
@@ -1089,36 +1134,23 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
   float* r_cb = r_c0 + TILE;
   float* r_sa = r_cb + TILE;
   int* t_local = reinterpret_cast<int*>(r_sa + TILE);
-  unsigned* t_hits = reinterpret_cast<unsigned*>(t_local + TILE);
   r_lse2[tid] = lse2;
   r_c0[tid] = c0;
   if constexpr (ENTGRAD) r_cb[tid] = cb;
   r_sa[tid] = sa;
   t_local[tid] = tl;
-  {
-    // bit w: wave w's 128 x 128 rectangle holds a target column
-    const int owner = tl >= 0 ? 2 * (tid >> 7) + (tl >> 7) : -1;
-    unsigned bits = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) bits |= (__ballot(owner == w) != 0ull ? 1u : 0u) << w;
-    if (lane == 0) t_hits[wave] = bits;
-  }
   __syncthreads();
 
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
   const float c1 = p.scale * LOG2E;
   const bool ragged = col0 + TILE > p.V;
-  const bool tgt = (__builtin_amdgcn_readfirstlane(t_hits[0] | t_hits[1] | t_hits[2] | t_hits[3]) >> wave) & 1u;
   unsigned colmask = 0;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) colmask |= (col0 + wc0 + 32 * nb + (lane & 31) < p.V ? 1u : 0u) << nb;
-  if (!ragged) {
-    if (!tgt) stage_dlogits<ENTGRAD, false, false>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
-    else stage_dlogits<ENTGRAD, false, true>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
-  } else {
-    if (!tgt) stage_dlogits<ENTGRAD, true, false>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
-    else stage_dlogits<ENTGRAD, true, true>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
-  }
+  if (!ragged)
+    stage_dlogits<ENTGRAD, false>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
+  else
+    stage_dlogits<ENTGRAD, true>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
   __syncthreads();
   store_tile_bf16(smem, p.dz + (long)row0 * p.ldz + ccol0, p.ldz, TILE, TILE);
 }
