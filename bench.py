@@ -235,6 +235,15 @@ def main():
     for _ in range(2):
         fwd()
     fwd_ms = float(np.median(timed(fwd, max(args.steps, 5))))
+    # token waves: the same forward with a workspace that holds 4096-row waves of partials
+    wave_rows = min(4096, -(-M // 256) * 256)
+    ws_wave = torch.empty(flce.forward_workspace_min(M, H, V, ent) * (wave_rows // 256),
+                          dtype=torch.uint8, device=dev)
+    assert flce.forward_wave_rows(M, H, V, ws_wave.numel(), ent) == wave_rows
+    fwd_wave = lambda: flce.forward(X, W, t, case.ignore_index, case.scale, ent,
+                                    workspace=ws_wave, out=(logprob, lse, entropy))
+    fwd_wave()
+    fwd_wave_ms = float(np.median(timed(fwd_wave, max(args.steps, 5))))
     part = lambda: flce.forward_partials(X, W, t, case.ignore_index, case.scale, ent, workspace=ws)
     part()
     k_ms = timed(part, max(args.steps, 5))
@@ -268,6 +277,9 @@ def main():
         "fwd_tflops": round(tf_f, 2),
         "fwd_pct_peak": round(100.0 * tf_f / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed": round(wall, 3),
+        "fwd_token_waves": {"wave_rows": wave_rows, "ms": round(fwd_wave_ms, 4),
+                            "tflops": round(flop_f / (fwd_wave_ms * 1e-3) / 1e12, 2),
+                            "workspace_bytes": int(ws_wave.numel()), "full_workspace_bytes": fwd_b},
         "roofline": {"bound": "mfma", "kernel": "fwd_tile_kernel (fused GEMM + online softmax)",
                      "achieved": round(k_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(k_tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),

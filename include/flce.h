@@ -89,11 +89,30 @@ flce_status_t flce_backward_chunk_cols(int64_t M, int64_t H, int64_t V, size_t w
                                        int64_t* chunk_cols);
 
 /*
+ * Smallest workspace flce_forward accepts, and the wave height it uses with a given
+ * workspace.  The forward walks the tokens in waves (the token-wave scheduling of
+ * the Liger-Kernel commit "native Blackwell tensor-parallel fused scaled linear
+ * cross-entropy", sections "Summary" and "Correctness": 4K waves, two-wave tails):
+ * a wave is a multiple of 256 rows whose per-tile partials (12 bytes per row per
+ * 256 vocabulary columns with entropy, 8 without) fit in the workspace.  The size
+ * from flce_workspace_query takes all rows in one wave; the minimum takes 256.
+ * Results are bitwise identical for every wave height: a row's tiles and merge do
+ * not depend on the wave it falls in.
+ */
+flce_status_t flce_forward_workspace_min(int64_t M, int64_t H, int64_t V, int compute_entropy,
+                                         size_t* bytes);
+
+/* Rows per token wave flce_forward would use with this workspace (a multiple of 256,
+ * at most M rounded up to 256); FLCE_ERR_WORKSPACE_TOO_SMALL below the minimum. */
+flce_status_t flce_forward_wave_rows(int64_t M, int64_t H, int64_t V, int compute_entropy,
+                                     size_t workspace_bytes, int64_t* rows);
+
+/*
  * Forward.  Writes logprob[M], lse[M] and, if compute_entropy == 1, entropy[M]
  * (all fp32).  entropy may be NULL only when compute_entropy == 0.
  * scale is the temperature factor applied to the fp32 accumulator (1/T).
- * workspace: device memory of at least *fwd_bytes from flce_workspace_query,
- * 256-byte aligned.
+ * workspace: device memory of at least flce_forward_workspace_min bytes (the
+ * *fwd_bytes of flce_workspace_query runs every row in one wave), 256-byte aligned.
  */
 flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets,
                            int64_t M, int64_t H, int64_t V, int64_t ignore_index, float scale,
@@ -104,8 +123,10 @@ flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets,
  * The two halves of flce_forward, for callers that exchange or inspect the
  * per-tile statistics (a vocabulary-sharded caller gathers them across shards
  * before merging).  flce_forward_partials runs the fused GEMM + online-softmax
- * kernel and leaves in the workspace, for every row m and 256-column vocabulary
- * tile j (j < ceil(V / 256), Mpad = 256 * ceil(M / 256)), at float offsets
+ * kernel over all rows in one wave (the workspace must hold *fwd_bytes of
+ * flce_workspace_query) and leaves in the workspace, for every row m and
+ * 256-column vocabulary tile j (j < ceil(V / 256), Mpad = 256 * ceil(M / 256)),
+ * at float offsets
  *   j * Mpad + m                       max_v z[m, v] over the tile
  *   (n_vt + j) * Mpad + m              sum_v exp(z[m, v] - max)
  *   (2 n_vt + j) * Mpad + m            sum_v exp(z[m, v] - max) (z[m, v] - max)  (entropy only)

@@ -65,11 +65,12 @@ struct FwdLayout {
   size_t off_m, off_s, off_u, off_zt, total;
 };
 
-FwdLayout fwd_layout(int64_t M, int64_t V, bool ent) {
+// Forward workspace for a wave of `rows` token rows (rows <= Mpad of the call).
+FwdLayout fwd_layout(int64_t rows, int64_t V, bool ent) {
   FwdLayout L;
-  L.n_mt = cdiv(M, flce::kFwdTileM);
+  L.n_mt = cdiv(rows, flce::kFwdTileM);
   L.n_vt = cdiv(V, flce::kFwdTileN);
-  L.Mpad = cdiv(M, kTile) * kTile;
+  L.Mpad = cdiv(rows, kTile) * kTile;
   const size_t part = align_up(size_t(L.n_vt) * size_t(L.Mpad) * sizeof(float));
   L.off_m = 0;
   L.off_s = part;
@@ -77,6 +78,19 @@ FwdLayout fwd_layout(int64_t M, int64_t V, bool ent) {
   L.off_zt = (ent ? 3 : 2) * part;
   L.total = L.off_zt + align_up(size_t(L.Mpad) * sizeof(float));
   return L;
+}
+
+// Tallest wave (a multiple of 256 rows, at most Mpad) whose forward partials fit in
+// `bytes`; 0 if not even one 256-row wave fits.
+int64_t wave_rows_for_workspace(int64_t M, int64_t V, bool ent, size_t bytes) {
+  const int64_t Mpad = cdiv(M, kTile) * kTile;
+  if (fwd_layout(Mpad, V, ent).total <= bytes) return Mpad;
+  int64_t lo = 0, hi = Mpad / kTile;  // in tiles: lo fits (or 0), hi does not
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) / 2;
+    if (fwd_layout(mid * kTile, V, ent).total <= bytes) lo = mid; else hi = mid;
+  }
+  return lo * kTile;
 }
 
 size_t bwd_bytes_for_chunk(int64_t M, int64_t H, int64_t V, int64_t chunk) {
@@ -141,6 +155,32 @@ flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_
   if (st != FLCE_OK) return st;
   if (fwd_bytes) *fwd_bytes = fwd_layout(M, V, compute_entropy == 1).total;
   if (bwd_bytes) *bwd_bytes = bwd_bytes_for_chunk(M, H, V, preferred_chunk(M, V));
+  return ok();
+}
+
+flce_status_t flce_forward_workspace_min(int64_t M, int64_t H, int64_t V, int compute_entropy,
+                                         size_t* bytes) {
+  if (compute_entropy != 0 && compute_entropy != 1)
+    return fail(FLCE_ERR_INVALID_VALUE, "compute_entropy must be 0 or 1");
+  flce_status_t st = check_shape(M, H, V);
+  if (st != FLCE_OK) return st;
+  if (!bytes) return fail(FLCE_ERR_INVALID_VALUE, "bytes is NULL");
+  *bytes = fwd_layout(kTile, V, compute_entropy == 1).total;
+  return ok();
+}
+
+flce_status_t flce_forward_wave_rows(int64_t M, int64_t H, int64_t V, int compute_entropy,
+                                     size_t workspace_bytes, int64_t* rows) {
+  if (compute_entropy != 0 && compute_entropy != 1)
+    return fail(FLCE_ERR_INVALID_VALUE, "compute_entropy must be 0 or 1");
+  flce_status_t st = check_shape(M, H, V);
+  if (st != FLCE_OK) return st;
+  if (!rows) return fail(FLCE_ERR_INVALID_VALUE, "rows is NULL");
+  const int64_t r = wave_rows_for_workspace(M, V, compute_entropy == 1, workspace_bytes);
+  if (r == 0)
+    return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the minimum %zu",
+                workspace_bytes, fwd_layout(kTile, V, compute_entropy == 1).total);
+  *rows = r;
   return ok();
 }
 
@@ -291,23 +331,37 @@ flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets,
   if (!X || !W || !targets || !logprob || !lse || !workspace)
     return fail(FLCE_ERR_INVALID_VALUE,
                 "NULL pointer among X, W, targets, logprob, lse, workspace");
-  FwdLayout L;
-  flce_status_t st =
-      check_forward_common(targets, M, H, V, compute_entropy, workspace, workspace_bytes, &L);
+  flce_status_t st = check_shape(M, H, V);
   if (st != FLCE_OK) return st;
+  if (compute_entropy != 0 && compute_entropy != 1)
+    return fail(FLCE_ERR_INVALID_VALUE, "compute_entropy must be 0 or 1");
+  if (!aligned(targets, 8)) return fail(FLCE_ERR_UNSUPPORTED, "targets must be 8-byte aligned");
+  if (!aligned(workspace, kAlign))
+    return fail(FLCE_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   st = check_forward_inputs(X, W, scale);
   if (st != FLCE_OK) return st;
   st = check_forward_outputs(compute_entropy, logprob, lse, entropy);
   if (st != FLCE_OK) return st;
   const bool ent = compute_entropy == 1;
+  // token waves: as many 256-row tiles per wave as the workspace holds partials for
+  const int64_t rows = wave_rows_for_workspace(M, V, ent, workspace_bytes);
+  if (rows == 0)
+    return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "forward needs at least %zu workspace bytes, got %zu",
+                fwd_layout(kTile, V, ent).total, workspace_bytes);
   char* ws = static_cast<char*>(workspace);
-  const flce::FwdTileArgs a = tile_args(X, W, targets, M, H, V, ignore_index, scale, ent, L, ws);
-  hipError_t e = flce::launch_fwd_tile(a, ent, stream);
-  if (e != hipSuccess) return hip_fail(e, "forward tile kernel launch");
-  const flce::FwdMergeArgs b =
-      merge_args(targets, M, V, ignore_index, ent, logprob, lse, entropy, L, ws);
-  e = flce::launch_fwd_merge(b, ent, stream);
-  if (e != hipSuccess) return hip_fail(e, "forward merge kernel launch");
+  for (int64_t r0 = 0; r0 < M; r0 += rows) {
+    const int64_t mw = M - r0 < rows ? M - r0 : rows;
+    const FwdLayout L = fwd_layout(mw, V, ent);
+    const flce::FwdTileArgs a =
+        tile_args(static_cast<const uint16_t*>(X) + r0 * H, W, targets + r0, mw, H, V,
+                  ignore_index, scale, ent, L, ws);
+    hipError_t e = flce::launch_fwd_tile(a, ent, stream);
+    if (e != hipSuccess) return hip_fail(e, "forward tile kernel launch");
+    const flce::FwdMergeArgs b = merge_args(targets + r0, mw, V, ignore_index, ent, logprob + r0,
+                                            lse + r0, ent ? entropy + r0 : nullptr, L, ws);
+    e = flce::launch_fwd_merge(b, ent, stream);
+    if (e != hipSuccess) return hip_fail(e, "forward merge kernel launch");
+  }
   return ok();
 }
 

@@ -18,9 +18,10 @@ STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_INVALID_VALUE", 2: "FLCE_ERR_UNSUPPORTED",
           3: "FLCE_ERR_WORKSPACE_TOO_SMALL", 4: "FLCE_ERR_HIP"}
 
 # Every symbol include/flce.h declares.
-EXPORTS = ("flce_workspace_query", "flce_backward_workspace_min", "flce_backward_chunk_cols",
-           "flce_forward", "flce_forward_partials", "flce_forward_merge", "flce_backward", "flce_status_string", "flce_last_error_message",
-           "flce_version")
+EXPORTS = ("flce_workspace_query", "flce_forward_workspace_min", "flce_forward_wave_rows",
+           "flce_backward_workspace_min", "flce_backward_chunk_cols", "flce_forward",
+           "flce_forward_partials", "flce_forward_merge", "flce_backward", "flce_status_string",
+           "flce_last_error_message", "flce_version")
 
 _lib = None
 
@@ -42,6 +43,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     c = ctypes
     P, I64, SZ = c.c_void_p, c.c_int64, c.c_size_t
     lib.flce_workspace_query.argtypes = [I64, I64, I64, c.c_int, c.POINTER(SZ), c.POINTER(SZ)]
+    lib.flce_forward_workspace_min.argtypes = [I64, I64, I64, c.c_int, c.POINTER(SZ)]
+    lib.flce_forward_wave_rows.argtypes = [I64, I64, I64, c.c_int, SZ, c.POINTER(I64)]
     lib.flce_backward_workspace_min.argtypes = [I64, I64, I64, c.POINTER(SZ)]
     lib.flce_backward_chunk_cols.argtypes = [I64, I64, I64, SZ, c.POINTER(I64)]
     lib.flce_forward.argtypes = [P, P, P, I64, I64, I64, I64, c.c_float, c.c_int, P, P, P, P, SZ, P]
@@ -50,8 +53,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.flce_forward_merge.argtypes = [P, I64, I64, I64, I64, c.c_int, P, P, P, P, SZ, P]
     lib.flce_backward.argtypes = [P, P, P, I64, I64, I64, I64, c.c_float, P, P, P, P, P, P, P,
                                   SZ, P]
-    for name in ("flce_workspace_query", "flce_backward_workspace_min", "flce_backward_chunk_cols",
-                 "flce_forward", "flce_forward_partials", "flce_forward_merge", "flce_backward"):
+    for name in ("flce_workspace_query", "flce_forward_workspace_min", "flce_forward_wave_rows",
+                 "flce_backward_workspace_min", "flce_backward_chunk_cols", "flce_forward",
+                 "flce_forward_partials", "flce_forward_merge", "flce_backward"):
         getattr(lib, name).restype = c.c_int
     lib.flce_status_string.argtypes = [c.c_int]
     lib.flce_status_string.restype = c.c_char_p
@@ -73,6 +77,20 @@ def workspace_query(M: int, H: int, V: int, compute_entropy: bool = True) -> Tup
     _check(load().flce_workspace_query(M, H, V, int(bool(compute_entropy)), ctypes.byref(fwd),
                                        ctypes.byref(bwd)))
     return fwd.value, bwd.value
+
+
+def forward_workspace_min(M: int, H: int, V: int, compute_entropy: bool = True) -> int:
+    b = ctypes.c_size_t()
+    _check(load().flce_forward_workspace_min(M, H, V, int(bool(compute_entropy)), ctypes.byref(b)))
+    return b.value
+
+
+def forward_wave_rows(M: int, H: int, V: int, workspace_bytes: int,
+                      compute_entropy: bool = True) -> int:
+    r = ctypes.c_int64()
+    _check(load().flce_forward_wave_rows(M, H, V, int(bool(compute_entropy)), workspace_bytes,
+                                         ctypes.byref(r)))
+    return r.value
 
 
 def backward_workspace_min(M: int, H: int, V: int) -> int:

@@ -53,6 +53,24 @@ def test_workspace_query_values():
     assert c % 256 == 0 and 256 <= c < 151936 + 256
 
 
+def test_forward_token_waves():
+    # one 256-row wave: 3 partial arrays of [512 tiles, 256 rows] fp32 + the target logits
+    mn = flce.forward_workspace_min(8192, 8192, 131072, True)
+    assert mn == 3 * 512 * 256 * 4 + 256 * 4
+    assert flce.forward_workspace_min(8192, 8192, 131072, False) == 2 * 512 * 256 * 4 + 256 * 4
+    full, _ = flce.workspace_query(8192, 8192, 131072, True)
+    assert flce.forward_wave_rows(8192, 8192, 131072, full) == 8192
+    assert flce.forward_wave_rows(8192, 8192, 131072, mn) == 256
+    w4k = 3 * 512 * 4096 * 4 + 4096 * 4
+    assert flce.forward_wave_rows(8192, 8192, 131072, w4k) == 4096
+    assert flce.forward_wave_rows(8192, 8192, 131072, w4k - 1) == 3840
+    # the wave never exceeds the padded token count
+    assert flce.forward_wave_rows(300, 64, 1000, 1 << 30) == 512
+    with pytest.raises(flce.FlceError) as e:
+        flce.forward_wave_rows(8192, 8192, 131072, mn - 1)
+    assert e.value.status == 3
+
+
 def _status(fn, *args):
     return fn(*args)
 

@@ -106,6 +106,34 @@ def test_chunked_backward_matches():
     assert gu.rel_max(res_small["dX"], res_full["dX"]) <= 5e-3
 
 
+def test_forward_token_waves_bitwise():
+    """Token waves of 256 and 1024 rows (a ragged last wave: 5000 = 4 * 1024 + 904)
+    give the same bits as one wave, and match the oracle."""
+    import torch
+    from log_prob_amd import flce
+    c = inputs.make_case("waves", 126, 5000, 64, 300, grad_mode="normal", ignore_frac=0.05)
+    print(f"[parity] token waves M={c.M} H={c.H} V={c.V}", flush=True)
+    X, W, t, _, _ = gu.to_dev(c)
+    full, _ = flce.workspace_query(c.M, c.H, c.V, True)
+    mn = flce.forward_workspace_min(c.M, c.H, c.V, True)
+    w1k = mn * 4  # room for four 256-row tiles of partials per wave
+    assert flce.forward_wave_rows(c.M, c.H, c.V, w1k) == 1024
+    assert flce.forward_wave_rows(c.M, c.H, c.V, mn) == 256
+    outs = []
+    for nbytes in (full, mn, w1k):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        outs.append([v.clone() for v in flce.forward(X, W, t, c.ignore_index, c.scale, True,
+                                                      workspace=ws)])
+    torch.cuda.synchronize()
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    o = ref.forward(c.X, c.W, c.targets, c.ignore_index, c.scale, True)
+    res = {k: v.cpu().numpy().astype(np.float64) for k, v in zip(("logprob", "lse", "entropy"),
+                                                                 outs[1])}
+    gu.check_forward(res, o, True, "token_waves")
+
+
 def test_zero_grads_write_zeros():
     import torch
     from log_prob_amd import flce
