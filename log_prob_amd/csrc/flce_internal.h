@@ -9,11 +9,7 @@ namespace flce {
 
 constexpr int kTile = 256;  // backward workgroup tile edge; row padding of every buffer
 // Forward workgroup tile (rows of X x columns of W); kTile is a multiple of both.
-#ifdef FLCE_FWD_PAIR
-constexpr int kFwdTileM = 128;
-#else
 constexpr int kFwdTileM = 256;
-#endif
 constexpr int kFwdTileN = 256;
 static_assert(kTile % kFwdTileM == 0 && kTile % kFwdTileN == 0, "forward tiles pad to kTile");
 

@@ -55,7 +55,7 @@ constexpr int NTHREADS = 256;    // 4 waves of 64 in a 2 x 2 grid over the workg
 #define FLCE_LOAD_GROUPS 16
 #endif
 #ifndef FLCE_LOAD_EARLY
-#define FLCE_LOAD_EARLY 8
+#define FLCE_LOAD_EARLY -1
 #endif
 
 // Pin the instruction order of a sub-step: the fragment reads of sub-step kk + 1
@@ -64,9 +64,10 @@ constexpr int NTHREADS = 256;    // 4 waves of 64 in a 2 x 2 grid over the workg
 // registers right after their last MFMA and issues each read only one MFMA group
 // ahead, exposing the LDS latency.
 constexpr bool SCHED_PIPE = FLCE_SCHED_PIPE != 0;
-// A stage's loads are issued in LOAD_GROUPS groups per MFMA sub-step, placed
-// between the sub-step's MFMA groups; with two stages, LOAD_EARLY of them under the
-// last sub-step of the step before, the others under sub-step 0.
+// A stage's loads are issued in LOAD_GROUPS groups per MFMA sub-step (at most one
+// group per MFMA), placed between the sub-step's MFMA groups: LOAD_EARLY of them (by
+// default half) under the last sub-step of the step before, the others under
+// sub-step 0.
 constexpr int LOAD_GROUPS = FLCE_LOAD_GROUPS;
 constexpr int LOAD_EARLY = FLCE_LOAD_EARLY;
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // beyond every descriptor's num_records
@@ -80,21 +81,25 @@ constexpr float LN2 = 0.6931471805599453f;
 // is the occupancy the register budget is sized for: 2 lets two workgroups share a
 // CU, so one workgroup's barrier and load-issue stalls hide under the other's
 // matrix work (their LDS footprints must then fit 160 KiB together).
-template <int TM_, int TN_, int BK_, int NST_, int WAVES_PER_EU_>
+template <int TM_, int TN_, int BK_, int NST_, int WAVES_PER_EU_, int WAVES_M_ = 2,
+          int WAVES_N_ = 2>
 struct Shape {
   static constexpr int TM = TM_, TN = TN_, BK = BK_, NST = NST_;
   static constexpr int WAVES_PER_EU = WAVES_PER_EU_;
-  static constexpr int WM = TM / 2, WN = TN / 2;      // wave tile
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;  // wave grid over the tile
+  static constexpr int NWAVES = WAVES_M * WAVES_N, NTHREADS = 64 * NWAVES;
+  static constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N;    // wave tile
   static constexpr int MB = WM / 32, NB = WN / 32;    // 32 x 32 MFMA blocks per wave
   static constexpr int KK = BK / 16;                  // MFMA sub-steps per stage
   static constexpr int A_BYTES = TM * BK * 2, B_BYTES = TN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int PIPE_BYTES = NST * STAGE_BYTES;
-  static constexpr int DMA_A = A_BYTES / 4096, DMA_B = B_BYTES / 4096;  // 1 KiB loads per wave
+  static constexpr int DMA_A = A_BYTES / (1024 * NWAVES), DMA_B = B_BYTES / (1024 * NWAVES);  // 1 KiB loads per wave
   static constexpr int DMA_STAGE = DMA_A + DMA_B;
   static_assert(MB >= 2 && MB % 2 == 0 && NB >= 1, "wave tile");
   static_assert(BK == 32 || BK == 64, "K per stage");
-  static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole loads per wave");
+  static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0,
+                "whole loads per wave");
   static_assert(NST >= 2 && NST <= 4, "stages");
 };
 #ifndef FLCE_BIG_BK
@@ -105,16 +110,10 @@ struct Shape {
 #endif
 // One workgroup per CU: 256 x 256 tiles, waves of 128 x 128, 128 KiB of LDS stages.
 using BigShape = Shape<256, 256, FLCE_BIG_BK, FLCE_BIG_NST, 1>;
-// Two workgroups per CU: 128 x 256 tiles, waves of 64 x 128, 3 x 24 KiB of LDS.
-using PairShape = Shape<128, 256, 32, 3, 2>;
-
-// The forward runs BigShape: PairShape raises MFMA utilisation per cycle only a
-// little and its extra LDS and L2 traffic lowers the power-limited clock more.
-#ifdef FLCE_FWD_PAIR
-using FwdShape = PairShape;
-#else
+// The forward runs BigShape.  Eight waves of 128 x 64 (two per SIMD, Shape<256, 256,
+// 64, 2, 2, 2, 4>) hide more stalls but read 1.5x the LDS; with the lean K loop they
+// measured 5% slower.
 using FwdShape = BigShape;
-#endif
 static_assert(FwdShape::TM == kFwdTileM && FwdShape::TN == kFwdTileN, "host and kernel tile");
 #ifndef FLCE_FWD_GROUP_M
 #define FLCE_FWD_GROUP_M (2048 / kFwdTileM)
@@ -226,18 +225,22 @@ __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
 // position of the lane's 16 bytes within the step (in 8-element chunks for KC, in
 // K rows for MN, one byte per load).  A step keeps the loads whose K position lies
 // below a uniform limit and turns the others into zero fills, without branches.
-template <bool KC, int ROWS, int BK>
+template <bool KC, int ROWS, int BK, int NWAVES = 4>
 struct DmaPlan {
-  static constexpr int N = ROWS * BK * 2 / 4096;  // loads per wave
+  static constexpr int N = ROWS * BK * 2 / (1024 * NWAVES);  // loads per wave
   static constexpr int CHUNKS = BK / 8;           // KC: 16-byte chunks per tile row
   static constexpr int GPR = ROWS / 8;            // MN: 16-byte granules per K row
   static constexpr int KPOS_MAX = KC ? CHUNKS : BK;
   uint32_t voff[N];
   uint32_t kpos[(N + 3) / 4];
   int wave;
+  i32x4 rsrc0;        // buffer descriptor of the tile's base (k = 0), wave-uniform
+  uint32_t ld_bytes;  // row pitch in bytes (an M/N-contiguous tile moves by k0 rows)
 
   __device__ __forceinline__ void init(const TileSrc& s, int wave_id) {
     wave = wave_id;
+    rsrc0 = make_rsrc_fixed(s.base);
+    ld_bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)(s.ld * 2));
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int q = 0; q < (N + 3) / 4; ++q) kpos[q] = 0;
@@ -278,30 +281,39 @@ struct TileDma {
   int lim;
 };
 
-template <bool KC, int ROWS, int BK>
-__device__ __forceinline__ TileDma tile_dma(const TileSrc& s, const DmaPlan<KC, ROWS, BK>& plan,
+// FAST: the step lies entirely inside K (no per-lane K check, `lim` unused).  The
+// descriptor and offsets are derived from the plan with scalar arithmetic only.
+template <bool FAST, bool KC, int ROWS, int BK, int NW>
+__device__ __forceinline__ TileDma tile_dma(const TileSrc& s, const DmaPlan<KC, ROWS, BK, NW>& plan,
                                             int k0, bool active, const char* lds_tile) {
   TileDma d;
+  d.rsrc = plan.rsrc0;
   if constexpr (KC) {
-    d.rsrc = make_rsrc_fixed(s.base);
     d.soff = (uint32_t)k0 * 2u;
   } else {
-    d.rsrc = make_rsrc_fixed(s.base + (long)k0 * s.ld);
+    const uint64_t base = ((uint64_t)(uint32_t)plan.rsrc0.y << 32 | (uint32_t)plan.rsrc0.x) +
+                          (uint64_t)(uint32_t)k0 * plan.ld_bytes;
+    d.rsrc.x = (int)(uint32_t)base;
+    d.rsrc.y = (int)((base >> 32) & 0xffffu);
     d.soff = 0u;
   }
   d.lds0 = lds_addr_of(lds_tile) + (uint32_t)(plan.wave * plan.N * 1024);
-  const int rem = s.kvalid - k0;  // K extent left from k0 (a multiple of 8 for KC)
-  d.lim = !active ? 0 : KC ? min(max((rem + 7) >> 3, 0), plan.CHUNKS) : min(max(rem, 0), BK);
+  if constexpr (FAST) {
+    d.lim = KC ? plan.CHUNKS : BK;
+  } else {
+    const int rem = s.kvalid - k0;  // K extent left from k0 (a multiple of 8 for KC)
+    d.lim = !active ? 0 : KC ? min(max((rem + 7) >> 3, 0), plan.CHUNKS) : min(max(rem, 0), BK);
+  }
   return d;
 }
 
 // Load j of a tile.  m0 holds the LDS base of a group of 4 loads; `set_m0` rewrites
 // it (required for the first load issued after any other code that may touch m0 is
 // scheduled in between), the other loads of the group ride on the immediate offset.
-template <bool KC, int ROWS, int BK>
-__device__ __forceinline__ void tile_load(const TileDma& d, const DmaPlan<KC, ROWS, BK>& plan, int j,
+template <bool FAST, bool KC, int ROWS, int BK, int NW>
+__device__ __forceinline__ void tile_load(const TileDma& d, const DmaPlan<KC, ROWS, BK, NW>& plan, int j,
                                           bool set_m0) {
-  const uint32_t v = plan.off(j, d.lim);
+  const uint32_t v = FAST ? plan.voff[j] : plan.off(j, d.lim);
   const uint32_t m0 = d.lds0 + (uint32_t)(j & ~3) * 1024u;
   switch (j & 3) {
     case 0: dma16<0>(d.rsrc, v, d.soff, m0); break;
@@ -311,20 +323,12 @@ __device__ __forceinline__ void tile_load(const TileDma& d, const DmaPlan<KC, RO
   }
 }
 
-template <bool KC, int ROWS, int BK>
-__device__ __forceinline__ void load_tile_async(const TileSrc& s, const DmaPlan<KC, ROWS, BK>& plan,
-                                                int k0, const char* lds_tile) {
-  const TileDma d = tile_dma(s, plan, k0, true, lds_tile);
-#pragma unroll
-  for (int j = 0; j < plan.N; ++j) tile_load(d, plan, j, false);
-}
-
 // The loads of one whole stage: stage load j < DMA_A is load j of the A tile, the
 // rest are the B tile's.
-template <class S, bool A_KC, bool B_KC>
+template <class S, bool A_KC, bool B_KC, bool FAST = false>
 struct StageDma {
-  using PA = DmaPlan<A_KC, S::TM, S::BK>;
-  using PB = DmaPlan<B_KC, S::TN, S::BK>;
+  using PA = DmaPlan<A_KC, S::TM, S::BK, S::NWAVES>;
+  using PB = DmaPlan<B_KC, S::TN, S::BK, S::NWAVES>;
   TileDma a, b;
   const PA* pa;
   const PB* pb;
@@ -333,9 +337,9 @@ struct StageDma {
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
       if (j < S::DMA_A)
-        tile_load(a, *pa, j, j == j0);
+        tile_load<FAST>(a, *pa, j, j == j0);
       else
-        tile_load(b, *pb, j - S::DMA_A, j == j0 || j == S::DMA_A);
+        tile_load<FAST>(b, *pb, j - S::DMA_A, j == j0 || j == S::DMA_A);
     }
   }
 };
@@ -352,7 +356,9 @@ struct FragPlan {
   static constexpr int ROW_BYTES = KC ? BK * 2 : ROWS * 2;  // bytes per LDS row
   uint32_t off[NBLK][KC ? BK / 16 : 2];  // [block][kk] for KC, [block][half] for MN
 
-  __device__ __forceinline__ void init(int idx_base, int lane) {
+  // region: LDS byte offset of the operand's stage-0 tile, folded into the offsets so
+  // that a stage is selected by an instruction's immediate offset
+  __device__ __forceinline__ void init(int idx_base, int lane, uint32_t region) {
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) {
       const int idx0 = idx_base + 32 * blk;
@@ -361,7 +367,7 @@ struct FragPlan {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
           const int c = 2 * kk + (lane >> 5);
-          off[blk][kk] = r * ROW_BYTES + ((c ^ kc_swz<BK / 8>(r)) << 4);
+          off[blk][kk] = region + r * ROW_BYTES + ((c ^ kc_swz<BK / 8>(r)) << 4);
         }
       } else {
         const int g = lane >> 4, i = lane & 15;
@@ -369,7 +375,7 @@ struct FragPlan {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int k = 8 * (g >> 1) + 4 * hh + (i >> 2);   // kk adds 16 rows: k & 7 unchanged
-          off[blk][hh] = k * ROW_BYTES + ((((c0 >> 4) ^ (k & 7))) << 5) + ((c0 & 15) << 1);
+          off[blk][hh] = region + k * ROW_BYTES + ((((c0 >> 4) ^ (k & 7))) << 5) + ((c0 & 15) << 1);
         }
       }
     }
@@ -525,25 +531,33 @@ __device__ __forceinline__ void sched_substep() {
 // tile in the v_mfma_f32_32x32x16 layout: lane l, element e holds row
 // 8 (e / 4) + 4 (l / 32) + e % 4 and column l % 32.
 //
-// Pipeline: NST LDS stages.  The KK MFMA sub-steps of stage kt run with the
-// fragments of sub-step kk + 1 read (into the other register set) while the MFMAs
-// of sub-step kk are issued.  Before the last sub-step the wave waits for its own
-// loads of step kt + 1 and the barrier publishes that stage and releases stage kt
-// (all of whose reads have returned); the first fragments of step kt + 1 are then
-// read under the last sub-step's MFMAs, so no step starts with an LDS-latency
-// bubble.  The loads of step kt + NST go out in groups between MFMA groups: the
-// first EARLY of them under the last sub-step of step kt, right after the barrier
-// freed their stage, the rest under sub-step 0 of step kt + 1.  Every step issues
-// the same number of loads (steps past K only zero-fill their stage), so the wait
-// before each barrier is a fixed count.
+// Pipeline: two LDS stages, laid out as A0, A1, B0, B1 (the B region's base is folded
+// into the B fragment offsets, so every fragment read selects its stage with the
+// instruction's immediate offset and the K loop, unrolled by two, issues no address
+// arithmetic).  The KK MFMA sub-steps of stage kt run with the fragments of sub-step
+// kk + 1 read (into the other register set) while the MFMAs of sub-step kk are
+// issued.  Before the last sub-step the wave waits for its own loads of step kt + 1
+// and the barrier publishes that stage and releases stage kt (all of whose reads
+// have returned); the first fragments of step kt + 1 are then read under the last
+// sub-step's MFMAs, so no step starts with an LDS-latency bubble.  The loads of step
+// kt + 2 go out in groups between MFMA groups: the first EARLY of them under the last
+// sub-step of step kt, right after the barrier freed their stage, the rest under
+// sub-step 0 of step kt + 1.  Steps that lie entirely inside K take precomputed load
+// offsets; the last steps check each lane's K position, and steps past K only
+// zero-fill their stage, so every step issues the same number of loads and the wait
+// before each barrier is a fixed count.  Steps run in pairs (stage 0, stage 1); an
+// odd step count gets one step over a zero-filled stage.
 template <class S, bool A_KC, bool B_KC>
 __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem,
                                          const TileSrc& A, const TileSrc& B, int K) {
-  constexpr int KK = S::KK, D = S::DMA_STAGE, NST = S::NST;
-  constexpr int EARLY = LOAD_EARLY < D ? LOAD_EARLY : D;
-  static_assert((NST - 2) * D + EARLY < 64, "vmcnt range");
+  static_assert(S::NST == 2, "two LDS stages");
+  constexpr int KK = S::KK, D = S::DMA_STAGE;
+  constexpr int EARLY = LOAD_EARLY < 0 ? D / 2 : (LOAD_EARLY < D ? LOAD_EARLY : D);
+  constexpr int F = S::MB * S::NB, GR = LOAD_GROUPS < F ? LOAD_GROUPS : F;
+  static_assert(EARLY > 0 && EARLY < 64, "early loads");
+  static_assert(KK % 2 == 0, "sub-step 0 of every stage uses register set 0");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr0 = (wave >> 1) * S::WM, wc0 = (wave & 1) * S::WN;
+  const int wr0 = (wave / S::WAVES_N) * S::WM, wc0 = (wave % S::WAVES_N) * S::WN;
 #pragma unroll
   for (int mb = 0; mb < S::MB; ++mb)
 #pragma unroll
@@ -552,42 +566,49 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
       for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
 
   const int nk = (K + S::BK - 1) / S::BK;
+  // steps whose K range exists in both operands (an operand may hold fewer K rows than
+  // the loop runs over, e.g. X's M rows against a K of M rounded up to 256)
+  const int nfull = min(K, min(A.kvalid, B.kvalid)) / S::BK;
   typename StageDma<S, A_KC, B_KC>::PA plan_a;
   typename StageDma<S, A_KC, B_KC>::PB plan_b;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   plan_a.init(A, wave_u);
   plan_b.init(B, wave_u);
   Frags<S, A_KC, B_KC> frags;
-  frags.a.init(wr0, lane);
-  frags.b.init(wc0, lane);
-  // loads of step st into stage buffer `dst`; a step past K only zero-fills it
-  auto stage_dma = [&](int st, char* dst) {
-    StageDma<S, A_KC, B_KC> d;
+  frags.a.init(wr0, lane, 0u);
+  frags.b.init(wc0, lane, 2u * S::A_BYTES);
+  // loads of step st into stage s; a step past K only zero-fills it
+  auto stage_dma = [&](auto fast, int st, int s) {
+    constexpr bool FAST = decltype(fast)::value;
+    StageDma<S, A_KC, B_KC, FAST> d;
     d.pa = &plan_a;
     d.pb = &plan_b;
     const bool active = st < nk;
     const int k0 = (active ? st : 0) * S::BK;
-    d.a = tile_dma(A, plan_a, k0, active, dst);
-    d.b = tile_dma(B, plan_b, k0, active, dst + S::A_BYTES);
+    d.a = tile_dma<FAST>(A, plan_a, k0, active, smem + s * S::A_BYTES);
+    d.b = tile_dma<FAST>(B, plan_b, k0, active, smem + 2 * S::A_BYTES + s * S::B_BYTES);
     return d;
   };
-  auto stage_at = [&](int st) { return smem + (st % NST) * S::STAGE_BYTES; };
-  auto tiles_at = [&](int st) { return StagePtr{stage_at(st), stage_at(st) + S::A_BYTES}; };
-  // prologue: steps 0 .. NST - 2, and the early loads of step NST - 1
-#pragma unroll
-  for (int st = 0; st < NST - 1; ++st) stage_dma(st, stage_at(st)).issue(0, D);
-  if constexpr (EARLY > 0) stage_dma(NST - 1, stage_at(NST - 1)).issue(0, EARLY);
-  wait_vmcnt<(NST - 2) * D + EARLY>();  // step 0 has landed
+  using Slow = std::integral_constant<bool, false>;
+  using Fast = std::integral_constant<bool, true>;
+  using Stage0 = std::integral_constant<int, 0>;
+  using Stage1 = std::integral_constant<int, 1>;
+  // prologue: step 0, and the early loads of step 1
+  stage_dma(Slow(), 0, 0).issue(0, D);
+  stage_dma(Slow(), 1, 1).issue(0, EARLY);
+  wait_vmcnt<EARLY>();  // step 0 has landed
   __syncthreads();
-  static_assert(KK % 2 == 0, "sub-step 0 of every stage uses register set 0");
   bf16x8 af[2][S::MB], bfr[2][S::NB];
-  read_frags<S>(af[0], bfr[0], tiles_at(0), frags, 0);
-  constexpr auto groups = std::make_integer_sequence<int, LOAD_GROUPS>();
-  for (int kt = 0; kt < nk; ++kt) {
-    const StagePtr cur = tiles_at(kt);
+  read_frags<S>(af[0], bfr[0], StagePtr{smem, smem}, frags, 0);
+  constexpr auto groups = std::make_integer_sequence<int, GR>();
+  // one K step computed from stage STG (kt % 2 == STG)
+  auto step = [&](auto stg, auto fast, int kt) {
+    constexpr int STG = decltype(stg)::value;
+    const StagePtr cur{smem + STG * S::A_BYTES, smem + STG * S::B_BYTES};
+    const StagePtr nxt{smem + (1 - STG) * S::A_BYTES, smem + (1 - STG) * S::B_BYTES};
     {
-      StageDma<S, A_KC, B_KC> dma = stage_dma(kt + NST - 1, stage_at(kt + NST - 1));
-      substep_with_loads<0, 1, LOAD_GROUPS, EARLY, D, S>(acc, af, bfr, cur, frags, dma, groups);
+      auto dma = stage_dma(fast, kt + 1, 1 - STG);
+      substep_with_loads<0, 1, GR, EARLY, D, S>(acc, af, bfr, cur, frags, dma, groups);
     }
 #pragma unroll
     for (int kk = 1; kk < KK - 1; ++kk) {
@@ -599,20 +620,26 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
     // keep the barrier after every MFMA issued so far (the compiler would hoist it)
     __builtin_amdgcn_sched_barrier(0);
 #endif
-    // the loads of steps kt + 2 .. kt + NST - 1 may still be in flight
-    wait_vmcnt<(NST - 2) * D>();
+    wait_vmcnt<0>();
     __syncthreads();
-    // (after the last step this reads a stale stage; the values are never used)
-    const StagePtr next = tiles_at(kt + 1);
-    if constexpr (EARLY > 0) {
-      // stage kt is free now: it receives step kt + NST
-      StageDma<S, A_KC, B_KC> dma = stage_dma(kt + NST, stage_at(kt));
-      substep_with_loads<KK - 1, 0, LOAD_GROUPS, 0, EARLY, S>(acc, af, bfr, next, frags, dma, groups);
-    } else {
-      read_frags<S>(af[0], bfr[0], next, frags, 0);
-      mfma_block<S::MB, S::NB>(acc, af[1], bfr[1]);
-      sched_substep<S, true>();
+    // stage kt is free now: it receives step kt + 2 (after the last step this reads
+    // a stale stage; the values are never used)
+    {
+      auto dma = stage_dma(fast, kt + 2, STG);
+      substep_with_loads<KK - 1, 0, GR, 0, EARLY, S>(acc, af, bfr, nxt, frags, dma, groups);
     }
+  };
+  int kt = 0;
+  // iteration kt loads steps kt + 1 and kt + 2: both inside K while kt + 2 < nfull
+  for (; kt + 3 < nfull; kt += 2) {
+    step(Stage0(), Fast(), kt);
+    step(Stage1(), Fast(), kt + 1);
+  }
+  // the rest, also in pairs: with an odd step count the last step computes on a
+  // zero-filled stage and adds exact zeros
+  for (; kt < nk; kt += 2) {
+    step(Stage0(), Slow(), kt);
+    step(Stage1(), Slow(), kt + 1);
   }
   // the zero fills issued under the last steps must land before the caller reuses LDS
   wait_vmcnt<0>();
@@ -761,24 +788,28 @@ __device__ __forceinline__ void lane_row_max(const f32x16 (&acc)[S::MB][S::NB],
     }
 }
 
-// Shifted sums of each row slot over the lane's NB columns, in log2 units:
-// s = sum 2^d and u = sum 2^d d with d = c1 acc - m2 (c1 = scale log2 e, m2 = the
-// row maximum of c1 acc, read for both column halves from `red`).
+// Shifted sums of the 32 row slots of blocks mb0, mb0 + 1 over the lane's NB columns,
+// in log2 units: s = sum 2^d and u = sum 2^d d with d = c1 acc - m2 (c1 = scale
+// log2 e, m2 = the row maximum of c1 acc, from the WAVES_N column parts in `red`).
 template <bool ENT, bool RAGGED, class S>
 __device__ __forceinline__ void lane_row_sums(const f32x16 (&acc)[S::MB][S::NB], const float* red,
                                               int wr0, int lane, float c1, unsigned colmask,
-                                              float (&sv)[16 * S::MB],
-                                              float (&uv)[ENT ? 16 * S::MB : 1]) {
+                                              int mb0, float (&sv)[32], float (&uv)[ENT ? 32 : 1]) {
   const float ac1 = fabsf(c1);
 #pragma unroll
-  for (int mb = 0; mb < S::MB; ++mb)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       // rows 8 q + 4 (lane / 32) + 0..3 of block mb: slots e = 4 q + 0..3
+      const int mb = mb0 + mi;
       const int rb = wr0 + 32 * mb + 8 * q + 4 * (lane >> 5);
-      const float4 h0 = *reinterpret_cast<const float4*>(red + rb);
-      const float4 h1 = *reinterpret_cast<const float4*>(red + S::TM + rb);
-      const float mh[4] = {fmaxf(h0.x, h1.x), fmaxf(h0.y, h1.y), fmaxf(h0.z, h1.z), fmaxf(h0.w, h1.w)};
+      float mh[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int cp = 0; cp < S::WAVES_N; ++cp) {
+        const float4 h = *reinterpret_cast<const float4*>(red + cp * S::TM + rb);
+        mh[0] = fmaxf(mh[0], h.x); mh[1] = fmaxf(mh[1], h.y);
+        mh[2] = fmaxf(mh[2], h.z); mh[3] = fmaxf(mh[3], h.w);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = 4 * q + j;
@@ -792,8 +823,8 @@ __device__ __forceinline__ void lane_row_sums(const f32x16 (&acc)[S::MB][S::NB],
           s += pe;
           if constexpr (ENT) u = fmaf(pe, RAGGED ? fmaxf(d, -3.0e38f) : d, u);
         }
-        sv[16 * mb + e] = s;
-        if constexpr (ENT) uv[16 * mb + e] = u;
+        sv[16 * mi + e] = s;
+        if constexpr (ENT) uv[16 * mi + e] = u;
       }
     }
 }
@@ -805,11 +836,12 @@ __device__ __forceinline__ void lane_row_sums(const f32x16 (&acc)[S::MB][S::NB],
 // sum against the same shift and their partials simply add; thread t < TM writes the
 // partials of tile row t.
 template <class S, bool ENT>
-__global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(FwdTileArgs p) {
+__global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(FwdTileArgs p) {
   constexpr int TM = S::TM, TN = S::TN, MB = S::MB, NB = S::NB, WM = S::WM, WN = S::WN;
   constexpr int P = MB / 2;  // groups of 32 row slots per lane
+  constexpr int CP = S::WAVES_N;  // column parts: waves sharing the same rows
   __shared__ __attribute__((aligned(1024))) char smem[S::PIPE_BYTES];
-  static_assert(7 * TM * 4 <= S::PIPE_BYTES, "epilogue buffers");
+  static_assert((3 * CP + 1) * TM * 4 <= S::PIPE_BYTES, "epilogue buffers");
   int mt, vt;
   tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, FWD_GROUP_M, mt, vt);
   const int row0 = mt * TM, col0 = vt * TN;
@@ -833,14 +865,14 @@ __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(Fwd
   mainloop<S, true, true>(acc, smem, A, B, p.H);
   // (the mainloop ends with a barrier: the LDS is free)
 
-  const int wr0 = (wave >> 1) * WM, wc0 = (wave & 1) * WN, wn = wave & 1;
+  const int wr0 = (wave / CP) * WM, wc0 = (wave % CP) * WN, wn = wave % CP;
   const int lc = lane & 31;
   const float c1 = p.scale * LOG2E;  // logits in log2 units: z2 = c1 acc
 
-  // epilogue LDS: half-row maxima [2][TM], sums [2][2][TM], target columns [TM]
+  // epilogue LDS: row maxima per column part [CP][TM], sums [CP][2][TM], target columns [TM]
   float* red = reinterpret_cast<float*>(smem);
-  float* comb = red + 2 * TM;
-  int* t_col = reinterpret_cast<int*>(comb + 4 * TM);
+  float* comb = red + CP * TM;
+  int* t_col = reinterpret_cast<int*>(comb + 2 * CP * TM);
   if (tid < TM) t_col[tid] = tl;
 
   const bool ragged = col0 + TN > p.V;
@@ -848,7 +880,7 @@ __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(Fwd
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) colmask |= (col0 + wc0 + 32 * nb + lc < p.V ? 1u : 0u) << nb;
 
-  // row maxima of sgn(c1) acc: lane, half-wave, then both column halves via LDS
+  // row maxima of sgn(c1) acc: lane, half-wave, then the column parts via LDS
   {
     float mx[32 * P];
     if (!ragged) {
@@ -890,29 +922,34 @@ __global__ __launch_bounds__(NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(Fwd
       }
     }
 
-  // shifted sums against the full-row maximum
-  float sv[32 * P], uv[ENT ? 32 * P : 1];
-  if (!ragged)
-    lane_row_sums<ENT, false, S>(acc, red, wr0, lane, c1, colmask, sv, uv);
-  else
-    lane_row_sums<ENT, true, S>(acc, red, wr0, lane, c1, colmask, sv, uv);
-  reduce_scatter32<P>(sv, lane, [](float a, float b) { return a + b; });
-  if constexpr (ENT) reduce_scatter32<P>(uv, lane, [](float a, float b) { return a + b; });
-
+  // shifted sums against the full-row maximum, 32 row slots (two blocks) at a time
 #pragma unroll
   for (int pp = 0; pp < P; ++pp) {
+    float sv[32], uv[ENT ? 32 : 1];
+    if (!ragged)
+      lane_row_sums<ENT, false, S>(acc, red, wr0, lane, c1, colmask, 2 * pp, sv, uv);
+    else
+      lane_row_sums<ENT, true, S>(acc, red, wr0, lane, c1, colmask, 2 * pp, sv, uv);
+    reduce_scatter32<1>(sv, lane, [](float a, float b) { return a + b; });
+    if constexpr (ENT) reduce_scatter32<1>(uv, lane, [](float a, float b) { return a + b; });
     const int mb = 2 * pp + (lc >> 4), e = lc & 15;
     const int rl = wr0 + 32 * mb + acc_row(lane, e);
-    comb[(wn * 2 + 0) * TM + rl] = sv[32 * pp];
-    if constexpr (ENT) comb[(wn * 2 + 1) * TM + rl] = uv[32 * pp];
+    comb[(wn * 2 + 0) * TM + rl] = sv[0];
+    if constexpr (ENT) comb[(wn * 2 + 1) * TM + rl] = uv[0];
   }
   __syncthreads();
   if (tid < TM) {
-    const float m2 = fabsf(c1) * fmaxf(red[tid], red[TM + tid]);
+    float mx = red[tid], sm = comb[tid], um = comb[TM + tid];
+#pragma unroll
+    for (int cp = 1; cp < CP; ++cp) {
+      mx = fmaxf(mx, red[cp * TM + tid]);
+      sm += comb[(2 * cp) * TM + tid];
+      if constexpr (ENT) um += comb[(2 * cp + 1) * TM + tid];
+    }
     const long off = (long)vt * p.Mpad + row0 + tid;
-    p.part_m[off] = m2 * LN2;
-    p.part_s[off] = comb[0 * TM + tid] + comb[2 * TM + tid];
-    if constexpr (ENT) p.part_u[off] = (comb[1 * TM + tid] + comb[3 * TM + tid]) * LN2;
+    p.part_m[off] = fabsf(c1) * mx * LN2;
+    p.part_s[off] = sm;
+    if constexpr (ENT) p.part_u[off] = um * LN2;
   }
 }
 
@@ -1234,9 +1271,9 @@ __global__ void fill_u16_kernel(uint16_t* __restrict__ p, long n) {
 hipError_t launch_fwd_tile(const FwdTileArgs& a, bool ent, hipStream_t s) {
   const unsigned g = (unsigned)((long)a.n_mt * a.n_vt);
   if (ent)
-    fwd_tile_kernel<FwdShape, true><<<g, NTHREADS, 0, s>>>(a);
+    fwd_tile_kernel<FwdShape, true><<<g, FwdShape::NTHREADS, 0, s>>>(a);
   else
-    fwd_tile_kernel<FwdShape, false><<<g, NTHREADS, 0, s>>>(a);
+    fwd_tile_kernel<FwdShape, false><<<g, FwdShape::NTHREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 
