@@ -1003,9 +1003,6 @@ __global__ __launch_bounds__(MERGE_ROWS * MERGE_SLICES) void fwd_merge_kernel(Fw
 }
 
 // ---------------------------------------------------------------------------
-// Backward d-logits for one vocabulary chunk: dzs = scale * dz in bf16, written to
-// a [Mpad, ldz] buffer (chunk column j = vocabulary column vbase + j).  Columns past
-// V and rows past M are written as zero.
 // Stage a wave's d-logits, d = 2^(c1 acc - lse2) (c0 + cb acc) + [column = target] sa
 // (per-row parameters in LDS, see bwd_dlogits_kernel).  RAGGED: columns past V
 // (colmask bit nb clear) become 0.  Every wave runs the same instruction stream
@@ -1060,60 +1057,6 @@ __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4]
         for (int nb = 0; nb < 4; ++nb)
           stage_pair_bf16(tile, lane, rb + jp, wc0 + 32 * nb + lc, v[0][nb], v[1][nb]);
       }
-    }
-}
-
-// Backward d-logits for one vocabulary chunk: dzs = scale * dz in bf16, written to
-// a [Mpad, ldz] buffer (chunk column j = vocabulary column vbase + j).  Columns past
-// V and rows past M are written as zero.
-// Stage a wave's d-logits, d = 2^(c1 acc - lse2) (c0 + cb acc) + [column = target] sa
-// (per-row parameters in LDS, see bwd_dlogits_kernel).  TGT: the wave's rectangle holds
-// a target column; RAGGED: columns past V (colmask bit nb clear) become 0.
-template <bool ENTGRAD, bool RAGGED, bool TGT>
-__device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4][4],
-                                              const float* r_lse2, const float* r_c0,
-                                              const float* r_cb, const float* r_sa,
-                                              const int* t_local, int wr0, int wc0, int lane,
-                                              float c1, unsigned colmask) {
-  const int lc = lane & 31;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // rows rb .. rb + 3 are the lane's slots e = 4 q .. 4 q + 3 of block mb
-      const int rb = wr0 + 32 * mb + 8 * q + 4 * (lane >> 5);
-      const float4 L4 = *reinterpret_cast<const float4*>(r_lse2 + rb);
-      const float4 C4 = *reinterpret_cast<const float4*>(r_c0 + rb);
-      const float L[4] = {L4.x, L4.y, L4.z, L4.w}, C0[4] = {C4.x, C4.y, C4.z, C4.w};
-      float CB[4] = {0.f, 0.f, 0.f, 0.f}, SA[4] = {0.f, 0.f, 0.f, 0.f};
-      int DD[4] = {-1, -1, -1, -1};  // target column - first column of the lane
-      if constexpr (ENTGRAD) {
-        const float4 B4 = *reinterpret_cast<const float4*>(r_cb + rb);
-        CB[0] = B4.x; CB[1] = B4.y; CB[2] = B4.z; CB[3] = B4.w;
-      }
-      if constexpr (TGT) {
-        const float4 S4 = *reinterpret_cast<const float4*>(r_sa + rb);
-        const int4 T4 = *reinterpret_cast<const int4*>(t_local + rb);
-        SA[0] = S4.x; SA[1] = S4.y; SA[2] = S4.z; SA[3] = S4.w;
-        DD[0] = T4.x - wc0 - lc; DD[1] = T4.y - wc0 - lc; DD[2] = T4.z - wc0 - lc; DD[3] = T4.w - wc0 - lc;
-      }
-#pragma unroll
-      for (int jp = 0; jp < 4; jp += 2)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          float v[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int j = jp + h;
-            const float av = acc[mb][nb][4 * q + j];
-            const float pr = __builtin_amdgcn_exp2f(fmaf(av, c1, -L[j]));
-            float d = pr * (ENTGRAD ? fmaf(CB[j], av, C0[j]) : C0[j]);
-            if constexpr (TGT) d += DD[j] == 32 * nb ? SA[j] : 0.f;
-            if constexpr (RAGGED) d = ((colmask >> nb) & 1u) ? d : 0.f;
-            v[h] = d;
-          }
-          stage_pair_bf16(tile, lane, rb + jp, wc0 + 32 * nb + lc, v[0], v[1]);
-        }
     }
 }
 
@@ -1197,7 +1140,9 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
 __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
   int ti, th;
-  tile_coords(blockIdx.x, gridDim.x, p.n_i, p.n_h, 8, ti, th);
+  // groups run along H: the few X^T tiles stay in L2 while each dzs tile is read by
+  // one group of an XCD at a time, so dzs streams from HBM about once per H group
+  tile_coords(blockIdx.x, gridDim.x, p.n_h, p.n_i, 8, th, ti);
   const int i0 = ti * TILE, h0 = th * TILE;
   f32x16 acc[4][4];
   // dzs has Mpad rows (rows past M hold zeros); X has only M rows.
