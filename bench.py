@@ -249,6 +249,42 @@ def main():
     k_ms = timed(part, max(args.steps, 5))
     k_avg = float(np.mean(k_ms))
 
+    # one rank's share of a vocabulary-parallel split of the same workload: the rank's
+    # forward partials, the merge over all ranks' gathered partials, and the rank's
+    # backward (compute only: the all-gather and the dX all-reduce are the caller's)
+    shard_out = {}
+    dXp = torch.empty((M, H), dtype=torch.float32, device=dev)
+    for P in (2, 4, 8):
+        if V % P or (V // P) % 256:
+            continue
+        Vs = V // P
+        offs = [r * Vs for r in range(P + 1)]
+        stride = -(-flce.workspace_query(M, H, Vs, ent)[0] // 256) * 256
+        gathered = torch.empty(P * stride, dtype=torch.uint8, device=dev)
+        for r in range(P):
+            flce.forward_partials_shard(X, W[offs[r]:offs[r + 1]], t, offs[r], case.ignore_index,
+                                        case.scale, ent, workspace=gathered[r * stride:(r + 1) * stride])
+
+        def rank_fwd():
+            flce.forward_partials_shard(X, W[0:Vs], t, 0, case.ignore_index, case.scale, ent,
+                                        workspace=gathered[0:stride])
+            flce.forward_merge_shards(t, offs, gathered, stride, case.ignore_index, ent,
+                                      out=(logprob, lse, entropy))
+
+        def rank_bwd():
+            flce.backward_shard(X, W[0:Vs], t, 0, V, lse, entropy if gent is not None else None,
+                                glp, gent, dX_partial=dXp, ignore_index=case.ignore_index,
+                                scale=case.scale, workspace=ws, dW_shard=dW[0:Vs])
+        rank_fwd()
+        rank_bwd()
+        sf = float(np.median(timed(rank_fwd, max(args.steps, 5))))
+        sb = float(np.median(timed(rank_bwd, max(args.steps, 5))))
+        shard_out[f"tp{P}"] = {"V_shard": Vs, "fwd_ms": round(sf, 4),
+                               "fwd_tflops": round(2.0 * M * H * Vs / (sf * 1e-3) / 1e12, 2),
+                               "fwd_bwd_ms": round(sf + sb, 4),
+                               "fwd_bwd_tflops": round(8.0 * M * H * Vs / ((sf + sb) * 1e-3) / 1e12, 2)}
+        del gathered
+
     flop_f = 2.0 * M * H * V
     flop_fb = 8.0 * M * H * V
     tf_fb = flop_fb / (ms * 1e-3) / 1e12
@@ -280,6 +316,7 @@ def main():
         "fwd_token_waves": {"wave_rows": wave_rows, "ms": round(fwd_wave_ms, 4),
                             "tflops": round(flop_f / (fwd_wave_ms * 1e-3) / 1e12, 2),
                             "workspace_bytes": int(ws_wave.numel()), "full_workspace_bytes": fwd_b},
+        "vocab_shard_rank": shard_out,
         "roofline": {"bound": "mfma", "kernel": "fwd_tile_kernel (fused GEMM + online softmax)",
                      "achieved": round(k_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(k_tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),

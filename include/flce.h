@@ -158,6 +158,73 @@ flce_status_t flce_backward(const void* X, const void* W, const int64_t* targets
                             void* dX, void* dW,
                             void* workspace, size_t workspace_bytes, struct ihipStream_t* stream);
 
+/*
+ * Vocabulary shards (the tensor-parallel split of Liger-Kernel "native Blackwell
+ * tensor-parallel fused scaled linear cross-entropy", sections "Summary" and
+ * "Implementation": each rank holds a contiguous block of W's rows; SkyRL PR 2141,
+ * review of the TP-aware adapter: the rank only shifts vocabulary ids).  A shard is
+ * W rows [v_offset, v_offset + V_shard) of a vocabulary of V_total ids; targets stay
+ * global ids.  The three calls below are what one rank runs; the exchange between
+ * ranks (an all-gather of the partials, a sum of the dX partials) belongs to the
+ * caller's communication library.
+ *
+ * flce_forward_partials_shard: as flce_forward_partials for W_shard [V_shard, H]
+ * (the workspace layout is that of flce_forward_partials with V = V_shard; its
+ * size is *fwd_bytes of flce_workspace_query(M, H, V_shard, ...)).  The target
+ * logit of row m is written only if this shard owns t[m].  v_offset must be in
+ * [0, 2^30 - V_shard].
+ */
+flce_status_t flce_forward_partials_shard(const void* X, const void* W_shard,
+                                          const int64_t* targets, int64_t M, int64_t H,
+                                          int64_t V_shard, int64_t v_offset,
+                                          int64_t ignore_index, float scale, int compute_entropy,
+                                          void* workspace, size_t workspace_bytes,
+                                          struct ihipStream_t* stream);
+
+/*
+ * Merge of the gathered partials of n_shards shards (1 <= n_shards <= 64) into
+ * logprob, lse and entropy over the whole vocabulary.  shard_offsets is a HOST
+ * array of n_shards + 1 ids: shard r covers [shard_offsets[r], shard_offsets[r + 1]),
+ * shard_offsets[0] = 0 and the sequence strictly increases (V_total =
+ * shard_offsets[n_shards]).  Shard r's partials, exactly as
+ * flce_forward_partials_shard left them, start at byte r * shard_stride_bytes of
+ * `gathered` (device memory of n_shards * shard_stride_bytes bytes, 256-byte
+ * aligned; the stride is a multiple of 256 and at least every shard's forward
+ * workspace size).  Validity uses V_total; the target logit comes from the owning
+ * shard.  Results match flce_forward on the whole vocabulary up to fp32 summation
+ * order.
+ */
+flce_status_t flce_forward_merge_shards(const int64_t* targets, int64_t M, int64_t n_shards,
+                                        const int64_t* shard_offsets, int64_t ignore_index,
+                                        int compute_entropy, float* logprob, float* lse,
+                                        float* entropy, const void* gathered,
+                                        size_t shard_stride_bytes, struct ihipStream_t* stream);
+
+/* Workspace bytes for flce_backward_shard: the minimum (one 256-column d-logit
+ * chunk) and the preferred size (the d-logits of up to 2 GiB of columns at once).
+ * Either output may be NULL. */
+flce_status_t flce_backward_shard_workspace_query(int64_t M, int64_t H, int64_t V_shard,
+                                                  size_t* min_bytes, size_t* preferred_bytes);
+
+/*
+ * Backward of one shard, given the global lse (and entropy) from the merge:
+ * writes dW_shard [V_shard, H] bf16 (the shard's rows of dW) and this shard's
+ * term of dX, dz_shard W_shard * scale, in fp32 to dX_partial [M, H]: overwritten
+ * if accumulate == 0, added to if accumulate == 1 (one GPU can sum several shards
+ * in a fixed order this way; across ranks the terms are summed by an all-reduce).
+ * dX = sum over shards of dX_partial.  A row is valid iff t[m] != ignore_index and
+ * 0 <= t[m] < V_total.  workspace: at least the minimum of
+ * flce_backward_shard_workspace_query, 256-byte aligned.
+ */
+flce_status_t flce_backward_shard(const void* X, const void* W_shard, const int64_t* targets,
+                                  int64_t M, int64_t H, int64_t V_shard, int64_t v_offset,
+                                  int64_t V_total, int64_t ignore_index, float scale,
+                                  const float* lse, const float* entropy,
+                                  const float* grad_logprob, const float* grad_entropy,
+                                  float* dX_partial, int accumulate, void* dW_shard,
+                                  void* workspace, size_t workspace_bytes,
+                                  struct ihipStream_t* stream);
+
 /* Static description of a status code. */
 const char* flce_status_string(flce_status_t status);
 

@@ -241,8 +241,8 @@ flce_status_t check_forward_outputs(int compute_entropy, const float* logprob, c
 }
 
 flce::FwdTileArgs tile_args(const void* X, const void* W, const int64_t* targets, int64_t M,
-                            int64_t H, int64_t V, int64_t ignore_index, float scale, bool ent,
-                            const FwdLayout& L, char* ws) {
+                            int64_t H, int64_t V, int64_t v_off, int64_t ignore_index,
+                            float scale, bool ent, const FwdLayout& L, char* ws) {
   flce::FwdTileArgs a{};
   a.X = static_cast<const uint16_t*>(X);
   a.W = static_cast<const uint16_t*>(W);
@@ -250,6 +250,7 @@ flce::FwdTileArgs tile_args(const void* X, const void* W, const int64_t* targets
   a.M = int(M);
   a.H = int(H);
   a.V = int(V);
+  a.v_off = v_off;
   a.ignore_index = ignore_index;
   a.scale = scale;
   a.n_mt = int(L.n_mt);
@@ -262,45 +263,122 @@ flce::FwdTileArgs tile_args(const void* X, const void* W, const int64_t* targets
   return a;
 }
 
-flce::FwdMergeArgs merge_args(const int64_t* targets, int64_t M, int64_t V, int64_t ignore_index,
-                              bool ent, float* logprob, float* lse, float* entropy,
-                              const FwdLayout& L, const char* ws) {
+// Entry r of a shard table: the partials of vocabulary ids [v_lo, v_hi), laid out as
+// fwd_layout(rows, v_hi - v_lo) at byte offset `at` from the merge's base.
+void set_shard(flce::ShardTable& t, int r, int64_t v_lo, int64_t v_hi, const FwdLayout& L,
+               size_t at) {
+  t.v_lo[r] = v_lo;
+  t.v_lo[r + 1] = v_hi;
+  t.n_vt[r] = int(L.n_vt);
+  t.part_m[r] = long((at + L.off_m) / sizeof(float));
+  t.part_s[r] = long((at + L.off_s) / sizeof(float));
+  t.part_u[r] = long((at + L.off_u) / sizeof(float));
+  t.zt[r] = long((at + L.off_zt) / sizeof(float));
+}
+
+flce::FwdMergeArgs merge_args(const int64_t* targets, int64_t M, int64_t ignore_index, bool ent,
+                              float* logprob, float* lse, float* entropy, int64_t Mpad,
+                              const void* base) {
   flce::FwdMergeArgs b{};
   b.targets = targets;
   b.M = int(M);
-  b.V = int(V);
   b.ignore_index = ignore_index;
-  b.n_vt = int(L.n_vt);
-  b.Mpad = int(L.Mpad);
-  b.part_m = reinterpret_cast<const float*>(ws + L.off_m);
-  b.part_s = reinterpret_cast<const float*>(ws + L.off_s);
-  b.part_u = ent ? reinterpret_cast<const float*>(ws + L.off_u) : nullptr;
-  b.zt = reinterpret_cast<const float*>(ws + L.off_zt);
+  b.Mpad = int(Mpad);
+  b.base = static_cast<const float*>(base);
   b.logprob = logprob;
   b.lse = lse;
   b.entropy = ent ? entropy : nullptr;
   return b;
 }
 
+// Merge of one unsharded layout at ws.
+flce::FwdMergeArgs merge_args_single(const int64_t* targets, int64_t M, int64_t V,
+                                     int64_t ignore_index, bool ent, float* logprob, float* lse,
+                                     float* entropy, const FwdLayout& L, const char* ws) {
+  flce::FwdMergeArgs b = merge_args(targets, M, ignore_index, ent, logprob, lse, entropy, L.Mpad, ws);
+  b.sh.n = 1;
+  set_shard(b.sh, 0, 0, V, L, 0);
+  return b;
+}
+
 }  // namespace
+
+flce_status_t flce_forward_partials_shard(const void* X, const void* W_shard,
+                                          const int64_t* targets, int64_t M, int64_t H,
+                                          int64_t V_shard, int64_t v_offset,
+                                          int64_t ignore_index, float scale, int compute_entropy,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  if (!X || !W_shard || !targets || !workspace)
+    return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among X, W, targets, workspace");
+  if (v_offset < 0 || v_offset > kMaxV - V_shard)
+    return fail(FLCE_ERR_INVALID_VALUE, "v_offset %lld out of range for a shard of %lld rows",
+                (long long)v_offset, (long long)V_shard);
+  FwdLayout L;
+  flce_status_t st = check_forward_common(targets, M, H, V_shard, compute_entropy, workspace,
+                                          workspace_bytes, &L);
+  if (st != FLCE_OK) return st;
+  st = check_forward_inputs(X, W_shard, scale);
+  if (st != FLCE_OK) return st;
+  const bool ent = compute_entropy == 1;
+  const flce::FwdTileArgs a = tile_args(X, W_shard, targets, M, H, V_shard, v_offset,
+                                        ignore_index, scale, ent, L,
+                                        static_cast<char*>(workspace));
+  const hipError_t e = flce::launch_fwd_tile(a, ent, stream);
+  if (e != hipSuccess) return hip_fail(e, "forward tile kernel launch");
+  return ok();
+}
 
 flce_status_t flce_forward_partials(const void* X, const void* W, const int64_t* targets,
                                     int64_t M, int64_t H, int64_t V, int64_t ignore_index,
                                     float scale, int compute_entropy, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
-  if (!X || !W || !targets || !workspace)
-    return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among X, W, targets, workspace");
-  FwdLayout L;
-  flce_status_t st =
-      check_forward_common(targets, M, H, V, compute_entropy, workspace, workspace_bytes, &L);
-  if (st != FLCE_OK) return st;
-  st = check_forward_inputs(X, W, scale);
+  return flce_forward_partials_shard(X, W, targets, M, H, V, 0, ignore_index, scale,
+                                     compute_entropy, workspace, workspace_bytes, stream);
+}
+
+flce_status_t flce_forward_merge_shards(const int64_t* targets, int64_t M, int64_t n_shards,
+                                        const int64_t* shard_offsets, int64_t ignore_index,
+                                        int compute_entropy, float* logprob, float* lse,
+                                        float* entropy, const void* gathered,
+                                        size_t shard_stride_bytes, hipStream_t stream) {
+  if (!targets || !shard_offsets || !logprob || !lse || !gathered)
+    return fail(FLCE_ERR_INVALID_VALUE,
+                "NULL pointer among targets, shard_offsets, logprob, lse, gathered");
+  if (n_shards < 1 || n_shards > flce::kMaxShards)
+    return fail(FLCE_ERR_UNSUPPORTED, "n_shards must be in [1, %d] (got %lld)", flce::kMaxShards,
+                (long long)n_shards);
+  if (compute_entropy != 0 && compute_entropy != 1)
+    return fail(FLCE_ERR_INVALID_VALUE, "compute_entropy must be 0 or 1");
+  if (shard_offsets[0] != 0)
+    return fail(FLCE_ERR_INVALID_VALUE, "shard_offsets[0] must be 0 (got %lld)",
+                (long long)shard_offsets[0]);
+  if (!aligned(targets, 8)) return fail(FLCE_ERR_UNSUPPORTED, "targets must be 8-byte aligned");
+  if (!aligned(gathered, kAlign) || shard_stride_bytes % kAlign != 0)
+    return fail(FLCE_ERR_UNSUPPORTED, "gathered and shard_stride_bytes must be 256-byte aligned");
+  flce_status_t st = check_forward_outputs(compute_entropy, logprob, lse, entropy);
   if (st != FLCE_OK) return st;
   const bool ent = compute_entropy == 1;
-  const flce::FwdTileArgs a = tile_args(X, W, targets, M, H, V, ignore_index, scale, ent, L,
-                                        static_cast<char*>(workspace));
-  const hipError_t e = flce::launch_fwd_tile(a, ent, stream);
-  if (e != hipSuccess) return hip_fail(e, "forward tile kernel launch");
+  flce::FwdMergeArgs b = merge_args(targets, M, ignore_index, ent, logprob, lse, entropy,
+                                    cdiv(M, kTile) * kTile, gathered);
+  b.sh.n = int(n_shards);
+  for (int64_t r = 0; r < n_shards; ++r) {
+    const int64_t lo = shard_offsets[r], hi = shard_offsets[r + 1];
+    if (hi <= lo)
+      return fail(FLCE_ERR_INVALID_VALUE, "shard %lld is empty or reversed ([%lld, %lld))",
+                  (long long)r, (long long)lo, (long long)hi);
+    st = check_shape(M, 8, hi - lo);
+    if (st != FLCE_OK) return st;
+    if (hi > kMaxV) return fail(FLCE_ERR_UNSUPPORTED, "vocabulary larger than 2^30");
+    const FwdLayout L = fwd_layout(M, hi - lo, ent);
+    if (L.total > shard_stride_bytes)
+      return fail(FLCE_ERR_WORKSPACE_TOO_SMALL,
+                  "shard %lld needs %zu bytes of partials, stride is %zu", (long long)r, L.total,
+                  shard_stride_bytes);
+    set_shard(b.sh, int(r), lo, hi, L, size_t(r) * shard_stride_bytes);
+  }
+  const hipError_t e = flce::launch_fwd_merge(b, ent, stream);
+  if (e != hipSuccess) return hip_fail(e, "forward merge kernel launch");
   return ok();
 }
 
@@ -317,8 +395,8 @@ flce_status_t flce_forward_merge(const int64_t* targets, int64_t M, int64_t H, i
   st = check_forward_outputs(compute_entropy, logprob, lse, entropy);
   if (st != FLCE_OK) return st;
   const bool ent = compute_entropy == 1;
-  const flce::FwdMergeArgs b = merge_args(targets, M, V, ignore_index, ent, logprob, lse, entropy,
-                                          L, static_cast<const char*>(workspace));
+  const flce::FwdMergeArgs b = merge_args_single(targets, M, V, ignore_index, ent, logprob, lse,
+                                                 entropy, L, static_cast<const char*>(workspace));
   const hipError_t e = flce::launch_fwd_merge(b, ent, stream);
   if (e != hipSuccess) return hip_fail(e, "forward merge kernel launch");
   return ok();
@@ -353,27 +431,27 @@ flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets,
     const int64_t mw = M - r0 < rows ? M - r0 : rows;
     const FwdLayout L = fwd_layout(mw, V, ent);
     const flce::FwdTileArgs a =
-        tile_args(static_cast<const uint16_t*>(X) + r0 * H, W, targets + r0, mw, H, V,
+        tile_args(static_cast<const uint16_t*>(X) + r0 * H, W, targets + r0, mw, H, V, 0,
                   ignore_index, scale, ent, L, ws);
     hipError_t e = flce::launch_fwd_tile(a, ent, stream);
     if (e != hipSuccess) return hip_fail(e, "forward tile kernel launch");
-    const flce::FwdMergeArgs b = merge_args(targets + r0, mw, V, ignore_index, ent, logprob + r0,
-                                            lse + r0, ent ? entropy + r0 : nullptr, L, ws);
+    const flce::FwdMergeArgs b =
+        merge_args_single(targets + r0, mw, V, ignore_index, ent, logprob + r0, lse + r0,
+                          ent ? entropy + r0 : nullptr, L, ws);
     e = flce::launch_fwd_merge(b, ent, stream);
     if (e != hipSuccess) return hip_fail(e, "forward merge kernel launch");
   }
   return ok();
 }
 
-flce_status_t flce_backward(const void* X, const void* W, const int64_t* targets, int64_t M,
-                            int64_t H, int64_t V, int64_t ignore_index, float scale,
-                            const float* lse, const float* entropy, const float* grad_logprob,
-                            const float* grad_entropy, void* dX, void* dW, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
-  if (!X || !W || !targets || !lse || !dX || !dW || !workspace)
-    return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among X, W, targets, lse, dX, dW, workspace");
-  flce_status_t st = check_shape(M, H, V);
-  if (st != FLCE_OK) return st;
+}  // extern "C"
+
+namespace {
+
+flce_status_t check_backward_inputs(const void* X, const void* W, const int64_t* targets,
+                                    float scale, const float* lse, const float* entropy,
+                                    const float* grad_logprob, const float* grad_entropy,
+                                    const void* dX, const void* dW, const void* workspace) {
   if (grad_entropy && !entropy)
     return fail(FLCE_ERR_INVALID_VALUE, "grad_entropy given but entropy is NULL");
   if (!std::isfinite(scale)) return fail(FLCE_ERR_INVALID_VALUE, "scale is not finite");
@@ -384,27 +462,24 @@ flce_status_t flce_backward(const void* X, const void* W, const int64_t* targets
     return fail(FLCE_ERR_UNSUPPORTED, "targets and fp32 vectors must be naturally aligned");
   if (!aligned(workspace, kAlign))
     return fail(FLCE_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-  const int64_t chunk = chunk_for_workspace(M, H, V, workspace_bytes);
-  if (chunk == 0)
-    return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "backward needs at least %zu workspace bytes, got %zu",
-                bwd_bytes_for_chunk(M, H, V, kTile), workspace_bytes);
+  return FLCE_OK;
+}
 
-  if (!grad_logprob && !grad_entropy) {
-    hipError_t e = flce::launch_fill_zero_u16(static_cast<uint16_t*>(dX), long(M * H), stream);
-    if (e == hipSuccess)
-      e = flce::launch_fill_zero_u16(static_cast<uint16_t*>(dW), long(V * H), stream);
-    if (e != hipSuccess) return hip_fail(e, "zero-fill kernel launch");
-    return ok();
-  }
-
+// The backward over vocabulary chunks of `chunk` columns of W (rows v_off .. v_off + V - 1
+// of a vocabulary of V_total ids).  dX goes either to dX_bf16 (through the fp32
+// accumulator `acc` in the workspace when there is more than one chunk) or, when
+// dX_bf16 is NULL, to the caller's fp32 `acc`, which it overwrites (acc_in false) or
+// adds to (acc_in true).
+flce_status_t backward_chunks(const void* X, const void* W, const int64_t* targets, int64_t M,
+                              int64_t H, int64_t V, int64_t v_off, int64_t V_total,
+                              int64_t ignore_index, float scale, const float* lse,
+                              const float* entropy, const float* grad_logprob,
+                              const float* grad_entropy, uint16_t* dX_bf16, float* acc,
+                              bool acc_in, void* dW, uint16_t* dz, int64_t chunk,
+                              hipStream_t stream) {
   const int64_t n_mt = cdiv(M, kTile), Mpad = n_mt * kTile;
   const int64_t Vpad = cdiv(V, kTile) * kTile;
   const int64_t n_chunks = cdiv(Vpad, chunk);
-  char* ws = static_cast<char*>(workspace);
-  uint16_t* dz = reinterpret_cast<uint16_t*>(ws);
-  float* acc = n_chunks > 1
-                   ? reinterpret_cast<float*>(ws + align_up(size_t(Mpad) * size_t(chunk) * 2))
-                   : nullptr;
   const bool entgrad = grad_entropy != nullptr;
   for (int64_t c = 0; c < n_chunks; ++c) {
     const int64_t vbase = c * chunk;
@@ -417,6 +492,8 @@ flce_status_t flce_backward(const void* X, const void* W, const int64_t* targets
     d.M = int(M);
     d.H = int(H);
     d.V = int(V);
+    d.v_off = v_off;
+    d.V_total = V_total;
     d.ignore_index = ignore_index;
     d.scale = scale;
     d.lse = lse;
@@ -452,7 +529,7 @@ flce_status_t flce_backward(const void* X, const void* W, const int64_t* targets
     x.ldz = long(chunk);
     x.W = static_cast<const uint16_t*>(W);
     x.acc = acc;
-    x.dX = static_cast<uint16_t*>(dX);
+    x.dX = dX_bf16;
     x.M = int(M);
     x.H = int(H);
     x.V = int(V);
@@ -460,11 +537,120 @@ flce_status_t flce_backward(const void* X, const void* W, const int64_t* targets
     x.kcols = int(kc);
     x.n_m = int(n_mt);
     x.n_h = int(cdiv(H, kTile));
-    x.mode = n_chunks == 1 ? 0 : (c == 0 ? 1 : (c == n_chunks - 1 ? 3 : 2));
+    if (dX_bf16)
+      x.mode = n_chunks == 1 ? 0 : (c == 0 ? 1 : (c == n_chunks - 1 ? 3 : 2));
+    else
+      x.mode = (c == 0 && !acc_in) ? 1 : 2;
     e = flce::launch_gemm_dx(x, stream);
     if (e != hipSuccess) return hip_fail(e, "dX GEMM launch");
   }
   return ok();
+}
+
+// Widest d-logit chunk (a multiple of 256, at most the padded shard width) that fits
+// `bytes` when the workspace holds nothing else; 0 if none.
+int64_t shard_chunk_for_workspace(int64_t M, int64_t V, size_t bytes) {
+  const int64_t Mpad = cdiv(M, kTile) * kTile;
+  const int64_t Vpad = cdiv(V, kTile) * kTile;
+  int64_t c = int64_t(bytes / (size_t(Mpad) * 2)) / kTile * kTile;
+  if (c > kMaxChunk) c = kMaxChunk;
+  if (c > Vpad) c = Vpad;
+  while (c >= kTile && align_up(size_t(Mpad) * size_t(c) * 2) > bytes) c -= kTile;
+  return c >= kTile ? c : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+flce_status_t flce_backward(const void* X, const void* W, const int64_t* targets, int64_t M,
+                            int64_t H, int64_t V, int64_t ignore_index, float scale,
+                            const float* lse, const float* entropy, const float* grad_logprob,
+                            const float* grad_entropy, void* dX, void* dW, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!X || !W || !targets || !lse || !dX || !dW || !workspace)
+    return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among X, W, targets, lse, dX, dW, workspace");
+  flce_status_t st = check_shape(M, H, V);
+  if (st != FLCE_OK) return st;
+  st = check_backward_inputs(X, W, targets, scale, lse, entropy, grad_logprob, grad_entropy, dX,
+                             dW, workspace);
+  if (st != FLCE_OK) return st;
+  const int64_t chunk = chunk_for_workspace(M, H, V, workspace_bytes);
+  if (chunk == 0)
+    return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "backward needs at least %zu workspace bytes, got %zu",
+                bwd_bytes_for_chunk(M, H, V, kTile), workspace_bytes);
+
+  if (!grad_logprob && !grad_entropy) {
+    hipError_t e = flce::launch_fill_zero_u16(static_cast<uint16_t*>(dX), long(M * H), stream);
+    if (e == hipSuccess)
+      e = flce::launch_fill_zero_u16(static_cast<uint16_t*>(dW), long(V * H), stream);
+    if (e != hipSuccess) return hip_fail(e, "zero-fill kernel launch");
+    return ok();
+  }
+
+  const int64_t Mpad = cdiv(M, kTile) * kTile;
+  const int64_t Vpad = cdiv(V, kTile) * kTile;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws);
+  float* acc = chunk < Vpad
+                   ? reinterpret_cast<float*>(ws + align_up(size_t(Mpad) * size_t(chunk) * 2))
+                   : nullptr;
+  return backward_chunks(X, W, targets, M, H, V, 0, V, ignore_index, scale, lse, entropy,
+                         grad_logprob, grad_entropy, static_cast<uint16_t*>(dX), acc, false, dW,
+                         dz, chunk, stream);
+}
+
+flce_status_t flce_backward_shard_workspace_query(int64_t M, int64_t H, int64_t V_shard,
+                                                  size_t* min_bytes, size_t* preferred_bytes) {
+  flce_status_t st = check_shape(M, H, V_shard);
+  if (st != FLCE_OK) return st;
+  const int64_t Mpad = cdiv(M, kTile) * kTile;
+  if (min_bytes) *min_bytes = align_up(size_t(Mpad) * size_t(kTile) * 2);
+  if (preferred_bytes)
+    *preferred_bytes = align_up(size_t(Mpad) * size_t(preferred_chunk(M, V_shard)) * 2);
+  return ok();
+}
+
+flce_status_t flce_backward_shard(const void* X, const void* W_shard, const int64_t* targets,
+                                  int64_t M, int64_t H, int64_t V_shard, int64_t v_offset,
+                                  int64_t V_total, int64_t ignore_index, float scale,
+                                  const float* lse, const float* entropy,
+                                  const float* grad_logprob, const float* grad_entropy,
+                                  float* dX_partial, int accumulate, void* dW_shard,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!X || !W_shard || !targets || !lse || !dX_partial || !dW_shard || !workspace)
+    return fail(FLCE_ERR_INVALID_VALUE,
+                "NULL pointer among X, W_shard, targets, lse, dX_partial, dW_shard, workspace");
+  flce_status_t st = check_shape(M, H, V_shard);
+  if (st != FLCE_OK) return st;
+  if (V_total > kMaxV) return fail(FLCE_ERR_UNSUPPORTED, "V_total larger than 2^30");
+  if (v_offset < 0 || V_shard > V_total - v_offset)
+    return fail(FLCE_ERR_INVALID_VALUE, "shard [%lld, %lld) does not lie in [0, V_total=%lld)",
+                (long long)v_offset, (long long)(v_offset + V_shard), (long long)V_total);
+  if (accumulate != 0 && accumulate != 1)
+    return fail(FLCE_ERR_INVALID_VALUE, "accumulate must be 0 or 1");
+  st = check_backward_inputs(X, W_shard, targets, scale, lse, entropy, grad_logprob,
+                             grad_entropy, dX_partial, dW_shard, workspace);
+  if (st != FLCE_OK) return st;
+  const int64_t chunk = shard_chunk_for_workspace(M, V_shard, workspace_bytes);
+  if (chunk == 0)
+    return fail(FLCE_ERR_WORKSPACE_TOO_SMALL,
+                "shard backward needs at least %zu workspace bytes, got %zu",
+                align_up(size_t(cdiv(M, kTile) * kTile) * size_t(kTile) * 2), workspace_bytes);
+
+  if (!grad_logprob && !grad_entropy) {
+    hipError_t e = flce::launch_fill_zero_u16(static_cast<uint16_t*>(dW_shard),
+                                              long(V_shard * H), stream);
+    if (e == hipSuccess && !accumulate)
+      e = flce::launch_fill_zero_u16(reinterpret_cast<uint16_t*>(dX_partial), long(2 * M * H),
+                                     stream);
+    if (e != hipSuccess) return hip_fail(e, "zero-fill kernel launch");
+    return ok();
+  }
+  return backward_chunks(X, W_shard, targets, M, H, V_shard, v_offset, V_total, ignore_index,
+                         scale, lse, entropy, grad_logprob, grad_entropy, nullptr, dX_partial,
+                         accumulate == 1, dW_shard, static_cast<uint16_t*>(workspace), chunk,
+                         stream);
 }
 
 }  // extern "C"

@@ -15,9 +15,10 @@ static_assert(kTile % kFwdTileM == 0 && kTile % kFwdTileN == 0, "forward tiles p
 
 struct FwdTileArgs {
   const uint16_t* X;        // bf16 [M, H]
-  const uint16_t* W;        // bf16 [V, H]
-  const int64_t* targets;   // [M]
+  const uint16_t* W;        // bf16 [V, H]: vocabulary rows v_off .. v_off + V - 1
+  const int64_t* targets;   // [M], global vocabulary ids
   int M, H, V;
+  int64_t v_off;            // global id of W's first row (0 when W is the whole vocabulary)
   int64_t ignore_index;
   float scale;
   int n_mt, n_vt;           // forward tiles along M and V
@@ -28,25 +29,39 @@ struct FwdTileArgs {
   float* zt;                // [Mpad] target logit (written by the owning tile)
 };
 
+// Vocabulary shards whose partials one merge combines (a single shard for an
+// unsharded call).  Shard r covers global ids v_lo[r] .. v_lo[r + 1] - 1; its partial
+// arrays (n_vt[r] tiles of Mpad floats each) start at float offsets part_m[r],
+// part_s[r], part_u[r] (entropy only) and its target logits at zt[r], all relative
+// to FwdMergeArgs::base.
+constexpr int kMaxShards = 64;
+struct ShardTable {
+  int n;
+  int64_t v_lo[kMaxShards + 1];
+  int n_vt[kMaxShards];
+  long part_m[kMaxShards], part_s[kMaxShards], part_u[kMaxShards], zt[kMaxShards];
+};
+
 struct FwdMergeArgs {
   const int64_t* targets;
-  int M, V;
+  int M;
   int64_t ignore_index;
-  int n_vt, Mpad;
-  const float* part_m;
-  const float* part_s;
-  const float* part_u;
-  const float* zt;
+  int Mpad;
+  const float* base;
+  ShardTable sh;
   float* logprob;
   float* lse;
   float* entropy;
 };
+static_assert(sizeof(FwdMergeArgs) <= 4096, "merge arguments travel as kernel arguments");
 
 struct DlogitsArgs {
   const uint16_t* X;
-  const uint16_t* W;
-  const int64_t* targets;
+  const uint16_t* W;          // bf16 [V, H]: vocabulary rows v_off .. v_off + V - 1
+  const int64_t* targets;     // global vocabulary ids
   int M, H, V;
+  int64_t v_off;              // global id of W's first row
+  int64_t V_total;            // a row is valid iff its target lies in [0, V_total)
   int64_t ignore_index;
   float scale;
   const float* lse;

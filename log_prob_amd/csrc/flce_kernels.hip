@@ -854,8 +854,9 @@ __global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(
     const int r = row0 + tid;
     if (tid < TM && r < p.M) {
       const int64_t t = p.targets[r];
+      const int64_t tw = t - p.v_off;  // target as a row of W
       const int64_t hi = col0 + TN < p.V ? col0 + TN : p.V;
-      if (t != p.ignore_index && t >= col0 && t < hi) tl = (int)(t - col0);
+      if (t != p.ignore_index && tw >= col0 && tw < hi) tl = (int)(tw - col0);
     }
   }
 
@@ -955,6 +956,8 @@ __global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(
 
 // Merge of the per-tile partials of each row: m* = max m_j, S = sum s_j e^(m_j - m*),
 // U = sum e^(m_j - m*) (u_j + (m_j - m*) s_j); lse = m* + log S, entropy = log S - U / S.
+// The tiles j run over every shard of the table in order (one shard when the
+// vocabulary is not split); the target logit comes from the shard that owns the target.
 // A workgroup takes MERGE_ROWS rows; its MERGE_SLICES waves split each row's tiles
 // (lanes read consecutive rows of one tile, so every load is a coalesced 256 bytes)
 // and combine their maxima, then their sums, through LDS.
@@ -967,7 +970,10 @@ __global__ __launch_bounds__(MERGE_ROWS * MERGE_SLICES) void fwd_merge_kernel(Fw
   const bool live = row < p.M;
   float m = -INFINITY;
   if (live)
-    for (int j = sl; j < p.n_vt; j += MERGE_SLICES) m = fmaxf(m, p.part_m[(long)j * p.Mpad + row]);
+    for (int r = 0; r < p.sh.n; ++r) {
+      const float* pm = p.base + p.sh.part_m[r] + row;
+      for (int j = sl; j < p.sh.n_vt[r]; j += MERGE_SLICES) m = fmaxf(m, pm[(long)j * p.Mpad]);
+    }
   sm[0][sl][lr] = m;
   __syncthreads();
   float ms = -INFINITY;
@@ -975,13 +981,18 @@ __global__ __launch_bounds__(MERGE_ROWS * MERGE_SLICES) void fwd_merge_kernel(Fw
   for (int k = 0; k < MERGE_SLICES; ++k) ms = fmaxf(ms, sm[0][k][lr]);
   float S = 0.f, U = 0.f;
   if (live)
-    for (int j = sl; j < p.n_vt; j += MERGE_SLICES) {
-      const long off = (long)j * p.Mpad + row;
-      const float dm = p.part_m[off] - ms;
-      const float a = __expf(dm);
-      const float s = p.part_s[off];
-      S += s * a;
-      if constexpr (ENT) U += a * (p.part_u[off] + dm * s);
+    for (int r = 0; r < p.sh.n; ++r) {
+      const float* pm = p.base + p.sh.part_m[r] + row;
+      const float* ps = p.base + p.sh.part_s[r] + row;
+      const float* pu = p.base + p.sh.part_u[r] + row;
+      for (int j = sl; j < p.sh.n_vt[r]; j += MERGE_SLICES) {
+        const long off = (long)j * p.Mpad;
+        const float dm = pm[off] - ms;
+        const float a = __expf(dm);
+        const float s = ps[off];
+        S += s * a;
+        if constexpr (ENT) U += a * (pu[off] + dm * s);
+      }
     }
   sm[1][sl][lr] = S;
   sm[2][sl][lr] = U;
@@ -996,9 +1007,15 @@ __global__ __launch_bounds__(MERGE_ROWS * MERGE_SLICES) void fwd_merge_kernel(Fw
   }
   const float logS = logf(S);
   const int64_t t = p.targets[row];
-  const bool valid = t != p.ignore_index && t >= 0 && t < p.V;
+  const bool valid = t != p.ignore_index && t >= 0 && t < p.sh.v_lo[p.sh.n];
+  float zt = 0.f;
+  if (valid) {
+    int r = 0;
+    while (r + 1 < p.sh.n && t >= p.sh.v_lo[r + 1]) ++r;
+    zt = p.base[p.sh.zt[r] + row];
+  }
   p.lse[row] = ms + logS;
-  p.logprob[row] = valid ? p.zt[row] - (ms + logS) : 0.f;
+  p.logprob[row] = valid ? zt - (ms + logS) : 0.f;
   if constexpr (ENT) p.entropy[row] = valid ? logS - U / S : 0.f;
 }
 
@@ -1087,7 +1104,8 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
     const int r = row0 + tid;
     if (r < p.M) {
       const int64_t t = p.targets[r];
-      const bool valid = t != p.ignore_index && t >= 0 && t < p.V;
+      const bool valid = t != p.ignore_index && t >= 0 && t < p.V_total;
+      const int64_t tw = t - p.v_off;  // target as a row of W (owned iff 0 <= tw < V)
       const float lse = p.lse[r];
       lse2 = lse * LOG2E;
       if (valid) {
@@ -1099,7 +1117,7 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
           c0 = p.scale * (b * (lse - p.entropy[r]) - a);
           cb = -p.scale * p.scale * b;
         }
-        if (t >= col0 && t < col0 + TILE) tl = (int)(t - col0);
+        if (tw >= col0 && tw < col0 + TILE && tw < p.V) tl = (int)(tw - col0);
       }
     }
   }

@@ -20,7 +20,9 @@ STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_INVALID_VALUE", 2: "FLCE_ERR_UNSUPPORTED",
 # Every symbol include/flce.h declares.
 EXPORTS = ("flce_workspace_query", "flce_forward_workspace_min", "flce_forward_wave_rows",
            "flce_backward_workspace_min", "flce_backward_chunk_cols", "flce_forward",
-           "flce_forward_partials", "flce_forward_merge", "flce_backward", "flce_status_string",
+           "flce_forward_partials", "flce_forward_merge", "flce_backward",
+           "flce_forward_partials_shard", "flce_forward_merge_shards",
+           "flce_backward_shard_workspace_query", "flce_backward_shard", "flce_status_string",
            "flce_last_error_message", "flce_version")
 
 _lib = None
@@ -53,9 +55,19 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.flce_forward_merge.argtypes = [P, I64, I64, I64, I64, c.c_int, P, P, P, P, SZ, P]
     lib.flce_backward.argtypes = [P, P, P, I64, I64, I64, I64, c.c_float, P, P, P, P, P, P, P,
                                   SZ, P]
+    lib.flce_forward_partials_shard.argtypes = [P, P, P, I64, I64, I64, I64, I64, c.c_float,
+                                                c.c_int, P, SZ, P]
+    lib.flce_forward_merge_shards.argtypes = [P, I64, I64, c.POINTER(I64), I64, c.c_int, P, P, P,
+                                              P, SZ, P]
+    lib.flce_backward_shard_workspace_query.argtypes = [I64, I64, I64, c.POINTER(SZ),
+                                                        c.POINTER(SZ)]
+    lib.flce_backward_shard.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, c.c_float, P, P, P,
+                                        P, P, c.c_int, P, P, SZ, P]
     for name in ("flce_workspace_query", "flce_forward_workspace_min", "flce_forward_wave_rows",
                  "flce_backward_workspace_min", "flce_backward_chunk_cols", "flce_forward",
-                 "flce_forward_partials", "flce_forward_merge", "flce_backward"):
+                 "flce_forward_partials", "flce_forward_merge", "flce_backward",
+                 "flce_forward_partials_shard", "flce_forward_merge_shards",
+                 "flce_backward_shard_workspace_query", "flce_backward_shard"):
         getattr(lib, name).restype = c.c_int
     lib.flce_status_string.argtypes = [c.c_int]
     lib.flce_status_string.restype = c.c_char_p
@@ -103,6 +115,13 @@ def backward_chunk_cols(M: int, H: int, V: int, workspace_bytes: int) -> int:
     c = ctypes.c_int64()
     _check(load().flce_backward_chunk_cols(M, H, V, workspace_bytes, ctypes.byref(c)))
     return c.value
+
+
+def backward_shard_workspace_query(M: int, H: int, V_shard: int) -> Tuple[int, int]:
+    lo, pref = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().flce_backward_shard_workspace_query(M, H, V_shard, ctypes.byref(lo),
+                                                      ctypes.byref(pref)))
+    return lo.value, pref.value
 
 
 # ----------------------------------------------------------------------------
@@ -224,3 +243,77 @@ def backward(X, W, targets, lse, entropy=None, grad_logprob=None, grad_entropy=N
                                 _ptr(grad_entropy), _ptr(dX), _ptr(dW), _ptr(workspace),
                                 workspace.numel(), _stream(dev)))
     return dX, dW
+
+
+# ----------------------------------------------------------------------------
+# vocabulary shards: what one rank of a vocabulary-parallel group runs
+def forward_partials_shard(X, W_shard, targets, v_offset: int, ignore_index: int = -100,
+                           scale: float = 1.0, compute_entropy: bool = True, workspace=None):
+    """Partials of the shard W_shard = rows [v_offset, v_offset + V_shard) of W."""
+    import torch
+    M, H = X.shape
+    Vs = W_shard.shape[0]
+    _require(X, "X", torch.bfloat16, (M, H))
+    _require(W_shard, "W_shard", torch.bfloat16, (Vs, H))
+    _require(targets, "targets", torch.int64, (M,))
+    if workspace is None:
+        workspace = alloc_workspace(workspace_query(M, H, Vs, compute_entropy)[0], X.device)
+    _check(load().flce_forward_partials_shard(_ptr(X), _ptr(W_shard), _ptr(targets), M, H, Vs,
+                                              int(v_offset), int(ignore_index), float(scale),
+                                              int(bool(compute_entropy)), _ptr(workspace),
+                                              workspace.numel(), _stream(X.device)))
+    return workspace
+
+
+def forward_merge_shards(targets, shard_offsets, gathered, shard_stride_bytes: int,
+                         ignore_index: int = -100, compute_entropy: bool = True, out=None):
+    """Merge gathered shard partials (shard r at byte r * stride of `gathered`)."""
+    import torch
+    M = targets.shape[0]
+    _require(targets, "targets", torch.int64, (M,))
+    offs = (ctypes.c_int64 * len(shard_offsets))(*[int(v) for v in shard_offsets])
+    dev = targets.device
+    if out is None:
+        logprob = torch.empty(M, dtype=torch.float32, device=dev)
+        lse = torch.empty(M, dtype=torch.float32, device=dev)
+        entropy = torch.empty(M, dtype=torch.float32, device=dev) if compute_entropy else None
+    else:
+        logprob, lse, entropy = out
+    _check(load().flce_forward_merge_shards(_ptr(targets), M, len(shard_offsets) - 1, offs,
+                                            int(ignore_index), int(bool(compute_entropy)),
+                                            _ptr(logprob), _ptr(lse), _ptr(entropy),
+                                            _ptr(gathered), int(shard_stride_bytes),
+                                            _stream(dev)))
+    return logprob, lse, entropy
+
+
+def backward_shard(X, W_shard, targets, v_offset: int, V_total: int, lse, entropy=None,
+                   grad_logprob=None, grad_entropy=None, dX_partial=None, accumulate=False,
+                   ignore_index: int = -100, scale: float = 1.0, workspace=None, dW_shard=None):
+    """(dX_partial fp32 [M, H], dW_shard bf16) of one shard; dX is the sum over shards."""
+    import torch
+    M, H = X.shape
+    Vs = W_shard.shape[0]
+    _require(X, "X", torch.bfloat16, (M, H))
+    _require(W_shard, "W_shard", torch.bfloat16, (Vs, H))
+    _require(targets, "targets", torch.int64, (M,))
+    _require(lse, "lse", torch.float32, (M,))
+    for name, t in (("entropy", entropy), ("grad_logprob", grad_logprob),
+                    ("grad_entropy", grad_entropy)):
+        if t is not None:
+            _require(t, name, torch.float32, (M,))
+    dev = X.device
+    if dX_partial is None:
+        dX_partial = torch.empty((M, H), dtype=torch.float32, device=dev)
+    _require(dX_partial, "dX_partial", torch.float32, (M, H))
+    if dW_shard is None:
+        dW_shard = torch.empty_like(W_shard)
+    if workspace is None:
+        workspace = alloc_workspace(backward_shard_workspace_query(M, H, Vs)[1], dev)
+    _check(load().flce_backward_shard(_ptr(X), _ptr(W_shard), _ptr(targets), M, H, Vs,
+                                      int(v_offset), int(V_total), int(ignore_index),
+                                      float(scale), _ptr(lse), _ptr(entropy),
+                                      _ptr(grad_logprob), _ptr(grad_entropy), _ptr(dX_partial),
+                                      int(bool(accumulate)), _ptr(dW_shard), _ptr(workspace),
+                                      workspace.numel(), _stream(dev)))
+    return dX_partial, dW_shard

@@ -139,3 +139,62 @@ def test_python_wrapper_raises():
     assert e.value.status == 1
     with pytest.raises(flce.FlceError):
         flce.backward_chunk_cols(100, 64, 1000, 10)
+
+
+def test_shard_workspace_query():
+    lo, pref = flce.backward_shard_workspace_query(8192, 8192, 16384)
+    assert lo == 8192 * 256 * 2
+    assert pref == 8192 * 16384 * 2          # the whole shard in one chunk
+    lo, pref = flce.backward_shard_workspace_query(300, 64, 1000)
+    assert lo == 512 * 256 * 2 and pref == 512 * 1024 * 2
+
+
+def _fps(lib, X=16, W=16, t=16, M=4, H=8, Vs=3, off=0, ign=-100, scale=1.0, ent=1, ws=256,
+         wsb=1 << 20):
+    return lib.flce_forward_partials_shard(X, W, t, M, H, Vs, off, ign, scale, ent, ws, wsb, None)
+
+
+def _merge(lib, offs, t=16, M=4, ign=-100, ent=1, lp=16, lse=16, entropy=16, g=256,
+           stride=1 << 16):
+    arr = None if offs is None else (ctypes.c_int64 * len(offs))(*offs)
+    n = 0 if offs is None else len(offs) - 1
+    return lib.flce_forward_merge_shards(t, M, n, arr, ign, ent, lp, lse, entropy, g, stride,
+                                         None)
+
+
+def _bws(lib, X=16, W=16, t=16, M=4, H=8, Vs=3, off=0, Vt=3, ign=-100, scale=1.0, lse=16,
+         ent=16, glp=16, gent=16, dXp=16, acc=0, dW=16, ws=256, wsb=1 << 20):
+    return lib.flce_backward_shard(X, W, t, M, H, Vs, off, Vt, ign, scale, lse, ent, glp, gent,
+                                   dXp, acc, dW, ws, wsb, None)
+
+
+def test_shard_argument_errors():
+    lib = flce.load()
+    INV, UNS, WS = 1, 2, 3
+    # forward partials of a shard
+    assert _fps(lib, off=-1) == INV
+    assert _fps(lib, off=(1 << 30) - 2) == INV   # shard would end past 2^30 ids
+    assert _fps(lib, W=None) == INV
+    assert _fps(lib, W=24) == UNS
+    assert _fps(lib, wsb=16) == WS
+    # merge of gathered partials
+    assert _merge(lib, None) == INV
+    assert _merge(lib, [0]) == UNS                       # no shard
+    assert _merge(lib, list(range(0, 66 * 256, 256))) == UNS   # 65 shards
+    assert _merge(lib, [1, 5, 9]) == INV                 # must start at 0
+    assert _merge(lib, [0, 5, 5]) == INV                 # empty shard
+    assert _merge(lib, [0, 5, 3]) == INV                 # reversed
+    assert _merge(lib, [0, 5, 9], g=128) == UNS
+    assert _merge(lib, [0, 5, 9], stride=1000) == UNS
+    assert _merge(lib, [0, 5, 9], stride=256) == WS      # below one shard's partials
+    assert _merge(lib, [0, 5, 9], ent=1, entropy=None) == INV
+    # backward of a shard
+    assert _bws(lib, off=-1) == INV
+    assert _bws(lib, off=1, Vs=3, Vt=3) == INV           # shard past V_total
+    assert _bws(lib, Vt=1 << 31) == UNS
+    assert _bws(lib, acc=2) == INV
+    assert _bws(lib, dXp=None) == INV
+    assert _bws(lib, ent=None) == INV                    # grad_entropy needs entropy
+    assert _bws(lib, dXp=20) == UNS
+    mn, _ = flce.backward_shard_workspace_query(4, 8, 3)
+    assert _bws(lib, wsb=mn - 1) == WS
