@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, help="workload config (default 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shard-bench", action="store_true",
+                    help="skip the per-rank vocabulary-shard timings (profiling runs)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the oracle sample (0: sized for ~15 s)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -254,7 +256,7 @@ def main():
     # backward (compute only: the all-gather and the dX all-reduce are the caller's)
     shard_out = {}
     dXp = torch.empty((M, H), dtype=torch.float32, device=dev)
-    for P in (2, 4, 8):
+    for P in (() if args.no_shard_bench else (2, 4, 8)):
         if V % P or (V // P) % 256:
             continue
         Vs = V // P
