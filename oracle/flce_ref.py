@@ -45,6 +45,7 @@ import numpy as np
 __all__ = [
     "decode_bf16", "valid_rows", "logits", "from_logits", "forward_f64", "forward",
     "forward_rows", "backward_f64", "backward", "dx_rows", "dw_rows", "row_block",
+    "nll_reduce", "nll_mean_grad",
 ]
 
 
@@ -216,3 +217,29 @@ def dw_rows(X_bits, W_bits, t, vrows, ignore_index, scale, lse, E,
     onehot = (t[:, None] == vrows[None, :]) & valid[:, None]
     dZc = a[:, None] * (onehot - Pc) + b[:, None] * Pc * (np.asarray(E)[:, None] - Zc)
     return s * (dZc.T @ Xd)
+
+
+def nll_reduce(logprob, t, V, ignore_index):
+    """Scalar cross-entropy reductions over the valid rows: (sum of -logprob, number of
+    valid rows, their mean; NaN when no row is valid).
+
+    The mean token-level NLL is the usual scalar loss of the fused linear
+    cross-entropy (Liger-Kernel commit "native Blackwell tensor-parallel fused scaled
+    linear cross-entropy", "Summary": NLL fused with the classifier GEMM); SkyRL PR
+    2141, "Summary", keeps such reductions out of the per-token log-prob kernels, so
+    here they run on the log-probs.
+    """
+    valid = valid_rows(t, V, ignore_index)
+    lp = np.asarray(logprob, np.float64)
+    total = float(-np.sum(lp[valid]))
+    n = int(np.count_nonzero(valid))
+    return total, n, (total / n if n else float("nan"))
+
+
+def nll_mean_grad(t, V, ignore_index, n_valid):
+    """dL/dlogprob of L = mean NLL over the valid rows: -1/n on valid rows, 0 elsewhere."""
+    valid = valid_rows(t, V, ignore_index)
+    g = np.zeros(len(valid))
+    if n_valid:
+        g[valid] = -1.0 / n_valid
+    return g

@@ -282,3 +282,47 @@ def test_subset_helpers_match_full():
     np.testing.assert_allclose(
         ref.dw_rows(c.X, c.W, c.targets, vrows, -100, c.scale, o["lse"], o["E"],
                     c.grad_logprob, c.grad_entropy), dW[vrows], atol=1e-13)
+
+
+def test_nll_reduce_against_torch_cross_entropy():
+    """Sum and mean NLL over valid rows equal torch's cross_entropy reductions (fp64 CPU
+    library routine, independent of the oracle's arithmetic)."""
+    rng = np.random.default_rng(23)
+    M, H, V = 13, 16, 41
+    X = _bits(rng.standard_normal((M, H)))
+    W = _bits(rng.standard_normal((V, H)) / 4)
+    t = rng.integers(0, V, M)
+    t[[1, 5, 9]] = -100
+    s = float(np.float32(0.9))
+    o = ref.forward(X, W, t, -100, s, False)
+    total, n, mean = ref.nll_reduce(o["logprob"], t, V, -100)
+    Z = s * (torch.tensor(ref.decode_bf16(X)) @ torch.tensor(ref.decode_bf16(W)).T)
+    tt = torch.tensor(t)
+    ce_sum = torch.nn.functional.cross_entropy(Z, tt, ignore_index=-100, reduction="sum")
+    ce_mean = torch.nn.functional.cross_entropy(Z, tt, ignore_index=-100, reduction="mean")
+    assert n == M - 3
+    np.testing.assert_allclose(total, float(ce_sum), rtol=1e-13)
+    np.testing.assert_allclose(mean, float(ce_mean), rtol=1e-13)
+    # the gradient of the mean NLL through the log-probs: torch autograd of the mean
+    Zg = Z.clone().requires_grad_(True)
+    torch.nn.functional.cross_entropy(Zg, tt, ignore_index=-100, reduction="mean").backward()
+    g = ref.nll_mean_grad(t, V, -100, n)
+    dZ = ref.from_logits(Z.numpy(), t, -100, False, grad_logprob=g)["dZ"]
+    np.testing.assert_allclose(dZ, Zg.grad.numpy(), atol=1e-14)
+
+
+def test_nll_reduce_special_cases():
+    # no valid row: sum 0, count 0, mean undefined (NaN), zero gradient
+    t = np.array([-100, 7, -3])
+    total, n, mean = ref.nll_reduce(np.array([1.0, 2.0, 3.0]), t, 5, -100)
+    assert total == 0.0 and n == 0 and np.isnan(mean)
+    assert np.all(ref.nll_mean_grad(t, 5, -100, 0) == 0.0)
+    # brute force on a tiny case: a plain loop over the rows
+    lp = np.array([-0.5, -1.25, -3.0, -0.125])
+    t = np.array([0, 2, 9, 1])        # row 2 is out of range
+    acc, cnt = 0.0, 0
+    for i in range(4):
+        if t[i] != -100 and 0 <= t[i] < 4:
+            acc += -lp[i]
+            cnt += 1
+    assert ref.nll_reduce(lp, t, 4, -100) == (acc, cnt, acc / cnt)
