@@ -225,6 +225,30 @@ flce_status_t flce_backward_shard(const void* X, const void* W_shard, const int6
                                   void* workspace, size_t workspace_bytes,
                                   struct ihipStream_t* stream);
 
+/*
+ * Scalar cross-entropy reductions over the valid rows of a forward's logprob
+ * (the token-level NLL of Liger-Kernel "native Blackwell tensor-parallel fused
+ * scaled linear cross-entropy", section "Summary", reduced outside the per-token
+ * kernels as SkyRL PR 2141, section "Summary", keeps it).  Writes three fp64
+ * values to the device array out: the sum of -logprob[m] over valid rows, the
+ * number of valid rows, and their mean (NaN when no row is valid).  One
+ * workgroup with a fixed summation order: the result is bitwise repeatable.
+ * Validity as in flce_forward (t != ignore_index and 0 <= t < V).
+ */
+flce_status_t flce_nll_reduce(const float* logprob, const int64_t* targets, int64_t M,
+                              int64_t V, int64_t ignore_index, double* out,
+                              struct ihipStream_t* stream);
+
+/*
+ * dL/dlogprob for L = the mean NLL: grad_logprob[m] = -1/n on valid rows and 0
+ * elsewhere, n read on the device from reduced[1] (the out array of
+ * flce_nll_reduce), so no host synchronisation is needed; all zeros when n = 0.
+ * The result is the grad_logprob argument of flce_backward.
+ */
+flce_status_t flce_nll_mean_grad(const int64_t* targets, int64_t M, int64_t V,
+                                 int64_t ignore_index, const double* reduced,
+                                 float* grad_logprob, struct ihipStream_t* stream);
+
 /* Static description of a status code. */
 const char* flce_status_string(flce_status_t status);
 

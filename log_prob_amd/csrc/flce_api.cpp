@@ -653,4 +653,39 @@ flce_status_t flce_backward_shard(const void* X, const void* W_shard, const int6
                          stream);
 }
 
+flce_status_t flce_nll_reduce(const float* logprob, const int64_t* targets, int64_t M,
+                              int64_t V, int64_t ignore_index, double* out, hipStream_t stream) {
+  if (!logprob || !targets || !out)
+    return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among logprob, targets, out");
+  if (M <= 0 || V <= 0)
+    return fail(FLCE_ERR_INVALID_VALUE, "M and V must be positive (got M=%lld V=%lld)",
+                (long long)M, (long long)V);
+  if (M > kMaxM || V > kMaxV)
+    return fail(FLCE_ERR_UNSUPPORTED, "shape too large (limits M, V <= 2^30)");
+  if (!aligned(logprob, 4) || !aligned(targets, 8) || !aligned(out, 8))
+    return fail(FLCE_ERR_UNSUPPORTED, "logprob, targets and out must be naturally aligned");
+  const hipError_t e = flce::launch_nll_reduce(logprob, targets, long(M), V, ignore_index, out,
+                                               stream);
+  if (e != hipSuccess) return hip_fail(e, "NLL reduction kernel launch");
+  return ok();
+}
+
+flce_status_t flce_nll_mean_grad(const int64_t* targets, int64_t M, int64_t V,
+                                 int64_t ignore_index, const double* reduced,
+                                 float* grad_logprob, hipStream_t stream) {
+  if (!targets || !reduced || !grad_logprob)
+    return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among targets, reduced, grad_logprob");
+  if (M <= 0 || V <= 0)
+    return fail(FLCE_ERR_INVALID_VALUE, "M and V must be positive (got M=%lld V=%lld)",
+                (long long)M, (long long)V);
+  if (M > kMaxM || V > kMaxV)
+    return fail(FLCE_ERR_UNSUPPORTED, "shape too large (limits M, V <= 2^30)");
+  if (!aligned(targets, 8) || !aligned(reduced, 8) || !aligned(grad_logprob, 4))
+    return fail(FLCE_ERR_UNSUPPORTED, "targets, reduced and grad_logprob must be naturally aligned");
+  const hipError_t e = flce::launch_nll_mean_grad(targets, long(M), V, ignore_index, reduced,
+                                                  grad_logprob, stream);
+  if (e != hipSuccess) return hip_fail(e, "NLL gradient kernel launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -104,5 +104,9 @@ hipError_t launch_dlogits(const DlogitsArgs& a, bool entropy_grad, hipStream_t s
 hipError_t launch_gemm_dw(const GemmDwArgs& a, hipStream_t s);
 hipError_t launch_gemm_dx(const GemmDxArgs& a, hipStream_t s);
 hipError_t launch_fill_zero_u16(uint16_t* p, long n, hipStream_t s);
+hipError_t launch_nll_reduce(const float* logprob, const int64_t* targets, long M, int64_t V,
+                             int64_t ignore_index, double* out, hipStream_t s);
+hipError_t launch_nll_mean_grad(const int64_t* targets, long M, int64_t V, int64_t ignore_index,
+                                const double* reduced, float* grad, hipStream_t s);
 
 }  // namespace flce

@@ -1223,6 +1223,58 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
   }
 }
 
+// Scalar cross-entropy reductions over the valid rows, in one workgroup so the order
+// of every addition is fixed (bitwise repeatable): thread t takes rows t, t + 1024, ...
+// in fp64, then a fixed tree over the threads.  out = {sum of -logprob, valid rows,
+// mean (NaN without a valid row)}.
+constexpr int NLL_THREADS = 1024;
+__global__ __launch_bounds__(NLL_THREADS) void nll_reduce_kernel(const float* __restrict__ logprob,
+                                                                 const int64_t* __restrict__ targets,
+                                                                 long M, int64_t V,
+                                                                 int64_t ignore_index,
+                                                                 double* __restrict__ out) {
+  __shared__ double ss[NLL_THREADS];
+  __shared__ long sc[NLL_THREADS];
+  const int t = threadIdx.x;
+  double s = 0.0;
+  long c = 0;
+  for (long i = t; i < M; i += NLL_THREADS) {
+    const int64_t tg = targets[i];
+    if (tg != ignore_index && tg >= 0 && tg < V) {
+      s -= (double)logprob[i];
+      ++c;
+    }
+  }
+  ss[t] = s;
+  sc[t] = c;
+  __syncthreads();
+  for (int w = NLL_THREADS / 2; w > 0; w >>= 1) {
+    if (t < w) {
+      ss[t] += ss[t + w];
+      sc[t] += sc[t + w];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    out[0] = ss[0];
+    out[1] = (double)sc[0];
+    out[2] = sc[0] > 0 ? ss[0] / (double)sc[0] : __builtin_nan("");
+  }
+}
+
+// grad[i] = -1 / n on valid rows (n = the valid-row count in reduced[1]), else 0.
+__global__ void nll_mean_grad_kernel(const int64_t* __restrict__ targets, long M, int64_t V,
+                                     int64_t ignore_index, const double* __restrict__ reduced,
+                                     float* __restrict__ grad) {
+  const double n = reduced[1];
+  const float g = n > 0.0 ? (float)(-1.0 / n) : 0.f;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < M; i += stride) {
+    const int64_t tg = targets[i];
+    grad[i] = (tg != ignore_index && tg >= 0 && tg < V) ? g : 0.f;
+  }
+}
+
 __global__ void fill_u16_kernel(uint16_t* __restrict__ p, long n) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const long stride = (long)gridDim.x * blockDim.x;
@@ -1265,6 +1317,20 @@ hipError_t launch_gemm_dw(const GemmDwArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_dx(const GemmDxArgs& a, hipStream_t s) {
   gemm_dx_kernel<<<(unsigned)((long)a.n_m * a.n_h), NTHREADS, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_nll_reduce(const float* logprob, const int64_t* targets, long M, int64_t V,
+                             int64_t ignore_index, double* out, hipStream_t s) {
+  nll_reduce_kernel<<<1, NLL_THREADS, 0, s>>>(logprob, targets, M, V, ignore_index, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_nll_mean_grad(const int64_t* targets, long M, int64_t V, int64_t ignore_index,
+                                const double* reduced, float* grad, hipStream_t s) {
+  long blocks = (M + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  nll_mean_grad_kernel<<<(unsigned)blocks, 256, 0, s>>>(targets, M, V, ignore_index, reduced, grad);
   return hipGetLastError();
 }
 

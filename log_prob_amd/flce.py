@@ -22,7 +22,8 @@ EXPORTS = ("flce_workspace_query", "flce_forward_workspace_min", "flce_forward_w
            "flce_backward_workspace_min", "flce_backward_chunk_cols", "flce_forward",
            "flce_forward_partials", "flce_forward_merge", "flce_backward",
            "flce_forward_partials_shard", "flce_forward_merge_shards",
-           "flce_backward_shard_workspace_query", "flce_backward_shard", "flce_status_string",
+           "flce_backward_shard_workspace_query", "flce_backward_shard", "flce_nll_reduce",
+           "flce_nll_mean_grad", "flce_status_string",
            "flce_last_error_message", "flce_version")
 
 _lib = None
@@ -63,7 +64,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                         c.POINTER(SZ)]
     lib.flce_backward_shard.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, c.c_float, P, P, P,
                                         P, P, c.c_int, P, P, SZ, P]
-    for name in ("flce_workspace_query", "flce_forward_workspace_min", "flce_forward_wave_rows",
+    lib.flce_nll_reduce.argtypes = [P, P, I64, I64, I64, P, P]
+    lib.flce_nll_mean_grad.argtypes = [P, I64, I64, I64, P, P, P]
+    for name in ("flce_nll_reduce", "flce_nll_mean_grad", "flce_workspace_query",
+                 "flce_forward_workspace_min", "flce_forward_wave_rows",
                  "flce_backward_workspace_min", "flce_backward_chunk_cols", "flce_forward",
                  "flce_forward_partials", "flce_forward_merge", "flce_backward",
                  "flce_forward_partials_shard", "flce_forward_merge_shards",
@@ -317,3 +321,33 @@ def backward_shard(X, W_shard, targets, v_offset: int, V_total: int, lse, entrop
                                       int(bool(accumulate)), _ptr(dW_shard), _ptr(workspace),
                                       workspace.numel(), _stream(dev)))
     return dX_partial, dW_shard
+
+
+# ----------------------------------------------------------------------------
+# scalar cross-entropy reductions on the log-probs
+def nll_reduce(logprob, targets, V: int, ignore_index: int = -100, out=None):
+    """fp64 device tensor [sum of -logprob over valid rows, valid rows, mean NLL]."""
+    import torch
+    M = logprob.shape[0]
+    _require(logprob, "logprob", torch.float32, (M,))
+    _require(targets, "targets", torch.int64, (M,))
+    if out is None:
+        out = torch.empty(3, dtype=torch.float64, device=logprob.device)
+    _require(out, "out", torch.float64, (3,))
+    _check(load().flce_nll_reduce(_ptr(logprob), _ptr(targets), M, int(V), int(ignore_index),
+                                  _ptr(out), _stream(logprob.device)))
+    return out
+
+
+def nll_mean_grad(targets, V: int, reduced, ignore_index: int = -100, out=None):
+    """grad_logprob of the mean NLL (-1/n on valid rows) from nll_reduce's output."""
+    import torch
+    M = targets.shape[0]
+    _require(targets, "targets", torch.int64, (M,))
+    _require(reduced, "reduced", torch.float64, (3,))
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=targets.device)
+    _require(out, "grad_logprob", torch.float32, (M,))
+    _check(load().flce_nll_mean_grad(_ptr(targets), M, int(V), int(ignore_index), _ptr(reduced),
+                                     _ptr(out), _stream(targets.device)))
+    return out

@@ -198,3 +198,17 @@ def test_shard_argument_errors():
     assert _bws(lib, dXp=20) == UNS
     mn, _ = flce.backward_shard_workspace_query(4, 8, 3)
     assert _bws(lib, wsb=mn - 1) == WS
+
+
+def test_nll_argument_errors():
+    lib = flce.load()
+    INV, UNS = 1, 2
+    assert lib.flce_nll_reduce(None, 16, 4, 3, -100, 16, None) == INV
+    assert lib.flce_nll_reduce(16, 16, 0, 3, -100, 16, None) == INV
+    assert lib.flce_nll_reduce(16, 16, 4, 0, -100, 16, None) == INV
+    assert lib.flce_nll_reduce(16, 16, 1 << 31, 3, -100, 16, None) == UNS
+    assert lib.flce_nll_reduce(18, 16, 4, 3, -100, 16, None) == UNS
+    assert lib.flce_nll_reduce(16, 16, 4, 3, -100, 20, None) == UNS
+    assert lib.flce_nll_mean_grad(16, 4, 3, -100, None, 16, None) == INV
+    assert lib.flce_nll_mean_grad(16, -1, 3, -100, 16, 16, None) == INV
+    assert lib.flce_nll_mean_grad(12, 4, 3, -100, 16, 16, None) == UNS
