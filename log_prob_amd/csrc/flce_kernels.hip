@@ -171,8 +171,12 @@ __device__ __forceinline__ int kc_swz(int r) {
 }
 
 // LDS layout of an MN tile of `cols` columns: BK K rows of 2 cols bytes (cols / 16
-// blocks of 32 bytes); block b of K row k sits at block position b ^ (k & 7).  The
-// 4 consecutive K rows one transposing read touches land on distinct blocks.
+// blocks of 32 bytes); block b of K row k sits at block position b ^ mn_swz(k).  Each
+// half-wave of a transposing fragment read takes two adjacent blocks (2j, 2j + 1) of
+// 4 consecutive K rows; mn_swz maps those 4 rows to {0, 2, 5, 7}, so the 8 (row,
+// block) pairs fall on the 8 distinct 32-byte bank groups of the 256-byte bank row
+// (with k & 7 as the swizzle they took only 4, a 2-way conflict on every read).
+__device__ __forceinline__ int mn_swz(int k) { return ((k & 3) << 1) ^ ((k >> 1) & 1); }
 
 // One 64-lane direct-to-LDS load: lane i's 16 bytes from byte offset voff of the
 // buffer go to LDS address lds_addr + 16 i.  Issued as inline assembly so that the
@@ -253,7 +257,7 @@ struct DmaPlan {
         b = (G % CHUNKS) ^ kc_swz<CHUNKS>(a);    // 16-byte chunk of K in the row
       } else {
         a = G / GPR;                             // K row
-        b = (G % GPR) ^ ((a & 7) << 1);          // 16-byte chunk of columns
+        b = (G % GPR) ^ (mn_swz(a) << 1);        // 16-byte chunk of columns
       }
       const bool ok = KC ? a < s.valid : 8 * b < s.valid;
       // the load's immediate offset (1 KiB x (j % 4)) is added back by the hardware
@@ -374,8 +378,8 @@ struct FragPlan {
         const int c0 = idx0 + 16 * (g & 1) + 4 * (i & 3);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int k = 8 * (g >> 1) + 4 * hh + (i >> 2);   // kk adds 16 rows: k & 7 unchanged
-          off[blk][hh] = region + k * ROW_BYTES + ((((c0 >> 4) ^ (k & 7))) << 5) + ((c0 & 15) << 1);
+          const int k = 8 * (g >> 1) + 4 * hh + (i >> 2);  // kk adds 16 rows: mn_swz unchanged
+          off[blk][hh] = region + k * ROW_BYTES + (((c0 >> 4) ^ mn_swz(k)) << 5) + ((c0 & 15) << 1);
         }
       }
     }
