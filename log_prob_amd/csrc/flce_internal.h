@@ -70,12 +70,12 @@ struct DlogitsArgs {
   const float* grad_entropy;  // NULL = 0
   int vbase;                  // first vocabulary column of the chunk
   int n_mt, n_vt;             // tiles along M and along the chunk
-  uint16_t* dz;               // bf16 [Mpad, ldz]: scale * dz of the chunk
+  uint16_t* dz;               // bf16 Mpad x ldz, tile-blocked: scale * dz of the chunk
   long ldz;
 };
 
 struct GemmDwArgs {
-  const uint16_t* dz;   // bf16 [Mpad, ldz]
+  const uint16_t* dz;   // bf16 Mpad x ldz, tile-blocked (256-row bands of 256 x 64 blocks)
   long ldz;
   const uint16_t* X;    // bf16 [M, H]
   uint16_t* dW;         // bf16 [V, H]
@@ -86,7 +86,7 @@ struct GemmDwArgs {
 };
 
 struct GemmDxArgs {
-  const uint16_t* dz;   // bf16 [Mpad, ldz]
+  const uint16_t* dz;   // bf16 Mpad x ldz, tile-blocked (256-row bands of 256 x 64 blocks)
   long ldz;
   const uint16_t* W;    // bf16 [V, H]
   float* acc;           // fp32 [M, H] accumulator across chunks (modes 1-3)

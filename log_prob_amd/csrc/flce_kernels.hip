@@ -152,14 +152,20 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int n_m, int n
 //     matrix with leading dimension ld; `valid` rows of the tile exist.
 //  M/N-contiguous (MN): `base` is element (k = 0, column 0 of the tile) of a
 //     [K][cols] matrix with leading dimension ld; `valid` columns of the tile exist.
-// `kvalid` is the K extent that exists; `span` the number of elements from `base`
-// to the end of the underlying allocation (a bound for the buffer descriptor).
+// `kvalid` is the K extent that exists.  `band` = 0 for a row-major matrix; otherwise
+// the matrix is tile-blocked (the d-logit buffer): 256-row bands of `band` elements,
+// each a row of 256 x 64 blocks (16384 elements, row r of a block at 64 r).  A KC
+// operand then reads the rows of its band (base = the band's start, ld = 64) and moves
+// one block per 64 K; an MN operand reads 64-column blocks of consecutive K rows
+// (base = block 0 of band 0 of its columns).
+constexpr int BLK_ROWS = 256, BLK_COLS = 64, BLK_ELEMS = BLK_ROWS * BLK_COLS;
+static_assert(BigShape::BK == BLK_COLS && BigShape::TM == BLK_ROWS, "one block per K step");
 struct TileSrc {
   const uint16_t* base;
   long ld;
   int valid;
   int kvalid;
-  long span;
+  long band;
 };
 
 // LDS layout of a KC tile: rows of BK bf16 (BK / 8 chunks of 16 bytes); chunk c of
@@ -238,13 +244,19 @@ struct DmaPlan {
   uint32_t voff[N];
   uint32_t kpos[(N + 3) / 4];
   int wave;
-  i32x4 rsrc0;        // buffer descriptor of the tile's base (k = 0), wave-uniform
-  uint32_t ld_bytes;  // row pitch in bytes (an M/N-contiguous tile moves by k0 rows)
+  i32x4 rsrc0;         // buffer descriptor of the tile's base (k = 0), wave-uniform
+  uint32_t kc_bytes;   // KC: bytes per K element (2, or 512 in a blocked matrix)
+  uint32_t row_bytes;  // MN: bytes per K row within a 256-row band
+  uint32_t band_bytes; // MN: bytes per 256-row band
 
   __device__ __forceinline__ void init(const TileSrc& s, int wave_id) {
     wave = wave_id;
     rsrc0 = make_rsrc_fixed(s.base);
-    ld_bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)(s.ld * 2));
+    const bool blk = s.band != 0;
+    kc_bytes = blk ? 2u * BLK_ROWS : 2u;
+    row_bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)(blk ? 2 * BLK_COLS : s.ld * 2));
+    band_bytes = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(blk ? s.band * 2 : (long)BLK_ROWS * s.ld * 2));
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int q = 0; q < (N + 3) / 4; ++q) kpos[q] = 0;
@@ -260,8 +272,11 @@ struct DmaPlan {
         b = (G % GPR) ^ (mn_swz(a) << 1);        // 16-byte chunk of columns
       }
       const bool ok = KC ? a < s.valid : 8 * b < s.valid;
+      // element offset in the step: a blocked MN row's 16-byte chunk b lies in block b / 8
+      const long e = (!KC && blk) ? (long)(b >> 3) * BLK_ELEMS + (long)a * BLK_COLS + 8 * (b & 7)
+                                  : (long)a * s.ld + 8 * b;
       // the load's immediate offset (1 KiB x (j % 4)) is added back by the hardware
-      voff[j] = (ok ? (uint32_t)(((long)a * s.ld + 8 * b) * 2) : OOB_OFFSET) - 1024u * (j & 3);
+      voff[j] = (ok ? (uint32_t)(e * 2) : OOB_OFFSET) - 1024u * (j & 3);
       kpos[j >> 2] |= (uint32_t)(KC ? b : a) << (8 * (j & 3));
     }
   }
@@ -274,8 +289,9 @@ struct DmaPlan {
 };
 
 // Per-step state of one operand's loads.  A K-contiguous tile keeps one buffer base
-// for the whole K loop and moves with the scalar offset (k0 * 2 bytes stays far below
-// 2^31); an M/N-contiguous tile moves its base by k0 rows.  `lim` (uniform) is the
+// for the whole K loop and moves with the scalar offset (k0 times 2 bytes, or 512 in a
+// blocked matrix, stays below 2^31); an M/N-contiguous tile moves its base by k0 rows
+// (k0 / 256 bands and k0 % 256 rows of a band).  `lim` (uniform) is the
 // number of the step's K positions that exist: 0 for a step past the end of K, whose
 // loads then only zero-fill a free stage.
 struct TileDma {
@@ -293,10 +309,11 @@ __device__ __forceinline__ TileDma tile_dma(const TileSrc& s, const DmaPlan<KC, 
   TileDma d;
   d.rsrc = plan.rsrc0;
   if constexpr (KC) {
-    d.soff = (uint32_t)k0 * 2u;
+    d.soff = (uint32_t)k0 * plan.kc_bytes;
   } else {
     const uint64_t base = ((uint64_t)(uint32_t)plan.rsrc0.y << 32 | (uint32_t)plan.rsrc0.x) +
-                          (uint64_t)(uint32_t)k0 * plan.ld_bytes;
+                          (uint64_t)(uint32_t)(k0 >> 8) * plan.band_bytes +
+                          (uint64_t)(uint32_t)(k0 & 255) * plan.row_bytes;
     d.rsrc.x = (int)(uint32_t)base;
     d.rsrc.y = (int)((base >> 32) & 0xffffu);
     d.soff = 0u;
@@ -768,6 +785,21 @@ __device__ __forceinline__ void store_tile_bf16(const char* tile, uint16_t* dst,
   }
 }
 
+// Copy a staged 256 x 256 bf16 tile into its four 256 x 64 blocks of a tile-blocked
+// buffer (block q, columns 64 q .. 64 q + 63, at dst + q BLK_ELEMS; row r at 64 r).
+// Consecutive threads write consecutive 16 bytes, so each wave stores 1 KiB at once.
+__device__ __forceinline__ void store_tile_blocked(const char* tile, uint16_t* dst) {
+  const int t = threadIdx.x;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int G = it * NTHREADS + t;  // 16-byte granule in destination order
+    const int q = G >> 11, r = (G >> 3) & 255, c8 = G & 7;
+    const char* src = tile + (r << 9) + ((((q << 3) | c8) ^ out_swz(r)) << 4);
+    *reinterpret_cast<u32x4*>(dst + (long)q * BLK_ELEMS + r * BLK_COLS + 8 * c8) =
+        *reinterpret_cast<const u32x4*>(src);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Forward tile kernel.
 //
@@ -865,8 +897,8 @@ __global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(
   }
 
   f32x16 acc[MB][NB];
-  const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, (long)(p.M - row0) * p.H};
-  const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, (long)(p.V - col0) * p.H};
+  const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, 0};
+  const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, 0};
   mainloop<S, true, true>(acc, smem, A, B, p.H);
   // (the mainloop ends with a barrier: the LDS is free)
 
@@ -1082,7 +1114,9 @@ __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4]
 }
 
 // Backward d-logits for one vocabulary chunk: dzs = scale * dz in bf16, written to
-// a [Mpad, ldz] buffer (chunk column j = vocabulary column vbase + j).  Columns past
+// an Mpad x ldz tile-blocked buffer (chunk column j = vocabulary column vbase + j;
+// 256-row bands of 256 x 64 blocks, so that the GEMMs that read it take contiguous
+// 32 KiB blocks instead of 128-byte pieces of 256 KiB-apart rows).  Columns past
 // V and rows past M are written as zero.  With p = 2^(c1 acc - lse2) (c1 = scale log2 e)
 // and per-row a = grad_logprob, b = grad_entropy, E = lse - entropy (all 0 on ignored
 // rows):  scale dz = scale (a ([v = t] - p) + b p (E - scale acc))
@@ -1127,8 +1161,8 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
   }
 
   f32x16 acc[4][4];
-  const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, (long)(p.M - row0) * p.H};
-  const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, (long)(p.V - col0) * p.H};
+  const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, 0};
+  const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, 0};
   mainloop<BigShape, true, true>(acc, smem, A, B, p.H);
 
   float* r_lse2 = reinterpret_cast<float*>(smem + LDS_OUT);
@@ -1154,7 +1188,7 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
   else
     stage_dlogits<ENTGRAD, true>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
   __syncthreads();
-  store_tile_bf16(smem, p.dz + (long)row0 * p.ldz + ccol0, p.ldz, TILE, TILE);
+  store_tile_blocked(smem, p.dz + (long)mt * BLK_ROWS * p.ldz + (long)(ccol0 / BLK_COLS) * BLK_ELEMS);
 }
 
 // ---------------------------------------------------------------------------
@@ -1168,8 +1202,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
   const int i0 = ti * TILE, h0 = th * TILE;
   f32x16 acc[4][4];
   // dzs has Mpad rows (rows past M hold zeros); X has only M rows.
-  const TileSrc A{p.dz + i0, p.ldz, p.chunk_cols - i0, p.Mpad, (long)p.Mpad * p.ldz - i0};
-  const TileSrc B{p.X + h0, p.H, p.H - h0, p.M, (long)p.M * p.H - h0};
+  const TileSrc A{p.dz + (long)(i0 / BLK_COLS) * BLK_ELEMS, BLK_COLS, p.chunk_cols - i0, p.Mpad,
+                  (long)BLK_ROWS * p.ldz};
+  const TileSrc B{p.X + h0, p.H, p.H - h0, p.M, 0};
   mainloop<BigShape, false, false>(acc, smem, A, B, p.Mpad);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1188,11 +1223,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
   tile_coords(blockIdx.x, gridDim.x, p.n_m, p.n_h, 8, tm, th);
   const int m0 = tm * TILE, h0 = th * TILE;
   f32x16 acc[4][4];
-  // the chunk's kcols (padded) columns of dzs; W has V - vbase rows left
-  const TileSrc A{p.dz + (long)m0 * p.ldz, p.ldz, p.M - m0, p.kcols,
-                  (long)(p.M - m0) * p.ldz};
-  const TileSrc B{p.W + (long)p.vbase * p.H + h0, p.H, p.H - h0, p.V - p.vbase,
-                  (long)(p.V - p.vbase) * p.H - h0};
+  // the chunk's kcols (padded) columns of dzs (band tm of the blocked buffer); W has
+  // V - vbase rows left
+  const long band = (long)BLK_ROWS * p.ldz;
+  const TileSrc A{p.dz + (long)tm * band, BLK_COLS, p.M - m0, p.kcols, band};
+  const TileSrc B{p.W + (long)p.vbase * p.H + h0, p.H, p.H - h0, p.V - p.vbase, 0};
   mainloop<BigShape, true, false>(acc, smem, A, B, p.kcols);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
