@@ -18,6 +18,10 @@
  * logprob = 0 and entropy = 0 (lse is still written) and contribute nothing to
  * the gradients.
  *
+ * M = 0 (an empty batch) is accepted everywhere: workspace sizes are 0, the forward
+ * calls return FLCE_OK without touching any pointer, and the backward writes dW = 0
+ * (the only output with elements).  H and V must be positive.
+ *
  * Backward, for a loss L with dL/dlogprob = grad_logprob and dL/dentropy =
  * grad_entropy (Liger-Kernel PR 1294 "Triton MoE improvements and chunked GRPO
  * improvements", "Kernel design notes": logits tiles are recomputed to form

@@ -45,10 +45,13 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// M = 0 (an empty batch of tokens) is valid: the forward writes nothing and the
+// backward writes dW = 0.
 flce_status_t check_shape(int64_t M, int64_t H, int64_t V) {
-  if (M <= 0 || H <= 0 || V <= 0)
-    return fail(FLCE_ERR_INVALID_VALUE, "M, H and V must be positive (got M=%lld H=%lld V=%lld)",
-                (long long)M, (long long)H, (long long)V);
+  if (M < 0 || H <= 0 || V <= 0)
+    return fail(FLCE_ERR_INVALID_VALUE,
+                "M must be >= 0, H and V positive (got M=%lld H=%lld V=%lld)", (long long)M,
+                (long long)H, (long long)V);
   if (M > kMaxM || V > kMaxV || H > kMaxH)
     return fail(FLCE_ERR_UNSUPPORTED, "shape too large (limits M, V <= 2^30, H <= 2^20)");
   if (H % 8 != 0)
@@ -104,6 +107,7 @@ size_t bwd_bytes_for_chunk(int64_t M, int64_t H, int64_t V, int64_t chunk) {
 int64_t preferred_chunk(int64_t M, int64_t V) {
   const int64_t Mpad = cdiv(M, kTile) * kTile;
   const int64_t Vpad = cdiv(V, kTile) * kTile;
+  if (Mpad == 0) return Vpad < kMaxChunk ? Vpad : kMaxChunk;
   int64_t c = int64_t(kDzBudget / (size_t(Mpad) * 2)) / kTile * kTile;
   if (c < kTile) c = kTile;
   if (c > kMaxChunk) c = kMaxChunk;
@@ -114,6 +118,7 @@ int64_t preferred_chunk(int64_t M, int64_t V) {
 int64_t chunk_for_workspace(int64_t M, int64_t H, int64_t V, size_t bytes) {
   const int64_t Mpad = cdiv(M, kTile) * kTile;
   const int64_t Vpad = cdiv(V, kTile) * kTile;
+  if (Mpad == 0) return Vpad < kMaxChunk ? Vpad : kMaxChunk;  // nothing is staged
   if (Vpad <= kMaxChunk && bwd_bytes_for_chunk(M, H, V, Vpad) <= bytes) return Vpad;
   const size_t acc = align_up(size_t(M) * size_t(H) * sizeof(float));
   if (bytes <= acc) return 0;
@@ -126,6 +131,27 @@ int64_t chunk_for_workspace(int64_t M, int64_t H, int64_t V, size_t bytes) {
 
 flce_status_t hip_fail(hipError_t e, const char* what) {
   return fail(FLCE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// A forward over no tokens: only the scalar arguments are checked; nothing is read or
+// written, so every pointer may be NULL.
+flce_status_t check_empty(int64_t H, int64_t V, int compute_entropy) {
+  flce_status_t st = check_shape(0, H, V);
+  if (st != FLCE_OK) return st;
+  if (compute_entropy != 0 && compute_entropy != 1)
+    return fail(FLCE_ERR_INVALID_VALUE, "compute_entropy must be 0 or 1");
+  return ok();
+}
+
+// The backward over no tokens: dW = 0 (dX has no elements; nothing else is touched).
+flce_status_t zero_dw_of_empty_batch(int64_t H, int64_t V, void* dW, hipStream_t stream) {
+  flce_status_t st = check_shape(0, H, V);
+  if (st != FLCE_OK) return st;
+  if (!dW) return fail(FLCE_ERR_INVALID_VALUE, "dW is NULL");
+  if (!aligned(dW, 16)) return fail(FLCE_ERR_UNSUPPORTED, "dW must be 16-byte aligned");
+  const hipError_t e = flce::launch_fill_zero_u16(static_cast<uint16_t*>(dW), long(V * H), stream);
+  if (e != hipSuccess) return hip_fail(e, "zero-fill kernel launch");
+  return ok();
 }
 
 }  // namespace
@@ -165,7 +191,7 @@ flce_status_t flce_forward_workspace_min(int64_t M, int64_t H, int64_t V, int co
   flce_status_t st = check_shape(M, H, V);
   if (st != FLCE_OK) return st;
   if (!bytes) return fail(FLCE_ERR_INVALID_VALUE, "bytes is NULL");
-  *bytes = fwd_layout(kTile, V, compute_entropy == 1).total;
+  *bytes = M == 0 ? 0 : fwd_layout(kTile, V, compute_entropy == 1).total;
   return ok();
 }
 
@@ -176,6 +202,10 @@ flce_status_t flce_forward_wave_rows(int64_t M, int64_t H, int64_t V, int comput
   flce_status_t st = check_shape(M, H, V);
   if (st != FLCE_OK) return st;
   if (!rows) return fail(FLCE_ERR_INVALID_VALUE, "rows is NULL");
+  if (M == 0) {
+    *rows = 0;
+    return ok();
+  }
   const int64_t r = wave_rows_for_workspace(M, V, compute_entropy == 1, workspace_bytes);
   if (r == 0)
     return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the minimum %zu",
@@ -309,6 +339,7 @@ flce_status_t flce_forward_partials_shard(const void* X, const void* W_shard,
                                           int64_t ignore_index, float scale, int compute_entropy,
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream) {
+  if (M == 0) return check_empty(H, V_shard, compute_entropy);
   if (!X || !W_shard || !targets || !workspace)
     return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among X, W, targets, workspace");
   if (v_offset < 0 || v_offset > kMaxV - V_shard)
@@ -342,6 +373,8 @@ flce_status_t flce_forward_merge_shards(const int64_t* targets, int64_t M, int64
                                         int compute_entropy, float* logprob, float* lse,
                                         float* entropy, const void* gathered,
                                         size_t shard_stride_bytes, hipStream_t stream) {
+  if (M < 0) return fail(FLCE_ERR_INVALID_VALUE, "M must be >= 0 (got %lld)", (long long)M);
+  if (M == 0) return ok();
   if (!targets || !shard_offsets || !logprob || !lse || !gathered)
     return fail(FLCE_ERR_INVALID_VALUE,
                 "NULL pointer among targets, shard_offsets, logprob, lse, gathered");
@@ -386,6 +419,7 @@ flce_status_t flce_forward_merge(const int64_t* targets, int64_t M, int64_t H, i
                                  int64_t ignore_index, int compute_entropy, float* logprob,
                                  float* lse, float* entropy, const void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
+  if (M == 0) return check_empty(H, V, compute_entropy);
   if (!targets || !logprob || !lse || !workspace)
     return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among targets, logprob, lse, workspace");
   FwdLayout L;
@@ -406,6 +440,7 @@ flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets,
                            int64_t H, int64_t V, int64_t ignore_index, float scale,
                            int compute_entropy, float* logprob, float* lse, float* entropy,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (M == 0) return check_empty(H, V, compute_entropy);
   if (!X || !W || !targets || !logprob || !lse || !workspace)
     return fail(FLCE_ERR_INVALID_VALUE,
                 "NULL pointer among X, W, targets, logprob, lse, workspace");
@@ -568,6 +603,7 @@ flce_status_t flce_backward(const void* X, const void* W, const int64_t* targets
                             const float* lse, const float* entropy, const float* grad_logprob,
                             const float* grad_entropy, void* dX, void* dW, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
+  if (M == 0) return zero_dw_of_empty_batch(H, V, dW, stream);
   if (!X || !W || !targets || !lse || !dX || !dW || !workspace)
     return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among X, W, targets, lse, dX, dW, workspace");
   flce_status_t st = check_shape(M, H, V);
@@ -618,6 +654,13 @@ flce_status_t flce_backward_shard(const void* X, const void* W_shard, const int6
                                   const float* grad_logprob, const float* grad_entropy,
                                   float* dX_partial, int accumulate, void* dW_shard,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (M == 0) {
+    if (V_total > kMaxV) return fail(FLCE_ERR_UNSUPPORTED, "V_total larger than 2^30");
+    if (v_offset < 0 || V_shard > V_total - v_offset)
+      return fail(FLCE_ERR_INVALID_VALUE, "shard [%lld, %lld) does not lie in [0, V_total=%lld)",
+                  (long long)v_offset, (long long)(v_offset + V_shard), (long long)V_total);
+    return zero_dw_of_empty_batch(H, V_shard, dW_shard, stream);
+  }
   if (!X || !W_shard || !targets || !lse || !dX_partial || !dW_shard || !workspace)
     return fail(FLCE_ERR_INVALID_VALUE,
                 "NULL pointer among X, W_shard, targets, lse, dX_partial, dW_shard, workspace");
@@ -655,10 +698,10 @@ flce_status_t flce_backward_shard(const void* X, const void* W_shard, const int6
 
 flce_status_t flce_nll_reduce(const float* logprob, const int64_t* targets, int64_t M,
                               int64_t V, int64_t ignore_index, double* out, hipStream_t stream) {
-  if (!logprob || !targets || !out)
+  if (!out || (M > 0 && (!logprob || !targets)))
     return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among logprob, targets, out");
-  if (M <= 0 || V <= 0)
-    return fail(FLCE_ERR_INVALID_VALUE, "M and V must be positive (got M=%lld V=%lld)",
+  if (M < 0 || V <= 0)
+    return fail(FLCE_ERR_INVALID_VALUE, "M must be >= 0 and V positive (got M=%lld V=%lld)",
                 (long long)M, (long long)V);
   if (M > kMaxM || V > kMaxV)
     return fail(FLCE_ERR_UNSUPPORTED, "shape too large (limits M, V <= 2^30)");
@@ -673,11 +716,12 @@ flce_status_t flce_nll_reduce(const float* logprob, const int64_t* targets, int6
 flce_status_t flce_nll_mean_grad(const int64_t* targets, int64_t M, int64_t V,
                                  int64_t ignore_index, const double* reduced,
                                  float* grad_logprob, hipStream_t stream) {
+  if (M < 0 || V <= 0)
+    return fail(FLCE_ERR_INVALID_VALUE, "M must be >= 0 and V positive (got M=%lld V=%lld)",
+                (long long)M, (long long)V);
+  if (M == 0) return ok();
   if (!targets || !reduced || !grad_logprob)
     return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among targets, reduced, grad_logprob");
-  if (M <= 0 || V <= 0)
-    return fail(FLCE_ERR_INVALID_VALUE, "M and V must be positive (got M=%lld V=%lld)",
-                (long long)M, (long long)V);
   if (M > kMaxM || V > kMaxV)
     return fail(FLCE_ERR_UNSUPPORTED, "shape too large (limits M, V <= 2^30)");
   if (!aligned(targets, 8) || !aligned(reduced, 8) || !aligned(grad_logprob, 4))

@@ -90,7 +90,7 @@ def test_forward_argument_errors():
     assert _fwd(lib, t=None) == INV
     assert _fwd(lib, lse=None) == INV
     assert _fwd(lib, ws=None) == INV
-    assert _fwd(lib, M=0) == INV
+    assert _fwd(lib, M=-1) == INV
     assert _fwd(lib, V=-1) == INV
     assert _fwd(lib, ent=2) == INV
     assert _fwd(lib, entropy=None) == INV
@@ -135,7 +135,7 @@ def test_backward_argument_errors():
 
 def test_python_wrapper_raises():
     with pytest.raises(flce.FlceError) as e:
-        flce.workspace_query(0, 8, 8)
+        flce.workspace_query(-1, 8, 8)
     assert e.value.status == 1
     with pytest.raises(flce.FlceError):
         flce.backward_chunk_cols(100, 64, 1000, 10)
@@ -204,7 +204,7 @@ def test_nll_argument_errors():
     lib = flce.load()
     INV, UNS = 1, 2
     assert lib.flce_nll_reduce(None, 16, 4, 3, -100, 16, None) == INV
-    assert lib.flce_nll_reduce(16, 16, 0, 3, -100, 16, None) == INV
+    assert lib.flce_nll_reduce(16, 16, -1, 3, -100, 16, None) == INV
     assert lib.flce_nll_reduce(16, 16, 4, 0, -100, 16, None) == INV
     assert lib.flce_nll_reduce(16, 16, 1 << 31, 3, -100, 16, None) == UNS
     assert lib.flce_nll_reduce(18, 16, 4, 3, -100, 16, None) == UNS
@@ -212,3 +212,29 @@ def test_nll_argument_errors():
     assert lib.flce_nll_mean_grad(16, 4, 3, -100, None, 16, None) == INV
     assert lib.flce_nll_mean_grad(16, -1, 3, -100, 16, 16, None) == INV
     assert lib.flce_nll_mean_grad(12, 4, 3, -100, 16, 16, None) == UNS
+
+
+def test_empty_batch_needs_no_device():
+    """M = 0 is a valid, empty call: sizes are 0 and the forward and the merges return
+    FLCE_OK before any HIP call, with every pointer NULL."""
+    lib = flce.load()
+    assert flce.workspace_query(0, 64, 1000, True) == (0, 0)
+    assert flce.forward_workspace_min(0, 64, 1000) == 0
+    assert flce.forward_wave_rows(0, 64, 1000, 0) == 0
+    assert flce.backward_workspace_min(0, 64, 1000) == 0
+    assert flce.backward_chunk_cols(0, 64, 1000, 0) == 1024
+    assert _fwd(lib, X=None, W=None, t=None, M=0, lp=None, lse=None, entropy=None, ws=None,
+                wsb=0) == 0
+    assert lib.flce_forward_partials(None, None, None, 0, 64, 1000, -100, 1.0, 1, None, 0,
+                                     None) == 0
+    assert lib.flce_forward_merge(None, 0, 64, 1000, -100, 1, None, None, None, None, 0,
+                                  None) == 0
+    assert _merge(lib, [0, 5, 9], t=None, M=0, lp=None, lse=None, entropy=None, g=None) == 0
+    assert lib.flce_nll_mean_grad(None, 0, 1000, -100, None, None, None) == 0
+    # still checked: H, V and the flags
+    assert _fwd(lib, M=0, V=0) == 1
+    assert _fwd(lib, M=0, H=12) == 2
+    assert _fwd(lib, M=0, ent=3) == 1
+    # the empty backward must write dW = 0, so it needs dW (checked before any launch)
+    assert _bwd(lib, M=0, dW=None) == 1
+    assert _bwd(lib, M=0, dW=18) == 2
