@@ -54,28 +54,37 @@ def parse():
 
 
 def blas_reference(case, steps):
-    """Context, not a product path: the vendor bf16 GEMM for z = X W^T of the same shape,
-    which materialises the logits the fused kernel never writes."""
+    """Context, not a product path: the vendor bf16 GEMM (torch.matmul, hipBLASLt) on the
+    shapes and memory orders of the four GEMMs of a step: z = X W^T (forward and the
+    d-logit recompute; the library materialises the logits the fused kernels never
+    write), dX = dz W and dW = dz^T X, dz a [M, V] bf16 matrix."""
     import torch
     M, H, V = case.M, case.H, case.V
     g = torch.Generator(device="cuda").manual_seed(0)
-    a = torch.randn(M, H, device="cuda", dtype=torch.bfloat16, generator=g)
-    b = torch.randn(V, H, device="cuda", dtype=torch.bfloat16, generator=g)
-    c = torch.empty(M, V, device="cuda", dtype=torch.bfloat16)
-    for _ in range(3):
-        torch.matmul(a, b.t(), out=c)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        torch.matmul(a, b.t(), out=c)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    tf = 2.0 * M * H * V / (ms * 1e-3) / 1e12
-    print(json.dumps({"blas_reference": "torch.matmul bf16 X @ W^T", "M": M, "H": H, "V": V,
-                      "ms": round(ms, 4), "tflops": round(tf, 2),
-                      "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
+    X = torch.randn(M, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    W = torch.randn(V, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    dz = torch.randn(M, V, device="cuda", dtype=torch.bfloat16, generator=g)
+    z = torch.empty(M, V, device="cuda", dtype=torch.bfloat16)
+    dX = torch.empty(M, H, device="cuda", dtype=torch.bfloat16)
+    dW = torch.empty(V, H, device="cuda", dtype=torch.bfloat16)
+    cases = (("z = X @ W^T", lambda: torch.matmul(X, W.t(), out=z)),
+             ("dX = dz @ W", lambda: torch.matmul(dz, W, out=dX)),
+             ("dW = dz^T @ X", lambda: torch.matmul(dz.t(), X, out=dW)))
+    for name, fn in cases:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = 2.0 * M * H * V / (ms * 1e-3) / 1e12
+        print(json.dumps({"blas_reference": f"torch.matmul bf16 {name}", "M": M, "H": H,
+                          "V": V, "ms": round(ms, 4), "tflops": round(tf, 2),
+                          "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
 
 
 PROFILE = os.path.join(ROOT, "profiles", "fwd_bwd_M8192_H8192_V131072.md")
