@@ -355,8 +355,10 @@ flce_status_t flce_forward_partials_shard(const void* X, const void* W_shard,
   const flce::FwdTileArgs a = tile_args(X, W_shard, targets, M, H, V_shard, v_offset,
                                         ignore_index, scale, ent, L,
                                         static_cast<char*>(workspace));
-  const hipError_t e = flce::launch_fwd_tile(a, ent, stream);
+  hipError_t e = flce::launch_fwd_tile(a, ent, stream);
   if (e != hipSuccess) return hip_fail(e, "forward tile kernel launch");
+  e = flce::launch_target_logit(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "target logit kernel launch");
   return ok();
 }
 
@@ -470,6 +472,8 @@ flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets,
                   ignore_index, scale, ent, L, ws);
     hipError_t e = flce::launch_fwd_tile(a, ent, stream);
     if (e != hipSuccess) return hip_fail(e, "forward tile kernel launch");
+    e = flce::launch_target_logit(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "target logit kernel launch");
     const flce::FwdMergeArgs b =
         merge_args_single(targets + r0, mw, V, ignore_index, ent, logprob + r0, lse + r0,
                           ent ? entropy + r0 : nullptr, L, ws);

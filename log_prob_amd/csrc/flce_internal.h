@@ -26,7 +26,7 @@ struct FwdTileArgs {
   float* part_m;            // [n_vt, Mpad] tile row max of z
   float* part_s;            // [n_vt, Mpad] sum exp(z - m)
   float* part_u;            // [n_vt, Mpad] sum exp(z - m) (z - m)   (entropy only)
-  float* zt;                // [Mpad] target logit (written by the owning tile)
+  float* zt;                // [Mpad] target logit (target_logit_kernel, rows W holds)
 };
 
 // Vocabulary shards whose partials one merge combines (a single shard for an
@@ -99,6 +99,7 @@ struct GemmDxArgs {
 };
 
 hipError_t launch_fwd_tile(const FwdTileArgs& a, bool entropy, hipStream_t s);
+hipError_t launch_target_logit(const FwdTileArgs& a, hipStream_t s);
 hipError_t launch_fwd_merge(const FwdMergeArgs& a, bool entropy, hipStream_t s);
 hipError_t launch_dlogits(const DlogitsArgs& a, bool entropy_grad, hipStream_t s);
 hipError_t launch_gemm_dw(const GemmDwArgs& a, hipStream_t s);

@@ -807,19 +807,43 @@ __device__ __forceinline__ void store_tile_blocked(const char* tile, uint16_t* d
 // sgn * acc (sgn = -1 if NEG): the row maximum of z = scale * acc is |scale| times
 // the maximum of sgn(scale) * acc.  In a RAGGED tile columns past V are skipped
 // (bit nb of colmask: column 32 nb + lane % 32 of the wave tile exists).
+// v_max3_f32 issued directly: fmaxf on values the compiler cannot prove to be quiet
+// NaNs (here, MFMA results) costs one quieting v_max per input.  NEG applies the
+// source negation modifier to all three inputs.
+template <bool NEG>
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  if constexpr (NEG)
+    asm("v_max3_f32 %0, -%1, -%2, -%3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  else
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 template <bool NEG, bool RAGGED, class S>
 __device__ __forceinline__ void lane_row_max(const f32x16 (&acc)[S::MB][S::NB],
                                              float (&mx)[16 * S::MB], unsigned colmask) {
+  static_assert(S::NB == 4, "four columns per lane and row slot");
 #pragma unroll
   for (int mb = 0; mb < S::MB; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float m = -INFINITY;
+      float v[4];
 #pragma unroll
-      for (int nb = 0; nb < S::NB; ++nb) {
-        const float a = NEG ? -acc[mb][nb][e] : acc[mb][nb][e];
-        m = fmaxf(m, RAGGED && !((colmask >> nb) & 1u) ? -INFINITY : a);
+      for (int nb = 0; nb < 4; ++nb) v[nb] = acc[mb][nb][e];
+      if constexpr (RAGGED) {
+        // columns past V take the value that the (negated) maximum ignores
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          v[nb] = ((colmask >> nb) & 1u) ? v[nb] : (NEG ? INFINITY : -INFINITY);
       }
+      const float m3 = max3_raw<NEG>(v[0], v[1], v[2]);
+      // the running maximum is already negated: only the fourth input takes the modifier
+      float m;
+      if constexpr (NEG)
+        asm("v_max_f32 %0, %1, -%2" : "=v"(m) : "v"(m3), "v"(v[3]));
+      else
+        asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(m3), "v"(v[3]));
       mx[16 * mb + e] = m;
     }
 }
@@ -877,24 +901,12 @@ __global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(
   constexpr int P = MB / 2;  // groups of 32 row slots per lane
   constexpr int CP = S::WAVES_N;  // column parts: waves sharing the same rows
   __shared__ __attribute__((aligned(1024))) char smem[S::PIPE_BYTES];
-  static_assert((3 * CP + 1) * TM * 4 <= S::PIPE_BYTES, "epilogue buffers");
+  static_assert(3 * CP * TM * 4 <= S::PIPE_BYTES, "epilogue buffers");
   int mt, vt;
   tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, FWD_GROUP_M, mt, vt);
   const int row0 = mt * TM, col0 = vt * TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  // tile column of the target of row tid, or -1 (kept in a register over the mainloop,
-  // which needs all of the LDS)
-  int tl = -1;
-  {
-    const int r = row0 + tid;
-    if (tid < TM && r < p.M) {
-      const int64_t t = p.targets[r];
-      const int64_t tw = t - p.v_off;  // target as a row of W
-      const int64_t hi = col0 + TN < p.V ? col0 + TN : p.V;
-      if (t != p.ignore_index && tw >= col0 && tw < hi) tl = (int)(tw - col0);
-    }
-  }
 
   f32x16 acc[MB][NB];
   const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, 0};
@@ -906,11 +918,9 @@ __global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(
   const int lc = lane & 31;
   const float c1 = p.scale * LOG2E;  // logits in log2 units: z2 = c1 acc
 
-  // epilogue LDS: row maxima per column part [CP][TM], sums [CP][2][TM], target columns [TM]
+  // epilogue LDS: row maxima per column part [CP][TM], sums [CP][2][TM]
   float* red = reinterpret_cast<float*>(smem);
   float* comb = red + CP * TM;
-  int* t_col = reinterpret_cast<int*>(comb + 2 * CP * TM);
-  if (tid < TM) t_col[tid] = tl;
 
   const bool ragged = col0 + TN > p.V;
   unsigned colmask = 0;
@@ -935,29 +945,6 @@ __global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(
     }
   }
   __syncthreads();
-
-  // target logits: the lane holding (row, target column) writes z = scale * acc.
-  // Every wave scans its row slots, so that all tiles cost the same: the workgroups
-  // of an XCD then stay in step over K and share their operand tiles in L2 (a scan
-  // only where a target lies lets them drift apart and raises the L2 misses by half).
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int rb = wr0 + 32 * mb + 8 * q + 4 * (lane >> 5);
-      const int4 tc = *reinterpret_cast<const int4*>(t_col + rb);
-      const int tcs[4] = {tc.x, tc.y, tc.z, tc.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int dd = tcs[j] - wc0 - lc;  // 32 nb if this lane holds the target column
-        if ((unsigned)dd < (unsigned)WN && (dd & 31) == 0) {
-          float z = acc[mb][0][4 * q + j];
-#pragma unroll
-          for (int nb = 1; nb < NB; ++nb) z = (dd >> 5) == nb ? acc[mb][nb][4 * q + j] : z;
-          p.zt[row0 + rb + j] = z * p.scale;
-        }
-      }
-    }
 
   // shifted sums against the full-row maximum, 32 row slots (two blocks) at a time
 #pragma unroll
@@ -988,6 +975,39 @@ __global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(
     p.part_s[off] = sm;
     if constexpr (ENT) p.part_u[off] = um * LN2;
   }
+}
+
+// Target logit of every row whose target W holds: z[m, t[m]] = scale * X[m] . W[t[m] -
+// v_off], bf16 products accumulated in fp32 in a fixed order (each lane over a strided
+// set of 8-element groups, then a fixed butterfly over the wave).  A separate pass
+// rather than a pick in the tile epilogue: the pick would have to run in every wave
+// of every tile (a tile that picks only where a target lies costs more than the others
+// and breaks the lockstep of an XCD's tiles), which took a quarter of the epilogue.
+// One wave per row.
+constexpr int TL_ROWS = 4;
+__global__ __launch_bounds__(64 * TL_ROWS) void target_logit_kernel(FwdTileArgs p) {
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * TL_ROWS + (threadIdx.x >> 6);
+  if (row >= p.M) return;
+  const int64_t t = p.targets[row];
+  const int64_t tw = t - p.v_off;
+  if (t == p.ignore_index || tw < 0 || tw >= p.V) return;
+  const uint16_t* x = p.X + row * p.H;
+  const uint16_t* w = p.W + tw * p.H;
+  float s = 0.f;
+#pragma unroll 4
+  for (int k = 8 * lane; k < p.H; k += 8 * 64) {
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(x + k);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(w + k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s = fmaf(__uint_as_float(xv[i] << 16), __uint_as_float(wv[i] << 16), s);
+      s = fmaf(__uint_as_float(xv[i] & 0xffff0000u), __uint_as_float(wv[i] & 0xffff0000u), s);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) p.zt[row] = s * p.scale;
 }
 
 // Merge of the per-tile partials of each row: m* = max m_j, S = sum s_j e^(m_j - m*),
@@ -1328,6 +1348,12 @@ hipError_t launch_fwd_tile(const FwdTileArgs& a, bool ent, hipStream_t s) {
     fwd_tile_kernel<FwdShape, true><<<g, FwdShape::NTHREADS, 0, s>>>(a);
   else
     fwd_tile_kernel<FwdShape, false><<<g, FwdShape::NTHREADS, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_target_logit(const FwdTileArgs& a, hipStream_t s) {
+  const unsigned g = (unsigned)(((long)a.M + TL_ROWS - 1) / TL_ROWS);
+  target_logit_kernel<<<g, 64 * TL_ROWS, 0, s>>>(a);
   return hipGetLastError();
 }
 
