@@ -345,22 +345,29 @@ __device__ __forceinline__ void tile_load(const TileDma& d, const DmaPlan<KC, RO
 }
 
 // The loads of one whole stage: stage load j < DMA_A is load j of the A tile, the
-// rest are the B tile's.
-template <class S, bool A_KC, bool B_KC, bool FAST = false>
+// rest are the B tile's (B_FIRST: the other way round).  The first half of a stage's
+// loads goes out early (right after a barrier), so the order decides which operand
+// waits longer: issuing the L2-resident operand first measured faster (forward with W
+// first: +3%; dW with X^T first: -0.4%; dX with W first: +0.3%).
+template <class S, bool A_KC, bool B_KC, bool FAST = false, bool B_FIRST = false>
 struct StageDma {
   using PA = DmaPlan<A_KC, S::TM, S::BK, S::NWAVES>;
   using PB = DmaPlan<B_KC, S::TN, S::BK, S::NWAVES>;
   TileDma a, b;
   const PA* pa;
   const PB* pb;
-  // issue stage loads [j0, j1) back to back
+  // issue stage loads [j0, j1) back to back (B_FIRST: the B tile's loads come first)
   __device__ __forceinline__ void issue(int j0, int j1) const {
+    constexpr int DF = B_FIRST ? S::DMA_B : S::DMA_A;  // loads of the first tile
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
-      if (j < S::DMA_A)
-        tile_load<FAST>(a, *pa, j, j == j0);
-      else
-        tile_load<FAST>(b, *pb, j - S::DMA_A, j == j0 || j == S::DMA_A);
+      if (j < DF) {
+        if constexpr (B_FIRST) tile_load<FAST>(b, *pb, j, j == j0);
+        else tile_load<FAST>(a, *pa, j, j == j0);
+      } else {
+        if constexpr (B_FIRST) tile_load<FAST>(a, *pa, j - DF, j == j0 || j == DF);
+        else tile_load<FAST>(b, *pb, j - DF, j == j0 || j == DF);
+      }
     }
   }
 };
@@ -568,7 +575,7 @@ __device__ __forceinline__ void sched_substep() {
 // zero-fill their stage, so every step issues the same number of loads and the wait
 // before each barrier is a fixed count.  Steps run in pairs (stage 0, stage 1); an
 // odd step count gets one step over a zero-filled stage.
-template <class S, bool A_KC, bool B_KC>
+template <class S, bool A_KC, bool B_KC, bool B_FIRST = false>
 __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem,
                                          const TileSrc& A, const TileSrc& B, int K) {
   static_assert(S::NST == 2, "two LDS stages");
@@ -601,7 +608,7 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
   // loads of step st into stage s; a step past K only zero-fills it
   auto stage_dma = [&](auto fast, int st, int s) {
     constexpr bool FAST = decltype(fast)::value;
-    StageDma<S, A_KC, B_KC, FAST> d;
+    StageDma<S, A_KC, B_KC, FAST, B_FIRST> d;
     d.pa = &plan_a;
     d.pb = &plan_b;
     const bool active = st < nk;
@@ -1225,7 +1232,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
   const TileSrc A{p.dz + (long)(i0 / BLK_COLS) * BLK_ELEMS, BLK_COLS, p.chunk_cols - i0, p.Mpad,
                   (long)BLK_ROWS * p.ldz};
   const TileSrc B{p.X + h0, p.H, p.H - h0, p.M, 0};
-  mainloop<BigShape, false, false>(acc, smem, A, B, p.Mpad);
+  // the X^T loads (L2-resident) go out before the streamed d-logit loads of each step
+  mainloop<BigShape, false, false, true>(acc, smem, A, B, p.Mpad);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
