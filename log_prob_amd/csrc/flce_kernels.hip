@@ -5,14 +5,17 @@
 //   fwd_tile     one workgroup per (256-row M tile, 256-column V tile): bf16 MFMA
 //                mainloop over H, then an epilogue that reduces the logit tile to
 //                per-row partial statistics (max m, sum of exp(z - m), and
-//                sum of exp(z - m) (z - m) for entropy) and picks the target logit.
+//                sum of exp(z - m) (z - m) for entropy).
+//   target_logit z[m, t[m]] as one dot product per row.
 //   fwd_merge    combines the per-tile partials of each row (max first, then the
 //                rescaled sums) into lse, logprob and entropy.
+// Scalar reductions: nll_reduce (sum, count and mean of -logprob over valid rows) and
+// nll_mean_grad (the mean NLL's gradient with respect to logprob).
 // Backward (Liger-Kernel PR 1294, "Kernel design notes": recompute the logits
 // tiles, emit d-logits in the input dtype into a reusable buffer, then two grad
 // GEMMs; SkyRL PR 2141, "Overview": split backward over the vocabulary):
 //   bwd_dlogits  the same mainloop, epilogue forms scale * dz in bf16 for one
-//                vocabulary chunk.
+//                vocabulary chunk, stored tile-blocked (256 x 64 blocks).
 //   gemm_dw      dW[chunk] = dz_chunk^T X          (K = tokens)
 //   gemm_dx      dX (+)= dz_chunk W[chunk]          (K = chunk columns)
 //
@@ -25,7 +28,8 @@
 // dimension is contiguous is kept as 512-byte K rows and read with the gfx950
 // transposing read ds_read_b64_tr_b16, which hands each lane 4 consecutive K values
 // of one column.  Both layouts XOR-swizzle 16- or 32-byte blocks by row so the
-// fragment reads are free of bank conflicts.
+// fragment reads are free of bank conflicts.  Kernels and the host code take a
+// vocabulary offset, so the same kernels serve one shard of a split vocabulary.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
