@@ -92,11 +92,17 @@ KERNEL_SOURCES = ("log_prob_amd/csrc/flce_kernels.hip", "log_prob_amd/csrc/flce_
 
 
 def kernel_source_hash():
+    """SHA-256 of the kernel sources with comments and blank space removed, so that a
+    change to a comment does not disown the committed counter figures."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
