@@ -1247,6 +1247,68 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
   store_tile_bf16(smem, p.dW + (long)(p.vbase + i0) * p.H + h0, p.H, rows, p.H - h0);
 }
 
+// The fp32 side of a dX tile (modes 1-3).  Each wave moves its 128 x 128 block through
+// a private 32 KiB LDS slice, 64 rows at a time, so the fp32 accumulator is read and
+// written in 16-byte pieces (a half-wave covers 512 contiguous bytes of a row) and all
+// of a lane's loads of a slice are in flight together; per-element accesses in the
+// accumulator layout would wait on one read-modify-write after another.  Slice layout:
+// row r (0..63) at 512 r bytes, column c at float (c ^ 32 ((r >> 2) & 1)), so the two
+// half-waves of a staging write (rows r and r + 4) fall on different banks.
+// mode 1: acc = v; mode 2: acc += v; mode 3: dX = bf16(acc + v).
+__device__ __forceinline__ void dx_tile_f32(const f32x16 (&acc)[4][4], char* smem,
+                                            const GemmDxArgs& p, int m0, int h0, int wave,
+                                            int lane) {
+  const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
+  float* sl = reinterpret_cast<float*>(smem + wave * 32768);
+  const int lc = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = 32 * mi + acc_row(lane, e);  // (r >> 2) & 1 == hi
+          sl[r * 128 + ((32 * nb + lc) ^ (hi << 5))] = acc[2 * s + mi][nb][e];
+        }
+    __syncthreads();
+    const int rb = m0 + wr0 + 64 * s, cb = h0 + wc0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // granule g = 64 it + lane: row g / 32, columns 4 (g % 32) .. + 3
+      float4 old[16];
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int g = 64 * (16 * half + it) + lane, r = g >> 5, c = 4 * (g & 31);
+        const int m = rb + r, h = cb + c;
+        old[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.mode != 1 && m < p.M && h < p.H)
+          old[it] = *reinterpret_cast<const float4*>(p.acc + (long)m * p.H + h);
+      }
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int g = 64 * (16 * half + it) + lane, r = g >> 5, c = 4 * (g & 31);
+        const int m = rb + r, h = cb + c;
+        const float4 v = *reinterpret_cast<const float4*>(sl + r * 128 + (c ^ (((r >> 2) & 1) << 5)));
+        const float4 t = make_float4(old[it].x + v.x, old[it].y + v.y, old[it].z + v.z,
+                                     old[it].w + v.w);
+        if (m < p.M && h < p.H) {
+          if (p.mode == 3) {
+            const f32x2 lo = {t.x, t.y}, hi2 = {t.z, t.w};
+            const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+            const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2));
+            *reinterpret_cast<uint2*>(p.dX + (long)m * p.H + h) = make_uint2(a, b);
+          } else {
+            *reinterpret_cast<float4*>(p.acc + (long)m * p.H + h) = t;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // dX[m, h] (+)= sum_i dzs[m, i] W[vbase + i, h]: A = dzs (KC), B = W^T (MN), K = kcols.
 // mode 0: write bf16; 1: write fp32 accumulator; 2: accumulate fp32; 3: accumulate and write bf16.
 __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
@@ -1264,33 +1326,12 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
-  const int lc = lane & 31;
   if (p.mode == 0) {
     stage_wave_bf16(smem, wr0, wc0, lane, [&](int mb, int nb, int e) { return acc[mb][nb][e]; });
     __syncthreads();
     store_tile_bf16(smem, p.dX + (long)m0 * p.H + h0, p.H, p.M - m0, p.H - h0);
-  } else if (p.mode == 3) {
-    stage_wave_bf16(smem, wr0, wc0, lane, [&](int mb, int nb, int e) {
-      const int m = m0 + wr0 + 32 * mb + acc_row(lane, e), h = h0 + wc0 + 32 * nb + lc;
-      return acc[mb][nb][e] + (m < p.M && h < p.H ? p.acc[(long)m * p.H + h] : 0.f);
-    });
-    __syncthreads();
-    store_tile_bf16(smem, p.dX + (long)m0 * p.H + h0, p.H, p.M - m0, p.H - h0);
   } else {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wr0 + 32 * mb + acc_row(lane, e);
-        if (m >= p.M) continue;
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int h = h0 + wc0 + 32 * nb + lc;
-          if (h >= p.H) continue;
-          const long o = (long)m * p.H + h;
-          p.acc[o] = p.mode == 2 ? p.acc[o] + acc[mb][nb][e] : acc[mb][nb][e];
-        }
-      }
+    dx_tile_f32(acc, smem, p, m0, h0, wave, lane);
   }
 }
 
