@@ -1098,49 +1098,70 @@ __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4]
                                               const float* r_cb, const float* r_sa,
                                               const int* t_local, int wr0, int wc0, int lane,
                                               float c1, unsigned colmask) {
-  const int lc = lane & 31;
+  const int lc = lane & 31, hi = lane >> 5, odd = lane & 1;
+  // The lane writes rows r = rb + jp + odd (rb a multiple of 4 with bit 2 = hi, jp in
+  // {0, 2}), so out_swz(r) = 4 (odd | 2 hi) for all of them: one address per column
+  // block nb, and the row offsets 512 (32 mb + 8 q + jp) are immediates.
+  const int sw = odd | (hi << 1);
+  LDS_AS char* const t3 = (LDS_AS char*)tile;
+  const uint32_t base = (uint32_t)((wr0 + 4 * hi + odd) * 512 + (wc0 >> 3) * 16 + (lc & 6) * 2);
+  uint32_t addr[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) addr[nb] = base + (uint32_t)((((nb ^ sw) << 2) + (lc >> 3)) << 4);
+  // byte selectors of the pair exchange (v_perm_b32: bytes 0-3 from the second
+  // operand, this lane's pair; 4-7 from the first, the partner's): the even lane keeps
+  // both low halves (row r), the odd lane both high halves (row r + 1)
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       // rows rb .. rb + 3 are the lane's slots e = 4 q .. 4 q + 3 of block mb
-      const int rb = wr0 + 32 * mb + 8 * q + 4 * (lane >> 5);
+      const int rb = wr0 + 32 * mb + 8 * q + 4 * hi;
       const float4 L4 = *reinterpret_cast<const float4*>(r_lse2 + rb);
       const float4 C4 = *reinterpret_cast<const float4*>(r_c0 + rb);
-      const float4 S4 = *reinterpret_cast<const float4*>(r_sa + rb);
-      const int4 T4 = *reinterpret_cast<const int4*>(t_local + rb);
       const float L[4] = {L4.x, L4.y, L4.z, L4.w}, C0[4] = {C4.x, C4.y, C4.z, C4.w};
-      const float SA[4] = {S4.x, S4.y, S4.z, S4.w};
-      const int DD[4] = {T4.x - wc0 - lc, T4.y - wc0 - lc, T4.z - wc0 - lc, T4.w - wc0 - lc};
       float CB[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (ENTGRAD) {
         const float4 B4 = *reinterpret_cast<const float4*>(r_cb + rb);
         CB[0] = B4.x; CB[1] = B4.y; CB[2] = B4.z; CB[3] = B4.w;
       }
+      float d[4][4];
 #pragma unroll
-      for (int jp = 0; jp < 4; jp += 2) {
-        float v[2][4];
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int j = jp + h;
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            const float av = acc[mb][nb][4 * q + j];
-            const float pr = __builtin_amdgcn_exp2f(fmaf(av, c1, -L[j]));
-            float d = pr * (ENTGRAD ? fmaf(CB[j], av, C0[j]) : C0[j]);
-            if constexpr (RAGGED) d = ((colmask >> nb) & 1u) ? d : 0.f;
-            v[h][nb] = d;
-          }
-          // DD = 32 nb: this lane holds the target column of the row (in block nb)
-          if ((unsigned)DD[j] < 128u && (DD[j] & 31) == 0) {
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) v[h][nb] += (DD[j] >> 5) == nb ? SA[j] : 0.f;
-          }
+        for (int nb = 0; nb < 4; ++nb) {
+          float av;
+          asm("v_accvgpr_read_b32 %0, %1" : "=v"(av) : "a"(acc[mb][nb][4 * q + j]));
+          const float pr = __builtin_amdgcn_exp2f(fmaf(av, c1, -L[j]));
+          float v = pr * (ENTGRAD ? fmaf(CB[j], av, C0[j]) : C0[j]);
+          if constexpr (RAGGED) v = ((colmask >> nb) & 1u) ? v : 0.f;
+          d[j][nb] = v;
         }
+      // the target column of row rb + j lies in this lane's column nb iff
+      // t_local - wc0 - lc = 32 nb: rare, so one branch per four rows
+      const int4 T4 = *reinterpret_cast<const int4*>(t_local + rb);
+      const int DD[4] = {T4.x - wc0 - lc, T4.y - wc0 - lc, T4.z - wc0 - lc, T4.w - wc0 - lc};
+      if (((DD[0] & ~0x60) == 0) | ((DD[1] & ~0x60) == 0) | ((DD[2] & ~0x60) == 0) |
+          ((DD[3] & ~0x60) == 0)) {
+        const float4 S4 = *reinterpret_cast<const float4*>(r_sa + rb);
+        const float SA[4] = {S4.x, S4.y, S4.z, S4.w};
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          stage_pair_bf16(tile, lane, rb + jp, wc0 + 32 * nb + lc, v[0][nb], v[1][nb]);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) d[j][nb] += DD[j] == 32 * nb ? SA[j] : 0.f;
       }
+#pragma unroll
+      for (int jp = 0; jp < 4; jp += 2)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const f32x2 pr = {d[jp][nb], d[jp + 1][nb]};
+          const uint32_t own = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+          const uint32_t partner =
+              (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0xB1, 0xf, 0xf, true);
+          const uint32_t w = __builtin_amdgcn_perm(partner, own, sel);
+          *(LDS_AS uint32_t*)(t3 + addr[nb] + (32 * mb + 8 * q + jp) * 512) = w;
+        }
     }
 }
 
