@@ -796,21 +796,6 @@ __device__ __forceinline__ void store_tile_bf16(const char* tile, uint16_t* dst,
   }
 }
 
-// Copy a staged 256 x 256 bf16 tile into its four 256 x 64 blocks of a tile-blocked
-// buffer (block q, columns 64 q .. 64 q + 63, at dst + q BLK_ELEMS; row r at 64 r).
-// Consecutive threads write consecutive 16 bytes, so each wave stores 1 KiB at once.
-__device__ __forceinline__ void store_tile_blocked(const char* tile, uint16_t* dst) {
-  const int t = threadIdx.x;
-#pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
-    const int G = it * NTHREADS + t;  // 16-byte granule in destination order
-    const int q = G >> 11, r = (G >> 3) & 255, c8 = G & 7;
-    const char* src = tile + (r << 9) + ((((q << 3) | c8) ^ out_swz(r)) << 4);
-    *reinterpret_cast<u32x4*>(dst + (long)q * BLK_ELEMS + r * BLK_COLS + 8 * c8) =
-        *reinterpret_cast<const u32x4*>(src);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Forward tile kernel.
 //
@@ -1087,17 +1072,19 @@ __global__ __launch_bounds__(MERGE_ROWS * MERGE_SLICES) void fwd_merge_kernel(Fw
 }
 
 // ---------------------------------------------------------------------------
-// Stage a wave's d-logits, d = 2^(c1 acc - lse2) (c0 + cb acc) + [column = target] sa
-// (per-row parameters in LDS, see bwd_dlogits_kernel).  RAGGED: columns past V
-// (colmask bit nb clear) become 0.  Every wave runs the same instruction stream
-// whether or not it holds a target (the correction is a per-row-slot branch that
-// almost never has active lanes), which keeps the tiles of an XCD in step.
+// A wave's d-logits, d = 2^(c1 acc - lse2) (c0 + cb acc) + [column = target] sa
+// (per-row parameters in LDS, see bwd_dlogits_kernel), rounded to bf16, staged in the
+// wave's own part of the LDS tile and stored to the tile-blocked buffer at dst (the
+// tile's 256 x 64 block 0) 32 rows at a time.  RAGGED: columns past V (colmask bit nb
+// clear) become 0.  Every wave runs the same instruction stream whether or not it
+// holds a target (the correction is a branch per four rows that almost never has
+// active lanes), which keeps the tiles of an XCD in step.
 template <bool ENTGRAD, bool RAGGED>
 __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4][4],
                                               const float* r_lse2, const float* r_c0,
                                               const float* r_cb, const float* r_sa,
                                               const int* t_local, int wr0, int wc0, int lane,
-                                              float c1, unsigned colmask) {
+                                              float c1, unsigned colmask, uint16_t* dst) {
   const int lc = lane & 31, hi = lane >> 5, odd = lane & 1;
   // The lane writes rows r = rb + jp + odd (rb a multiple of 4 with bit 2 = hi, jp in
   // {0, 2}), so out_swz(r) = 4 (odd | 2 hi) for all of them: one address per column
@@ -1113,7 +1100,7 @@ __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4]
   // both low halves (row r), the odd lane both high halves (row r + 1)
   const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       // rows rb .. rb + 3 are the lane's slots e = 4 q .. 4 q + 3 of block mb
@@ -1163,6 +1150,18 @@ __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4]
           *(LDS_AS uint32_t*)(t3 + addr[nb] + (32 * mb + 8 * q + jp) * 512) = w;
         }
     }
+    // The wave's 32 rows of block mb are staged (only this wave touches them): store
+    // them as the rows of two 64-column blocks of the tile-blocked buffer, 1 KiB of
+    // consecutive rows per instruction, while the next block is computed.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int qb = it >> 2, r = wr0 + 32 * mb + 8 * (it & 3) + (lane >> 3), c8 = lane & 7;
+      const int c = (wc0 >> 3) + 8 * qb + c8;
+      const u32x4 v = *(LDS_AS const u32x4*)(t3 + r * 512 + ((c ^ out_swz(r)) << 4));
+      *reinterpret_cast<u32x4*>(dst + (long)((wc0 >> 6) + qb) * BLK_ELEMS + r * BLK_COLS + 8 * c8) = v;
+    }
+  }
 }
 
 // Backward d-logits for one vocabulary chunk: dzs = scale * dz in bf16, written to
@@ -1235,12 +1234,13 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
   unsigned colmask = 0;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) colmask |= (col0 + wc0 + 32 * nb + (lane & 31) < p.V ? 1u : 0u) << nb;
+  uint16_t* const dst = p.dz + (long)mt * BLK_ROWS * p.ldz + (long)(ccol0 / BLK_COLS) * BLK_ELEMS;
   if (!ragged)
-    stage_dlogits<ENTGRAD, false>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
+    stage_dlogits<ENTGRAD, false>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1,
+                                  colmask, dst);
   else
-    stage_dlogits<ENTGRAD, true>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1, colmask);
-  __syncthreads();
-  store_tile_blocked(smem, p.dz + (long)mt * BLK_ROWS * p.ldz + (long)(ccol0 / BLK_COLS) * BLK_ELEMS);
+    stage_dlogits<ENTGRAD, true>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1,
+                                 colmask, dst);
 }
 
 // ---------------------------------------------------------------------------
