@@ -797,6 +797,24 @@ __device__ __forceinline__ void store_tile_bf16(const char* tile, uint16_t* dst,
 }
 
 // ---------------------------------------------------------------------------
+// An accumulator value read from its accumulation register where it is used (for
+// values used once: left to itself, the register allocator moves the tile between
+// register files and reads some values several times).
+__device__ __forceinline__ float acc_read(float a) {
+  float r;
+  asm("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(a));
+  return r;
+}
+
+// v_max_f32 without the quieting of its inputs that fmaxf adds (the inputs are MFMA
+// results or maxima of them, never signaling NaNs).
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// ---------------------------------------------------------------------------
 // Forward tile kernel.
 //
 // Per-lane extreme of each row slot q = 16 mb + e over the lane's NB columns, on
@@ -933,7 +951,7 @@ __global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(
       if (c1 >= 0.f) lane_row_max<false, true, S>(acc, mx, colmask);
       else lane_row_max<true, true, S>(acc, mx, colmask);
     }
-    reduce_scatter32<P>(mx, lane, [](float a, float b) { return fmaxf(a, b); });
+    reduce_scatter32<P>(mx, lane, [](float a, float b) { return max_raw(a, b); });
 #pragma unroll
     for (int pp = 0; pp < P; ++pp) {
       const int mb = 2 * pp + (lc >> 4), e = lc & 15;
@@ -1118,8 +1136,7 @@ __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4]
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          float av;
-          asm("v_accvgpr_read_b32 %0, %1" : "=v"(av) : "a"(acc[mb][nb][4 * q + j]));
+          const float av = acc_read(acc[mb][nb][4 * q + j]);
           const float pr = __builtin_amdgcn_exp2f(fmaf(av, c1, -L[j]));
           float v = pr * (ENTGRAD ? fmaf(CB[j], av, C0[j]) : C0[j]);
           if constexpr (RAGGED) v = ((colmask >> nb) & 1u) ? v : 0.f;
@@ -1192,22 +1209,26 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
   {
     const int r = row0 + tid;
     if (r < p.M) {
+      // all of the row's loads go out together (validity selects afterwards, so no
+      // load waits for the target's): one round trip, under the mainloop's first loads
       const int64_t t = p.targets[r];
+      const float lse = p.lse[r];
+      const float a = p.grad_logprob ? p.grad_logprob[r] : 0.f;
+      float b = 0.f, ent = 0.f;
+      if constexpr (ENTGRAD) {
+        b = p.grad_entropy[r];
+        ent = p.entropy[r];
+      }
       const bool valid = t != p.ignore_index && t >= 0 && t < p.V_total;
       const int64_t tw = t - p.v_off;  // target as a row of W (owned iff 0 <= tw < V)
-      const float lse = p.lse[r];
       lse2 = lse * LOG2E;
-      if (valid) {
-        const float a = p.grad_logprob ? p.grad_logprob[r] : 0.f;
-        sa = p.scale * a;
-        c0 = -sa;
-        if constexpr (ENTGRAD) {
-          const float b = p.grad_entropy[r];
-          c0 = p.scale * (b * (lse - p.entropy[r]) - a);
-          cb = -p.scale * p.scale * b;
-        }
-        if (tw >= col0 && tw < col0 + TILE && tw < p.V) tl = (int)(tw - col0);
-      }
+      const float sa_r = p.scale * a;
+      const float c0_r = ENTGRAD ? p.scale * (b * (lse - ent) - a) : -sa_r;
+      const float cb_r = ENTGRAD ? -p.scale * p.scale * b : 0.f;
+      sa = valid ? sa_r : 0.f;
+      c0 = valid ? c0_r : 0.f;
+      cb = valid ? cb_r : 0.f;
+      tl = (valid && tw >= col0 && tw < col0 + TILE && tw < p.V) ? (int)(tw - col0) : -1;
     }
   }
 
