@@ -738,65 +738,6 @@ __device__ __forceinline__ void reduce_scatter32(float (&v)[32 * P], int lane, O
 }
 
 // ---------------------------------------------------------------------------
-// bf16 output tiles of the backward kernels are staged in LDS before 16-byte
-// coalesced stores.  Staging layout of a 256 x 256 tile: row r at byte 512 r, its
-// 16-byte chunk c (columns 8 c .. 8 c + 7) at chunk position c ^ out_swz(r).  The
-// swizzle sends the four rows one pair write touches (r0, r0 + 1, r0 + 4, r0 + 5,
-// r0 even within its group of 8) to four different 64-byte bank groups.
-__device__ __forceinline__ int out_swz(int r) { return ((r & 1) | ((r >> 1) & 2)) << 2; }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Stage two elements per lane as one packed bf16 pair.  In the MFMA layout, lanes 2i
-// and 2i + 1 hold adjacent columns (cl even, cl + 1) of the same rows; v0 is this
-// lane's element in row r0, v1 the one in row r0 + 1.  One DPP swap within each lane
-// pair lets the even lane write (r0, cl .. cl + 1) and the odd lane (r0 + 1, cl - 1 .. cl);
-// the conversion rounds to nearest even.
-__device__ __forceinline__ void stage_pair_bf16(char* tile, int lane, int r0, int cl, float v0,
-                                                float v1) {
-  const bool odd = (lane & 1) != 0;
-  const float recv = dpp_mov<0xB1>(odd ? v0 : v1);  // quad_perm [1, 0, 3, 2]
-  const f32x2 pr = {odd ? recv : v0, odd ? v1 : recv};
-  const int r = odd ? r0 + 1 : r0, c = cl & ~1;
-  *reinterpret_cast<uint32_t*>(tile + (r << 9) + ((((c >> 3) ^ out_swz(r))) << 4) + ((c & 7) << 1)) =
-      __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
-}
-
-// Stage a wave's 128 x 128 block of values f(mb, nb, e) (the accumulator layout:
-// element e of block (mb, nb) is row wr0 + 32 mb + acc_row(lane, e), column
-// wc0 + 32 nb + lane % 32) into a staged tile.
-template <class F>
-__device__ __forceinline__ void stage_wave_bf16(char* tile, int wr0, int wc0, int lane, F f) {
-  const int lc = lane & 31;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const int r0 = wr0 + 32 * mb + ((e >> 2) << 3) + ((lane >> 5) << 2) + (e & 3);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        stage_pair_bf16(tile, lane, r0, wc0 + 32 * nb + lc, f(mb, nb, e), f(mb, nb, e + 1));
-    }
-}
-
-// Copy a staged 256 x 256 bf16 tile to rows [0, nrows) and columns [0, ncols) of a
-// row-major matrix at dst with leading dimension ld; ncols is a multiple of 8.
-// 16-byte stores, 32 lanes per row.
-__device__ __forceinline__ void store_tile_bf16(const char* tile, uint16_t* dst, long ld, int nrows,
-                                                int ncols) {
-  const int t = threadIdx.x;
-#pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
-    const int G = it * NTHREADS + t;
-    const int r = G >> 5, c = G & 31;
-    const char* src = tile + (r << 9) + ((c ^ out_swz(r)) << 4);
-    if (r < nrows && 8 * c < ncols)
-      *reinterpret_cast<u32x4*>(dst + (long)r * ld + 8 * c) = *reinterpret_cast<const u32x4*>(src);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // An accumulator value read from its accumulation register where it is used (for
 // values used once: left to itself, the register allocator moves the tile between
 // register files and reads some values several times).
@@ -812,6 +753,115 @@ __device__ __forceinline__ float max_raw(float a, float b) {
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 output tiles of the backward kernels are staged in LDS before 16-byte
+// coalesced stores.  Staging layout of a 256 x 256 tile: row r at byte 512 r, its
+// 16-byte chunk c (columns 8 c .. 8 c + 7) at chunk position c ^ out_swz(r).  The
+// swizzle sends the four rows one pair write touches (r0, r0 + 1, r0 + 4, r0 + 5,
+// r0 even within its group of 8) to four different 64-byte bank groups.  Each wave
+// stages its own 128 x 128 block and stores it 32 rows (one block row mb) at a time,
+// right after staging them: no other wave touches those bytes, so no workgroup
+// barrier, and the stores overlap the staging of the next block row.
+__device__ __forceinline__ int out_swz(int r) { return ((r & 1) | ((r >> 1) & 2)) << 2; }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Staging of values in the accumulator layout (element e of block (mb, nb) is row
+// wr0 + 32 mb + acc_row(lane, e), column wc0 + 32 nb + lane % 32) as bf16 pairs.
+// Lanes 2i and 2i + 1 hold adjacent columns of the same rows; a lane's rows r, r + 1
+// (slots e = 4 q + jp, jp + 1 with jp in {0, 2}) are packed as one bf16x2 (row r
+// low), exchanged with the partner lane by a DPP swap, and one byte permute keeps the
+// even lane's row r (columns c, c + 1) and the odd lane's row r + 1 (c - 1, c); the
+// conversion rounds to nearest even.  The rows a lane writes are r = wr0 + 32 mb +
+// 8 q + 4 (lane / 32) + jp + (lane & 1), so out_swz(r) = 4 ((lane & 1) | 2 (lane /
+// 32)) for all of them: one address per column block nb, and the row offsets
+// 512 (32 mb + 8 q + jp) are immediates.
+struct WaveStager {
+  LDS_AS char* t3;
+  uint32_t addr[4];
+  uint32_t sel;  // v_perm_b32 byte selector: bytes 0-3 this lane's pair, 4-7 the partner's
+  int wr0, wc0, lane;
+
+  __device__ __forceinline__ void init(char* tile, int wr0_, int wc0_, int lane_) {
+    wr0 = wr0_;
+    wc0 = wc0_;
+    lane = lane_;
+    const int lc = lane & 31, hi = lane >> 5, odd = lane & 1;
+    const int sw = odd | (hi << 1);
+    t3 = (LDS_AS char*)tile;
+    const uint32_t base =
+        (uint32_t)((wr0 + 4 * hi + odd) * 512 + (wc0 >> 3) * 16 + (lc & 6) * 2);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) addr[nb] = base + (uint32_t)((((nb ^ sw) << 2) + (lc >> 3)) << 4);
+    sel = odd ? 0x03020706u : 0x05040100u;
+  }
+
+  // v0, v1: this lane's values in slots e = 4 q + jp and 4 q + jp + 1 of block (mb, nb)
+  __device__ __forceinline__ void put(int mb, int q, int jp, int nb, float v0, float v1) const {
+    const f32x2 pr = {v0, v1};
+    const uint32_t own = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+    const uint32_t partner = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0xB1, 0xf, 0xf, true);
+    *(LDS_AS uint32_t*)(t3 + addr[nb] + (32 * mb + 8 * q + jp) * 512) =
+        __builtin_amdgcn_perm(partner, own, sel);
+  }
+
+  // The 16 bytes of tile row r, chunk c (columns 8 c .. 8 c + 7).
+  __device__ __forceinline__ u32x4 get(int r, int c) const {
+    return *(LDS_AS const u32x4*)(t3 + r * 512 + ((c ^ out_swz(r)) << 4));
+  }
+
+  // Wait until this wave's staging writes are in LDS (its own reads follow).
+  __device__ __forceinline__ void fence() const { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+  // Store the wave's staged rows of block row mb to a tile-blocked buffer (dst = the
+  // tile's 256 x 64 block 0, block q at dst + q BLK_ELEMS, row r at 64 r): two pieces
+  // of 32 consecutive rows, 1 KiB per instruction.
+  __device__ __forceinline__ void store_blocked(int mb, uint16_t* dst) const {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int qb = it >> 2, r = wr0 + 32 * mb + 8 * (it & 3) + (lane >> 3), c8 = lane & 7;
+      const u32x4 v = get(r, (wc0 >> 3) + 8 * qb + c8);
+      *reinterpret_cast<u32x4*>(dst + (long)((wc0 >> 6) + qb) * BLK_ELEMS + r * BLK_COLS + 8 * c8) = v;
+    }
+  }
+
+  // Store the wave's staged rows of block row mb to rows [0, nrows) and columns
+  // [0, ncols) of a row-major matrix (dst = the tile's element (0, 0), leading
+  // dimension ld; ncols a multiple of 8): 4 rows of 256 bytes per instruction.
+  __device__ __forceinline__ void store_rows(int mb, uint16_t* dst, long ld, int nrows,
+                                             int ncols) const {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = wr0 + 32 * mb + 4 * it + (lane >> 4), c = (wc0 >> 3) + (lane & 15);
+      const u32x4 v = get(r, c);
+      if (r < nrows && 8 * c < ncols) *reinterpret_cast<u32x4*>(dst + (long)r * ld + 8 * c) = v;
+    }
+  }
+};
+
+// A wave's 128 x 128 accumulator block rounded to bf16 and stored to rows [0, nrows)
+// and columns [0, ncols) of a row-major matrix (dst = the tile's element (0, 0)).
+__device__ __forceinline__ void store_acc_bf16(char* tile, const f32x16 (&acc)[4][4], int wr0,
+                                               int wc0, int lane, uint16_t* dst, long ld,
+                                               int nrows, int ncols) {
+  WaveStager st;
+  st.init(tile, wr0, wc0, lane);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int jp = 0; jp < 4; jp += 2)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          st.put(mb, q, jp, nb, acc_read(acc[mb][nb][4 * q + jp]),
+                 acc_read(acc[mb][nb][4 * q + jp + 1]));
+    st.fence();
+    st.store_rows(mb, dst, ld, nrows, ncols);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1103,20 +1153,9 @@ __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4]
                                               const float* r_cb, const float* r_sa,
                                               const int* t_local, int wr0, int wc0, int lane,
                                               float c1, unsigned colmask, uint16_t* dst) {
-  const int lc = lane & 31, hi = lane >> 5, odd = lane & 1;
-  // The lane writes rows r = rb + jp + odd (rb a multiple of 4 with bit 2 = hi, jp in
-  // {0, 2}), so out_swz(r) = 4 (odd | 2 hi) for all of them: one address per column
-  // block nb, and the row offsets 512 (32 mb + 8 q + jp) are immediates.
-  const int sw = odd | (hi << 1);
-  LDS_AS char* const t3 = (LDS_AS char*)tile;
-  const uint32_t base = (uint32_t)((wr0 + 4 * hi + odd) * 512 + (wc0 >> 3) * 16 + (lc & 6) * 2);
-  uint32_t addr[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) addr[nb] = base + (uint32_t)((((nb ^ sw) << 2) + (lc >> 3)) << 4);
-  // byte selectors of the pair exchange (v_perm_b32: bytes 0-3 from the second
-  // operand, this lane's pair; 4-7 from the first, the partner's): the even lane keeps
-  // both low halves (row r), the odd lane both high halves (row r + 1)
-  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+  const int lc = lane & 31, hi = lane >> 5;
+  WaveStager st;
+  st.init(tile, wr0, wc0, lane);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -1158,26 +1197,10 @@ __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4]
 #pragma unroll
       for (int jp = 0; jp < 4; jp += 2)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const f32x2 pr = {d[jp][nb], d[jp + 1][nb]};
-          const uint32_t own = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
-          const uint32_t partner =
-              (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0xB1, 0xf, 0xf, true);
-          const uint32_t w = __builtin_amdgcn_perm(partner, own, sel);
-          *(LDS_AS uint32_t*)(t3 + addr[nb] + (32 * mb + 8 * q + jp) * 512) = w;
-        }
+        for (int nb = 0; nb < 4; ++nb) st.put(mb, q, jp, nb, d[jp][nb], d[jp + 1][nb]);
     }
-    // The wave's 32 rows of block mb are staged (only this wave touches them): store
-    // them as the rows of two 64-column blocks of the tile-blocked buffer, 1 KiB of
-    // consecutive rows per instruction, while the next block is computed.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int qb = it >> 2, r = wr0 + 32 * mb + 8 * (it & 3) + (lane >> 3), c8 = lane & 7;
-      const int c = (wc0 >> 3) + 8 * qb + c8;
-      const u32x4 v = *(LDS_AS const u32x4*)(t3 + r * 512 + ((c ^ out_swz(r)) << 4));
-      *reinterpret_cast<u32x4*>(dst + (long)((wc0 >> 6) + qb) * BLK_ELEMS + r * BLK_COLS + 8 * c8) = v;
-    }
+    st.fence();
+    st.store_blocked(mb, dst);
   }
 }
 
@@ -1283,10 +1306,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
-  stage_wave_bf16(smem, wr0, wc0, lane, [&](int mb, int nb, int e) { return acc[mb][nb][e]; });
-  __syncthreads();
   const int rows = min(min(TILE, p.chunk_cols - i0), p.V - (p.vbase + i0));
-  store_tile_bf16(smem, p.dW + (long)(p.vbase + i0) * p.H + h0, p.H, rows, p.H - h0);
+  store_acc_bf16(smem, acc, wr0, wc0, lane, p.dW + (long)(p.vbase + i0) * p.H + h0, p.H, rows,
+                 p.H - h0);
 }
 
 // The fp32 side of a dX tile (modes 1-3).  Each wave moves its 128 x 128 block through
@@ -1312,7 +1334,7 @@ __device__ __forceinline__ void dx_tile_f32(const f32x16 (&acc)[4][4], char* sme
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int r = 32 * mi + acc_row(lane, e);  // (r >> 2) & 1 == hi
-          sl[r * 128 + ((32 * nb + lc) ^ (hi << 5))] = acc[2 * s + mi][nb][e];
+          sl[r * 128 + ((32 * nb + lc) ^ (hi << 5))] = acc_read(acc[2 * s + mi][nb][e]);
         }
     __syncthreads();
     const int rb = m0 + wr0 + 64 * s, cb = h0 + wc0;
@@ -1356,7 +1378,9 @@ __device__ __forceinline__ void dx_tile_f32(const f32x16 (&acc)[4][4], char* sme
 __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
   int tm, th;
-  tile_coords(blockIdx.x, gridDim.x, p.n_m, p.n_h, 8, tm, th);
+  // groups run along H: in step, the XCDs read the same W columns (shared through the
+  // memory-side cache) while each streams d-logit bands of its own
+  tile_coords(blockIdx.x, gridDim.x, p.n_h, p.n_m, 8, th, tm);
   const int m0 = tm * TILE, h0 = th * TILE;
   f32x16 acc[4][4];
   // the chunk's kcols (padded) columns of dzs (band tm of the blocked buffer); W has
@@ -1369,9 +1393,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
   if (p.mode == 0) {
-    stage_wave_bf16(smem, wr0, wc0, lane, [&](int mb, int nb, int e) { return acc[mb][nb][e]; });
-    __syncthreads();
-    store_tile_bf16(smem, p.dX + (long)m0 * p.H + h0, p.H, p.M - m0, p.H - h0);
+    store_acc_bf16(smem, acc, wr0, wc0, lane, p.dX + (long)m0 * p.H + h0, p.H, p.M - m0,
+                   p.H - h0);
   } else {
     dx_tile_f32(acc, smem, p, m0, h0, wave, lane);
   }
