@@ -246,7 +246,6 @@ struct DmaPlan {
   static constexpr int GPR = ROWS / 8;            // MN: 16-byte granules per K row
   static constexpr int KPOS_MAX = KC ? CHUNKS : BK;
   uint32_t voff[N];
-  uint32_t kpos[(N + 3) / 4];
   int wave;
   i32x4 rsrc0;         // buffer descriptor of the tile's base (k = 0), wave-uniform
   uint32_t kc_bytes;   // KC: bytes per K element (2, or 512 in a blocked matrix)
@@ -262,8 +261,6 @@ struct DmaPlan {
     band_bytes = (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)(blk ? s.band * 2 : (long)BLK_ROWS * s.ld * 2));
     const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int q = 0; q < (N + 3) / 4; ++q) kpos[q] = 0;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       const int G = (wave * N + j) * 64 + lane;  // 16-byte granule of the tile
@@ -281,14 +278,25 @@ struct DmaPlan {
                                   : (long)a * s.ld + 8 * b;
       // the load's immediate offset (1 KiB x (j % 4)) is added back by the hardware
       voff[j] = (ok ? (uint32_t)(e * 2) : OOB_OFFSET) - 1024u * (j & 3);
-      kpos[j >> 2] |= (uint32_t)(KC ? b : a) << (8 * (j & 3));
+    }
+  }
+
+  // K position of load j's 16 bytes within a step (a 16-byte chunk of K for KC, a K row
+  // for MN), recomputed rather than kept: it is needed only in the few steps that
+  // reach past K, and registers live across the K loop are the scarcest
+  __device__ __forceinline__ int kpos(int j) const {
+    const int G = (wave * N + j) * 64 + (int)(threadIdx.x & 63);
+    if constexpr (KC) {
+      const int a = G / CHUNKS;
+      return (G % CHUNKS) ^ kc_swz<CHUNKS>(a);
+    } else {
+      return G / GPR;
     }
   }
 
   // offset of load j in a step of which `lim` K positions exist
   __device__ __forceinline__ uint32_t off(int j, int lim) const {
-    const uint32_t kp = (kpos[j >> 2] >> (8 * (j & 3))) & 0xffu;
-    return kp < (uint32_t)lim ? voff[j] : OOB_OFFSET - 1024u * (j & 3);
+    return kpos(j) < lim ? voff[j] : OOB_OFFSET - 1024u * (j & 3);
   }
 };
 
