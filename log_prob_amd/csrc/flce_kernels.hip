@@ -546,19 +546,24 @@ __device__ __forceinline__ void substep_with_loads(f32x16 (&acc)[S::MB][S::NB],
 }
 
 // Pin the instruction order of one MFMA sub-step whose successor's fragments are
-// read during it: (ds_read, MFMA) x R, then the remaining MFMAs.
-template <class S, bool READS>
+// read during it: (ds_read, MFMA) x P, then the remaining MFMAs or reads.  A
+// transposing fragment takes two read instructions, so an M/N-contiguous operand
+// doubles its share of the reads; left unpinned, the scheduler put the extra reads
+// right before the MFMAs that use them, which then waited for all LDS reads.
+template <class S, bool A_KC, bool B_KC, bool READS>
 __device__ __forceinline__ void sched_substep() {
-  constexpr int F = S::MB * S::NB;                          // MFMAs per sub-step
-  constexpr int R = S::MB + S::NB < F ? S::MB + S::NB : F;  // reads paired with MFMAs
+  constexpr int F = S::MB * S::NB;                                    // MFMAs per sub-step
+  constexpr int R = frag_read_instrs<S, A_KC, B_KC>(0, S::MB + S::NB);  // read instructions
+  constexpr int P = R < F ? R : F;                                    // reads paired with MFMAs
   if constexpr (SCHED_PIPE) {
     if constexpr (READS) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
+      for (int i = 0; i < P; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
-      if constexpr (F > R) __builtin_amdgcn_sched_group_barrier(0x008, F - R, 0);
+      if constexpr (F > P) __builtin_amdgcn_sched_group_barrier(0x008, F - P, 0);
+      if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, 0);
     } else {
       __builtin_amdgcn_sched_group_barrier(0x008, F, 0);
     }
@@ -654,7 +659,7 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
     for (int kk = 1; kk < KK - 1; ++kk) {
       read_frags<S>(af[(kk + 1) & 1], bfr[(kk + 1) & 1], cur, frags, kk + 1);
       mfma_block<S::MB, S::NB>(acc, af[kk & 1], bfr[kk & 1]);
-      sched_substep<S, true>();
+      sched_substep<S, A_KC, B_KC, true>();
     }
 #if FLCE_FENCE_BARRIER
     // keep the barrier after every MFMA issued so far (the compiler would hoist it)
