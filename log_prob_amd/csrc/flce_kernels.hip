@@ -776,7 +776,9 @@ __device__ __forceinline__ float max_raw(float a, float b) {
 // r0 even within its group of 8) to four different 64-byte bank groups.  Each wave
 // stages its own 128 x 128 block and stores it 32 rows (one block row mb) at a time,
 // right after staging them: no other wave touches those bytes, so no workgroup
-// barrier, and the stores overlap the staging of the next block row.
+// barrier, and the stores overlap the staging of the next block row.  The stores carry
+// the non-temporal hint: no tile re-reads what it writes, and the lines would
+// otherwise displace operand tiles in L2 (backward -0.7% at H = 2048, neutral at 8192).
 __device__ __forceinline__ int out_swz(int r) { return ((r & 1) | ((r >> 1) & 2)) << 2; }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -837,7 +839,8 @@ struct WaveStager {
     for (int it = 0; it < 8; ++it) {
       const int qb = it >> 2, r = wr0 + 32 * mb + 8 * (it & 3) + (lane >> 3), c8 = lane & 7;
       const u32x4 v = get(r, (wc0 >> 3) + 8 * qb + c8);
-      *reinterpret_cast<u32x4*>(dst + (long)((wc0 >> 6) + qb) * BLK_ELEMS + r * BLK_COLS + 8 * c8) = v;
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4*>(dst + (long)((wc0 >> 6) + qb) * BLK_ELEMS + r * BLK_COLS + 8 * c8));
     }
   }
 
@@ -850,7 +853,8 @@ struct WaveStager {
     for (int it = 0; it < 8; ++it) {
       const int r = wr0 + 32 * mb + 4 * it + (lane >> 4), c = (wc0 >> 3) + (lane & 15);
       const u32x4 v = get(r, c);
-      if (r < nrows && 8 * c < ncols) *reinterpret_cast<u32x4*>(dst + (long)r * ld + 8 * c) = v;
+      if (r < nrows && 8 * c < ncols)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + (long)r * ld + 8 * c));
     }
   }
 };
