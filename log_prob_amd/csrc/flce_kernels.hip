@@ -1381,7 +1381,8 @@ __device__ __forceinline__ void dx_tile_f32(const f32x16 (&acc)[4][4], char* sme
             const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2));
             *reinterpret_cast<uint2*>(p.dX + (long)m * p.H + h) = make_uint2(a, b);
           } else {
-            *reinterpret_cast<float4*>(p.acc + (long)m * p.H + h) = t;
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, t),
+                                        reinterpret_cast<u32x4*>(p.acc + (long)m * p.H + h));
           }
         }
       }
