@@ -82,7 +82,8 @@ flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_
 /*
  * Smallest workspace flce_backward accepts.  The backward walks the vocabulary
  * in chunks whose width it derives from the workspace it is given: the
- * preferred size holds every column in one chunk, the minimum holds one tile
+ * preferred size holds up to 4 GiB of bf16 d-logits per chunk (every column at once
+ * when they fit), the minimum holds one tile
  * column (256 vocabulary entries) per chunk plus an fp32 dX accumulator.
  * Results differ between chunk widths only by fp32 summation order in dX.
  */
@@ -205,7 +206,7 @@ flce_status_t flce_forward_merge_shards(const int64_t* targets, int64_t M, int64
                                         size_t shard_stride_bytes, struct ihipStream_t* stream);
 
 /* Workspace bytes for flce_backward_shard: the minimum (one 256-column d-logit
- * chunk) and the preferred size (the d-logits of up to 2 GiB of columns at once).
+ * chunk) and the preferred size (up to 4 GiB of bf16 d-logits per chunk).
  * Either output may be NULL. */
 flce_status_t flce_backward_shard_workspace_query(int64_t M, int64_t H, int64_t V_shard,
                                                   size_t* min_bytes, size_t* preferred_bytes);

@@ -34,8 +34,11 @@ constexpr int64_t kMaxV = int64_t(1) << 30;
 constexpr int64_t kMaxH = int64_t(1) << 20;
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 constexpr size_t kAlign = 256;
-// Preferred size of one d-logit chunk buffer: 2 GiB.
-constexpr size_t kDzBudget = size_t(2) << 30;
+// Preferred size of one d-logit chunk buffer: 4 GiB.  Wider chunks mean fewer passes
+// over the fp32 dX accumulator and fewer launches; past about 2000 K steps the dX GEMM's
+// tiles drift apart in L2 (M=32767, H=2048, V=151936: 3 chunks of 65536 columns -0.8 to
+// -1.8% against 5 of 32768, one chunk of 152064 +2%).
+constexpr size_t kDzBudget = size_t(4) << 30;
 // Widest d-logit chunk: keeps every byte offset the kernels form inside one
 // 256-row tile of the chunk buffer below 2^30.
 constexpr int64_t kMaxChunk = int64_t(1) << 21;

@@ -38,7 +38,8 @@ def test_workspace_query_values():
     assert fwd == 3 * 512 * 8192 * 4 + 8192 * 4
     fwd0, _ = flce.workspace_query(8192, 8192, 131072, False)
     assert fwd0 == 2 * 512 * 8192 * 4 + 8192 * 4
-    # backward preferred: one 2 GiB d-logit chunk covers the whole vocabulary here
+    # backward preferred: one d-logit chunk (2 GiB, within the 4 GiB budget) covers the
+    # whole vocabulary here
     assert bwd == 8192 * 131072 * 2
     assert flce.backward_chunk_cols(8192, 8192, 131072, bwd) == 131072
     # smaller workspaces shrink the chunk, down to one 256-column tile plus fp32 dX
