@@ -52,6 +52,10 @@ def test_workspace_query_values():
     _, bwd = flce.workspace_query(32767, 2048, 151936, True)
     c = flce.backward_chunk_cols(32767, 2048, 151936, bwd)
     assert c % 256 == 0 and 256 <= c < 151936 + 256
+    # d-logits past the 4 GiB chunk budget: 65536-column chunks (4 GiB of bf16 over
+    # 32768 padded rows) plus the fp32 dX accumulator
+    assert c == 65536
+    assert bwd == 32768 * 65536 * 2 + 32767 * 2048 * 4
 
 
 def test_forward_token_waves():
