@@ -1372,8 +1372,9 @@ __device__ __forceinline__ void dx_tile_f32(const f32x16 (&acc)[4][4], char* sme
         const int g = 64 * (16 * half + it) + lane, r = g >> 5, c = 4 * (g & 31);
         const int m = rb + r, h = cb + c;
         const float4 v = *reinterpret_cast<const float4*>(sl + r * 128 + (c ^ (((r >> 2) & 1) << 5)));
-        const float4 t = make_float4(old[it].x + v.x, old[it].y + v.y, old[it].z + v.z,
-                                     old[it].w + v.w);
+        const float4 t = p.mode == 1 ? v
+                                     : make_float4(old[it].x + v.x, old[it].y + v.y,
+                                                   old[it].z + v.z, old[it].w + v.w);
         if (m < p.M && h < p.H) {
           if (p.mode == 3) {
             const f32x2 lo = {t.x, t.y}, hi2 = {t.z, t.w};
