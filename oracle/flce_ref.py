@@ -45,7 +45,7 @@ import numpy as np
 __all__ = [
     "decode_bf16", "valid_rows", "logits", "from_logits", "forward_f64", "forward",
     "forward_rows", "backward_f64", "backward", "dx_rows", "dw_rows", "row_block",
-    "nll_reduce", "nll_mean_grad",
+    "nll_reduce", "nll_mean_grad", "policy_loss", "policy_loss_grad",
 ]
 
 
@@ -242,4 +242,59 @@ def nll_mean_grad(t, V, ignore_index, n_valid):
     g = np.zeros(len(valid))
     if n_valid:
         g[valid] = -1.0 / n_valid
+    return g
+
+
+def policy_loss(logprob, old_logprob, advantages, t, V, ignore_index, eps_low, eps_high,
+                denominator=0.0):
+    """Clipped policy-gradient loss on the per-token log-probs, token-mean aggregated.
+
+    Liger-Kernel PR 1294, "Chunked Triton GRPO loss": the loss sits on the per-token
+    log-probs of the fused linear path ("Setup": loss_type "dapo", clip eps 0.2/0.2,
+    num_items_in_batch; "Correctness": per-token loss and is_clipped outputs).  The page
+    names these settings without formulas; the reading here is the plainest one, the
+    clipped surrogate of proximal policy optimisation with a token-level ratio and the
+    DAPO token mean:
+
+      r_m   = exp(logprob_m - old_logprob_m)       (old_logprob None: r = 1)
+      c_m   = min(max(r_m, 1 - eps_low), 1 + eps_high)
+      l_m   = -min(r_m A_m, c_m A_m)               per-token loss, 0 on invalid rows
+      clip_m = c_m A_m < r_m A_m                   the minimum takes the clipped term
+      L     = sum of l_m over valid rows / N,      N = denominator if > 0, else the
+                                                   number of valid rows
+
+    Returns (per_token_loss [M], is_clipped bool [M], sum of l_m, valid rows, clipped
+    rows, L; NaN when N is 0).  Everything in float64.
+    """
+    valid = valid_rows(t, V, ignore_index)
+    lp = np.asarray(logprob, np.float64)
+    old = lp if old_logprob is None else np.asarray(old_logprob, np.float64)
+    A = np.asarray(advantages, np.float64)
+    r = np.exp(lp - old)
+    c = np.minimum(np.maximum(r, 1.0 - float(eps_low)), 1.0 + float(eps_high))
+    unclipped, clipped = r * A, c * A
+    loss = np.where(valid, -np.minimum(unclipped, clipped), 0.0)
+    is_clipped = valid & (clipped < unclipped)
+    n = int(np.count_nonzero(valid))
+    total = float(np.sum(loss))
+    N = float(denominator) if denominator > 0 else float(n)
+    return (loss, is_clipped, total, n, int(np.count_nonzero(is_clipped)),
+            total / N if N > 0 else float("nan"))
+
+
+def policy_loss_grad(logprob, old_logprob, advantages, t, V, ignore_index, eps_low, eps_high,
+                     N):
+    """dL/dlogprob of the token-mean clipped loss above: -r_m A_m / N on valid rows whose
+    minimum takes the unclipped term (d r_m / d logprob_m = r_m), 0 on clipped and
+    invalid rows and everywhere when N is 0."""
+    loss, is_clipped, _, _, _, _ = policy_loss(logprob, old_logprob, advantages, t, V,
+                                               ignore_index, eps_low, eps_high)
+    valid = valid_rows(t, V, ignore_index)
+    lp = np.asarray(logprob, np.float64)
+    old = lp if old_logprob is None else np.asarray(old_logprob, np.float64)
+    r = np.exp(lp - old)
+    g = np.zeros(len(valid))
+    if N > 0:
+        keep = valid & ~is_clipped
+        g[keep] = -r[keep] * np.asarray(advantages, np.float64)[keep] / float(N)
     return g
