@@ -254,6 +254,46 @@ flce_status_t flce_nll_mean_grad(const int64_t* targets, int64_t M, int64_t V,
                                  int64_t ignore_index, const double* reduced,
                                  float* grad_logprob, struct ihipStream_t* stream);
 
+/*
+ * Clipped policy-gradient loss on a forward's per-token log-probs, aggregated as a
+ * token mean (Liger-Kernel PR 1294, section "Chunked Triton GRPO loss": the loss on
+ * top of the fused linear log-probs, settings "Setup" (loss type dapo, clip range
+ * eps 0.2/0.2, num_items_in_batch) and per-token outputs "Correctness"; the page
+ * gives no formulas, this is the plain clipped-surrogate reading).  Per token m,
+ * valid as in flce_forward, in fp64:
+ *   r = exp(logprob[m] - old_logprob[m])          (old_logprob NULL: r = 1)
+ *   c = min(max(r, 1 - eps_low), 1 + eps_high)
+ *   per_token_loss[m] = -min(r A[m], c A[m])      (0 on invalid rows, as fp32)
+ *   is_clipped[m]     = c A[m] < r A[m]           (optional output, NULL to skip)
+ * and four fp64 values to the device array out: the sum of the per-token loss over
+ * valid rows, the number of valid rows, the number of clipped rows, and the loss
+ * sum / N with N = denominator if > 0 (the caller's normaliser, e.g. the number of
+ * items in the batch), else the number of valid rows; NaN when N is 0.  One
+ * workgroup with a fixed summation order: bitwise repeatable.  eps_low and
+ * eps_high must be finite and >= 0, denominator finite; all arrays on the device.
+ */
+flce_status_t flce_policy_loss_reduce(const float* logprob, const float* old_logprob,
+                                      const float* advantages, const int64_t* targets,
+                                      int64_t M, int64_t V, int64_t ignore_index,
+                                      double eps_low, double eps_high, double denominator,
+                                      float* per_token_loss, uint8_t* is_clipped, double* out,
+                                      struct ihipStream_t* stream);
+
+/*
+ * dL/dlogprob of the loss of flce_policy_loss_reduce (same inputs):
+ * grad_logprob[m] = -r A[m] / N on valid rows whose minimum takes the unclipped
+ * term, 0 on clipped and invalid rows, all zeros when N is 0.  With denominator <= 0,
+ * N is read on the device from reduced[1] (the out array of
+ * flce_policy_loss_reduce), so no host synchronisation is needed; reduced may be
+ * NULL when denominator > 0.  The result is the grad_logprob argument of
+ * flce_backward.
+ */
+flce_status_t flce_policy_loss_grad(const float* logprob, const float* old_logprob,
+                                    const float* advantages, const int64_t* targets, int64_t M,
+                                    int64_t V, int64_t ignore_index, double eps_low,
+                                    double eps_high, double denominator, const double* reduced,
+                                    float* grad_logprob, struct ihipStream_t* stream);
+
 /* Static description of a status code. */
 const char* flce_status_string(flce_status_t status);
 

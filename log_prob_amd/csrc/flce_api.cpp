@@ -740,3 +740,72 @@ flce_status_t flce_nll_mean_grad(const int64_t* targets, int64_t M, int64_t V,
 }
 
 }  // extern "C"
+
+namespace {
+flce_status_t policy_args(const float* logprob, const float* old_logprob,
+                          const float* advantages, const int64_t* targets, int64_t M, int64_t V,
+                          int64_t ignore_index, double eps_low, double eps_high,
+                          double denominator, flce::PolicyLossArgs* a) {
+  if (M < 0 || V <= 0)
+    return fail(FLCE_ERR_INVALID_VALUE, "M must be >= 0 and V positive (got M=%lld V=%lld)",
+                (long long)M, (long long)V);
+  if (M > kMaxM || V > kMaxV)
+    return fail(FLCE_ERR_UNSUPPORTED, "shape too large (limits M, V <= 2^30)");
+  if (M > 0 && (!logprob || !advantages || !targets))
+    return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among logprob, advantages, targets");
+  if (!std::isfinite(eps_low) || !std::isfinite(eps_high) || eps_low < 0.0 || eps_high < 0.0)
+    return fail(FLCE_ERR_INVALID_VALUE, "eps_low and eps_high must be finite and >= 0");
+  if (!std::isfinite(denominator))
+    return fail(FLCE_ERR_INVALID_VALUE, "denominator is not finite");
+  if (!aligned(logprob, 4) || !aligned(old_logprob, 4) || !aligned(advantages, 4) ||
+      !aligned(targets, 8))
+    return fail(FLCE_ERR_UNSUPPORTED, "logprob, old_logprob, advantages and targets must be "
+                "naturally aligned");
+  *a = flce::PolicyLossArgs{logprob, old_logprob, advantages, targets, long(M), V,
+                            ignore_index, eps_low, eps_high, denominator};
+  return FLCE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+flce_status_t flce_policy_loss_reduce(const float* logprob, const float* old_logprob,
+                                      const float* advantages, const int64_t* targets,
+                                      int64_t M, int64_t V, int64_t ignore_index,
+                                      double eps_low, double eps_high, double denominator,
+                                      float* per_token_loss, uint8_t* is_clipped, double* out,
+                                      hipStream_t stream) {
+  flce::PolicyLossArgs a;
+  flce_status_t st = policy_args(logprob, old_logprob, advantages, targets, M, V, ignore_index,
+                                 eps_low, eps_high, denominator, &a);
+  if (st != FLCE_OK) return st;
+  if (!out || (M > 0 && !per_token_loss))
+    return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among per_token_loss, out");
+  if (!aligned(out, 8) || !aligned(per_token_loss, 4))
+    return fail(FLCE_ERR_UNSUPPORTED, "per_token_loss and out must be naturally aligned");
+  const hipError_t e = flce::launch_policy_loss_reduce(a, per_token_loss, is_clipped, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "policy loss reduction kernel launch");
+  return ok();
+}
+
+flce_status_t flce_policy_loss_grad(const float* logprob, const float* old_logprob,
+                                    const float* advantages, const int64_t* targets, int64_t M,
+                                    int64_t V, int64_t ignore_index, double eps_low,
+                                    double eps_high, double denominator, const double* reduced,
+                                    float* grad_logprob, hipStream_t stream) {
+  flce::PolicyLossArgs a;
+  flce_status_t st = policy_args(logprob, old_logprob, advantages, targets, M, V, ignore_index,
+                                 eps_low, eps_high, denominator, &a);
+  if (st != FLCE_OK) return st;
+  if (M == 0) return ok();
+  if (!grad_logprob || (denominator <= 0.0 && !reduced))
+    return fail(FLCE_ERR_INVALID_VALUE,
+                "NULL pointer among grad_logprob, reduced (needed when denominator <= 0)");
+  if (!aligned(grad_logprob, 4) || !aligned(reduced, 8))
+    return fail(FLCE_ERR_UNSUPPORTED, "grad_logprob and reduced must be naturally aligned");
+  const hipError_t e = flce::launch_policy_loss_grad(a, reduced, grad_logprob, stream);
+  if (e != hipSuccess) return hip_fail(e, "policy loss gradient kernel launch");
+  return ok();
+}
+
+}  // extern "C"

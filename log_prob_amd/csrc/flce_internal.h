@@ -98,6 +98,18 @@ struct GemmDxArgs {
   int mode;             // 0 write bf16, 1 write acc, 2 add to acc, 3 add and write bf16
 };
 
+// Clipped policy loss over per-token log-probs (see flce_policy_loss_reduce).
+struct PolicyLossArgs {
+  const float* logprob;      // [M]
+  const float* old_logprob;  // [M] or nullptr (ratio 1)
+  const float* advantages;   // [M]
+  const int64_t* targets;    // [M]
+  long M;
+  int64_t V, ignore_index;
+  double eps_low, eps_high;
+  double denominator;        // > 0: the normaliser N; else the number of valid rows
+};
+
 hipError_t launch_fwd_tile(const FwdTileArgs& a, bool entropy, hipStream_t s);
 hipError_t launch_target_logit(const FwdTileArgs& a, hipStream_t s);
 hipError_t launch_fwd_merge(const FwdMergeArgs& a, bool entropy, hipStream_t s);
@@ -105,6 +117,10 @@ hipError_t launch_dlogits(const DlogitsArgs& a, bool entropy_grad, hipStream_t s
 hipError_t launch_gemm_dw(const GemmDwArgs& a, hipStream_t s);
 hipError_t launch_gemm_dx(const GemmDxArgs& a, hipStream_t s);
 hipError_t launch_fill_zero_u16(uint16_t* p, long n, hipStream_t s);
+hipError_t launch_policy_loss_reduce(const PolicyLossArgs& a, float* per_token_loss,
+                                     uint8_t* is_clipped, double* out, hipStream_t s);
+hipError_t launch_policy_loss_grad(const PolicyLossArgs& a, const double* reduced, float* grad,
+                                   hipStream_t s);
 hipError_t launch_nll_reduce(const float* logprob, const int64_t* targets, long M, int64_t V,
                              int64_t ignore_index, double* out, hipStream_t s);
 hipError_t launch_nll_mean_grad(const int64_t* targets, long M, int64_t V, int64_t ignore_index,

@@ -10,7 +10,9 @@
 //   fwd_merge    combines the per-tile partials of each row (max first, then the
 //                rescaled sums) into lse, logprob and entropy.
 // Scalar reductions: nll_reduce (sum, count and mean of -logprob over valid rows) and
-// nll_mean_grad (the mean NLL's gradient with respect to logprob).
+// nll_mean_grad (the mean NLL's gradient with respect to logprob); policy_loss_reduce
+// and policy_loss_grad (a clipped policy-gradient loss on the log-probs, token-mean
+// aggregated, and its gradient with respect to logprob).
 // Backward (Liger-Kernel PR 1294, "Kernel design notes": recompute the logits
 // tiles, emit d-logits in the input dtype into a reusable buffer, then two grad
 // GEMMs; SkyRL PR 2141, "Overview": split backward over the vocabulary):
@@ -1471,6 +1473,88 @@ __global__ void nll_mean_grad_kernel(const int64_t* __restrict__ targets, long M
   }
 }
 
+// Clipped policy loss on the per-token log-probs (Liger-Kernel PR 1294, "Chunked Triton
+// GRPO loss": the loss on top of the fused linear log-probs, with clip range and
+// token-level normalisation; the page gives no formulas, the plain reading is the
+// clipped surrogate).  Per valid token, in fp64: r = exp(logprob - old_logprob),
+// c = min(max(r, 1 - eps_low), 1 + eps_high), loss = -min(r A, c A), clipped iff
+// c A < r A.  Both kernels evaluate the same expression, so the gradient kernel takes
+// the same clip decision as the reduction.
+struct PolicyTerm {
+  double u, cl;  // r A and c A
+  bool valid;
+};
+__device__ __forceinline__ PolicyTerm policy_term(const PolicyLossArgs& p, long i) {
+  PolicyTerm o;
+  const int64_t tg = p.targets[i];
+  o.valid = tg != p.ignore_index && tg >= 0 && tg < p.V;
+  const double lp = (double)p.logprob[i];
+  const double old = p.old_logprob ? (double)p.old_logprob[i] : lp;
+  const double a = (double)p.advantages[i];
+  const double r = exp(lp - old);
+  const double c = fmin(fmax(r, 1.0 - p.eps_low), 1.0 + p.eps_high);
+  o.u = r * a;
+  o.cl = c * a;
+  return o;
+}
+
+// One workgroup, fixed summation order (bitwise repeatable): thread t takes tokens
+// t, t + 1024, ..., then a fixed tree.  Writes the per-token loss (0 on invalid rows)
+// and clip flags, and out = {sum of the loss, valid rows, clipped rows, sum / N} with
+// N = denominator if > 0, else the valid rows (NaN when N is 0).
+constexpr int PL_THREADS = 1024;
+__global__ __launch_bounds__(PL_THREADS) void policy_loss_reduce_kernel(
+    PolicyLossArgs p, float* __restrict__ per_token_loss, uint8_t* __restrict__ is_clipped,
+    double* __restrict__ out) {
+  __shared__ double ss[PL_THREADS];
+  __shared__ long sn[PL_THREADS], sk[PL_THREADS];
+  const int t = threadIdx.x;
+  double s = 0.0;
+  long n = 0, k = 0;
+  for (long i = t; i < p.M; i += PL_THREADS) {
+    const PolicyTerm o = policy_term(p, i);
+    const bool clipped = o.valid && o.cl < o.u;
+    const double loss = o.valid ? -fmin(o.u, o.cl) : 0.0;
+    per_token_loss[i] = (float)loss;
+    if (is_clipped) is_clipped[i] = clipped ? 1 : 0;
+    s += loss;
+    n += o.valid ? 1 : 0;
+    k += clipped ? 1 : 0;
+  }
+  ss[t] = s;
+  sn[t] = n;
+  sk[t] = k;
+  __syncthreads();
+  for (int w = PL_THREADS / 2; w > 0; w >>= 1) {
+    if (t < w) {
+      ss[t] += ss[t + w];
+      sn[t] += sn[t + w];
+      sk[t] += sk[t + w];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    const double N = p.denominator > 0.0 ? p.denominator : (double)sn[0];
+    out[0] = ss[0];
+    out[1] = (double)sn[0];
+    out[2] = (double)sk[0];
+    out[3] = N > 0.0 ? ss[0] / N : __builtin_nan("");
+  }
+}
+
+// grad[i] = -r A / N on valid tokens whose minimum takes the unclipped term, else 0;
+// N as in the reduction (the valid-row count read from reduced[1] when the
+// denominator is not positive).
+__global__ void policy_loss_grad_kernel(PolicyLossArgs p, const double* __restrict__ reduced,
+                                        float* __restrict__ grad) {
+  const double N = p.denominator > 0.0 ? p.denominator : reduced[1];
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < p.M; i += stride) {
+    const PolicyTerm o = policy_term(p, i);
+    grad[i] = (o.valid && !(o.cl < o.u) && N > 0.0) ? (float)(-o.u / N) : 0.f;
+  }
+}
+
 __global__ void fill_u16_kernel(uint16_t* __restrict__ p, long n) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const long stride = (long)gridDim.x * blockDim.x;
@@ -1533,6 +1617,20 @@ hipError_t launch_nll_mean_grad(const int64_t* targets, long M, int64_t V, int64
   long blocks = (M + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   nll_mean_grad_kernel<<<(unsigned)blocks, 256, 0, s>>>(targets, M, V, ignore_index, reduced, grad);
+  return hipGetLastError();
+}
+
+hipError_t launch_policy_loss_reduce(const PolicyLossArgs& a, float* per_token_loss,
+                                     uint8_t* is_clipped, double* out, hipStream_t s) {
+  policy_loss_reduce_kernel<<<1, PL_THREADS, 0, s>>>(a, per_token_loss, is_clipped, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_policy_loss_grad(const PolicyLossArgs& a, const double* reduced, float* grad,
+                                   hipStream_t s) {
+  long blocks = (a.M + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  policy_loss_grad_kernel<<<(unsigned)blocks, 256, 0, s>>>(a, reduced, grad);
   return hipGetLastError();
 }
 

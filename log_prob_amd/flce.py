@@ -23,7 +23,8 @@ EXPORTS = ("flce_workspace_query", "flce_forward_workspace_min", "flce_forward_w
            "flce_forward_partials", "flce_forward_merge", "flce_backward",
            "flce_forward_partials_shard", "flce_forward_merge_shards",
            "flce_backward_shard_workspace_query", "flce_backward_shard", "flce_nll_reduce",
-           "flce_nll_mean_grad", "flce_status_string",
+           "flce_nll_mean_grad", "flce_policy_loss_reduce", "flce_policy_loss_grad",
+           "flce_status_string",
            "flce_last_error_message", "flce_version")
 
 _lib = None
@@ -66,7 +67,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         P, P, c.c_int, P, P, SZ, P]
     lib.flce_nll_reduce.argtypes = [P, P, I64, I64, I64, P, P]
     lib.flce_nll_mean_grad.argtypes = [P, I64, I64, I64, P, P, P]
-    for name in ("flce_nll_reduce", "flce_nll_mean_grad", "flce_workspace_query",
+    D = c.c_double
+    lib.flce_policy_loss_reduce.argtypes = [P, P, P, P, I64, I64, I64, D, D, D, P, P, P, P]
+    lib.flce_policy_loss_grad.argtypes = [P, P, P, P, I64, I64, I64, D, D, D, P, P, P]
+    for name in ("flce_nll_reduce", "flce_nll_mean_grad", "flce_policy_loss_reduce",
+                 "flce_policy_loss_grad", "flce_workspace_query",
                  "flce_forward_workspace_min", "flce_forward_wave_rows",
                  "flce_backward_workspace_min", "flce_backward_chunk_cols", "flce_forward",
                  "flce_forward_partials", "flce_forward_merge", "flce_backward",
@@ -350,4 +355,53 @@ def nll_mean_grad(targets, V: int, reduced, ignore_index: int = -100, out=None):
     _require(out, "grad_logprob", torch.float32, (M,))
     _check(load().flce_nll_mean_grad(_ptr(targets), M, int(V), int(ignore_index), _ptr(reduced),
                                      _ptr(out), _stream(targets.device)))
+    return out
+
+
+def _policy_inputs(logprob, old_logprob, advantages, targets):
+    import torch
+    M = logprob.shape[0]
+    _require(logprob, "logprob", torch.float32, (M,))
+    if old_logprob is not None:
+        _require(old_logprob, "old_logprob", torch.float32, (M,))
+    _require(advantages, "advantages", torch.float32, (M,))
+    _require(targets, "targets", torch.int64, (M,))
+    return M
+
+
+def policy_loss_reduce(logprob, old_logprob, advantages, targets, V: int,
+                       ignore_index: int = -100, eps_low: float = 0.2, eps_high: float = 0.2,
+                       denominator: float = 0.0, with_clip_flags: bool = True):
+    """Clipped policy loss on the log-probs, token-mean aggregated (see include/flce.h):
+    (per-token loss fp32 [M], clip flags uint8 [M] or None, fp64 device tensor [loss sum,
+    valid rows, clipped rows, loss sum / N])."""
+    import torch
+    M = _policy_inputs(logprob, old_logprob, advantages, targets)
+    dev = logprob.device
+    per_token = torch.empty(M, dtype=torch.float32, device=dev)
+    clipped = torch.empty(M, dtype=torch.uint8, device=dev) if with_clip_flags else None
+    out = torch.empty(4, dtype=torch.float64, device=dev)
+    _check(load().flce_policy_loss_reduce(
+        _ptr(logprob), _ptr(old_logprob), _ptr(advantages), _ptr(targets), M, int(V),
+        int(ignore_index), float(eps_low), float(eps_high), float(denominator), _ptr(per_token),
+        _ptr(clipped), _ptr(out), _stream(dev)))
+    return per_token, clipped, out
+
+
+def policy_loss_grad(logprob, old_logprob, advantages, targets, V: int, reduced=None,
+                     ignore_index: int = -100, eps_low: float = 0.2, eps_high: float = 0.2,
+                     denominator: float = 0.0, out=None):
+    """grad_logprob of the loss of policy_loss_reduce; `reduced` is its fp64 output
+    (needed when denominator <= 0)."""
+    import torch
+    M = _policy_inputs(logprob, old_logprob, advantages, targets)
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=logprob.device)
+    _require(out, "grad_logprob", torch.float32, (M,))
+    if reduced is not None:
+        _require(reduced, "reduced", torch.float64, (4,))
+    _check(load().flce_policy_loss_grad(
+        _ptr(logprob), _ptr(old_logprob), _ptr(advantages), _ptr(targets), M, int(V),
+        int(ignore_index), float(eps_low), float(eps_high), float(denominator), _ptr(reduced),
+        _ptr(out), _stream(logprob.device)))
     return out

@@ -219,6 +219,36 @@ def test_nll_argument_errors():
     assert lib.flce_nll_mean_grad(12, 4, 3, -100, 16, 16, None) == UNS
 
 
+def test_policy_loss_argument_errors():
+    """Every invalid call of the policy-loss entry points fails on the host, before any
+    HIP call (fake, aligned device addresses; nothing is dereferenced)."""
+    lib = flce.load()
+    INV, UNS = 1, 2
+
+    def red(lp=16, old=None, adv=16, t=16, M=4, V=3, el=0.2, eh=0.2, den=0.0, ptl=16, out=16):
+        return lib.flce_policy_loss_reduce(lp, old, adv, t, M, V, -100, el, eh, den, ptl, None,
+                                           out, None)
+
+    def grad(lp=16, old=None, adv=16, t=16, M=4, V=3, el=0.2, eh=0.2, den=0.0, reduced=16,
+             g=16):
+        return lib.flce_policy_loss_grad(lp, old, adv, t, M, V, -100, el, eh, den, reduced, g,
+                                         None)
+
+    assert red(lp=None) == INV and red(adv=None) == INV and red(t=None) == INV
+    assert red(ptl=None) == INV and red(out=None) == INV
+    assert red(M=-1) == INV and red(V=0) == INV
+    assert red(M=1 << 31) == UNS
+    assert red(el=-0.1) == INV and red(eh=float("inf")) == INV and red(el=float("nan")) == INV
+    assert red(den=float("nan")) == INV
+    assert red(lp=18) == UNS and red(old=18) == UNS and red(t=20) == UNS and red(out=20) == UNS
+    assert grad(g=None) == INV
+    assert grad(reduced=None) == INV                    # the count is read from `reduced`
+    assert grad(V=0) == INV and grad(el=-1.0) == INV
+    assert grad(reduced=20) == UNS and grad(g=18) == UNS
+    # an empty batch of tokens launches nothing
+    assert grad(M=0, lp=None, adv=None, t=None, g=None, reduced=None) == 0
+
+
 def test_empty_batch_needs_no_device():
     """M = 0 is a valid, empty call: sizes are 0 and the forward and the merges return
     FLCE_OK before any HIP call, with every pointer NULL."""
