@@ -123,3 +123,64 @@ def test_normaliser_and_empty_batch():
     _, _, total, n, _, mean = ref.policy_loss(lp, old, A, tt, V, IGN, 0.2, 0.2)
     assert n == 0 and total == 0 and np.isnan(mean)
     assert np.all(ref.policy_loss_grad(lp, old, A, tt, V, IGN, 0.2, 0.2, 0) == 0)
+
+
+# --- planted mistakes: each must fail at least one of the pins above -------------
+import inspect  # noqa: E402
+import types  # noqa: E402
+
+_SRC = inspect.getsource(ref)
+MUTANTS = {
+    "min_to_max": ("loss = np.where(valid, -np.minimum(unclipped, clipped), 0.0)",
+                   "loss = np.where(valid, -np.maximum(unclipped, clipped), 0.0)"),
+    "loss_unmasked": ("loss = np.where(valid, -np.minimum(unclipped, clipped), 0.0)",
+                      "loss = -np.minimum(unclipped, clipped)"),
+    "eps_swapped": ("c = np.minimum(np.maximum(r, 1.0 - float(eps_low)), 1.0 + float(eps_high))",
+                    "c = np.minimum(np.maximum(r, 1.0 - float(eps_high)), 1.0 + float(eps_low))"),
+    "ratio_inverted": ("    r = np.exp(lp - old)\n    c = ", "    r = np.exp(old - lp)\n    c = "),
+    "tie_counts_as_clipped": ("is_clipped = valid & (clipped < unclipped)",
+                              "is_clipped = valid & (clipped <= unclipped)"),
+    "grad_sign": ("g[keep] = -r[keep] * np.asarray(advantages, np.float64)[keep] / float(N)",
+                  "g[keep] = r[keep] * np.asarray(advantages, np.float64)[keep] / float(N)"),
+    "grad_keeps_clipped": ("keep = valid & ~is_clipped", "keep = valid"),
+    "grad_drops_ratio": ("g[keep] = -r[keep] * np.asarray(advantages, np.float64)[keep] / float(N)",
+                         "g[keep] = -np.asarray(advantages, np.float64)[keep] / float(N)"),
+    "mean_over_all_rows": ("N = float(denominator) if denominator > 0 else float(n)",
+                           "N = float(denominator) if denominator > 0 else float(len(valid))"),
+}
+
+
+def _mutant(old, new):
+    assert _SRC.count(old) == 1, f"mutation site not found: {old}"
+    mod = types.ModuleType("flce_ref_policy_mutant")
+    exec(compile(_SRC.replace(old, new), "flce_ref_policy_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _pins_pass(m):
+    """True iff the module passes every pin of this file."""
+    global ref
+    saved = ref
+    ref = m
+    try:
+        for fn in (test_hand_worked_cases, test_on_policy_closed_form,
+                   test_gradient_against_torch_autograd,
+                   test_wide_clip_range_is_importance_weighted_policy_gradient,
+                   test_normaliser_and_empty_batch):
+            fn()
+        for seed in (1, 2, 3):
+            test_gradient_by_finite_differences(seed)
+        return True
+    except AssertionError:
+        return False
+    finally:
+        ref = saved
+
+
+def test_the_real_oracle_passes_the_pins():
+    assert _pins_pass(ref)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    assert not _pins_pass(_mutant(*MUTANTS[name])), f"mutant {name} passed every pin"
