@@ -371,16 +371,23 @@ def _policy_inputs(logprob, old_logprob, advantages, targets):
 
 def policy_loss_reduce(logprob, old_logprob, advantages, targets, V: int,
                        ignore_index: int = -100, eps_low: float = 0.2, eps_high: float = 0.2,
-                       denominator: float = 0.0, with_clip_flags: bool = True):
+                       denominator: float = 0.0, with_clip_flags: bool = True, out=None):
     """Clipped policy loss on the log-probs, token-mean aggregated (see include/flce.h):
     (per-token loss fp32 [M], clip flags uint8 [M] or None, fp64 device tensor [loss sum,
-    valid rows, clipped rows, loss sum / N])."""
+    valid rows, clipped rows, loss sum / N]).  `out` may supply those three buffers."""
     import torch
     M = _policy_inputs(logprob, old_logprob, advantages, targets)
     dev = logprob.device
-    per_token = torch.empty(M, dtype=torch.float32, device=dev)
-    clipped = torch.empty(M, dtype=torch.uint8, device=dev) if with_clip_flags else None
-    out = torch.empty(4, dtype=torch.float64, device=dev)
+    if out is not None:
+        per_token, clipped, out = out
+    else:
+        per_token = torch.empty(M, dtype=torch.float32, device=dev)
+        clipped = torch.empty(M, dtype=torch.uint8, device=dev) if with_clip_flags else None
+        out = torch.empty(4, dtype=torch.float64, device=dev)
+    _require(per_token, "per_token_loss", torch.float32, (M,))
+    if clipped is not None:
+        _require(clipped, "is_clipped", torch.uint8, (M,))
+    _require(out, "out", torch.float64, (4,))
     _check(load().flce_policy_loss_reduce(
         _ptr(logprob), _ptr(old_logprob), _ptr(advantages), _ptr(targets), M, int(V),
         int(ignore_index), float(eps_low), float(eps_high), float(denominator), _ptr(per_token),
