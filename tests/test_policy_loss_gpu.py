@@ -99,6 +99,13 @@ def test_policy_loss_nothing_valid_and_repeatable():
     ptl, clip, out, g = _run(lp, old, adv, t, V, 0.2, 0.2)
     assert int(out[1]) == 0 and out[0] == 0 and np.isnan(out[3])
     assert np.all(g == 0) and np.all(ptl == 0) and not clip.any()
+    # an empty batch of tokens: sums and counts 0, the mean NaN (0 / 0), or 0 over a
+    # positive normaliser
+    e = np.zeros(0, np.float32)
+    ptl, clip, out, g = _run(e, e, e, np.zeros(0, np.int64), V, 0.2, 0.2)
+    assert ptl.size == 0 and g.size == 0 and list(out[:3]) == [0, 0, 0] and np.isnan(out[3])
+    _, _, out, _ = _run(e, e, e, np.zeros(0, np.int64), V, 0.2, 0.2, den=64.0)
+    assert out[3] == 0.0
     lp, old, adv, t = _draw(7, 100003, V)
     a = _run(lp, old, adv, t, V, 0.2, 0.28)
     b = _run(lp, old, adv, t, V, 0.2, 0.28)
@@ -131,8 +138,8 @@ def test_policy_loss_gradient_through_backward():
     g_ref = ref.policy_loss_grad(o["logprob"], old_h.astype(np.float64), adv_h.astype(np.float64),
                                  c.targets, c.V, c.ignore_index, 0.2, 0.28, n)
     rdX, rdW = ref.backward(c.X, c.W, c.targets, c.ignore_index, c.scale, g_ref, None)
-    # the clip decisions of the two sides agree (log-probs differ by < 2e-3 only where
-    # no ratio sits that close to a boundary: checked, not assumed)
+    # the two sides take the same clip decisions: their log-probs differ by far less
+    # than any ratio's distance to a clip boundary in this case (asserted, not assumed)
     gg = g.cpu().numpy()
     assert np.array_equal(gg == 0, g_ref == 0)
     gu.check_grads(gu.bf16_to_np(dX), gu.bf16_to_np(dW), rdX, rdW, "policy_e2e")
