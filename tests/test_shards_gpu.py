@@ -170,3 +170,31 @@ def test_shards_full_size_against_golden(cfg, n_shards):
     got_dw = gu.bf16_to_np(dW.index_select(0, vrows))
     gu.check_grads(got_dx, got_dw, g["dx"], g["dw"], f"config{cfg} x{n_shards}")
     assert bool(torch.isfinite(dXp).all()) and bool(torch.isfinite(dW).all())
+
+
+def _random_splits(n=8, seed=20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M, H, V = int(rng.integers(1, 900)), int(8 * rng.integers(1, 60)), int(rng.integers(2, 4000))
+        P = int(rng.integers(2, min(V, 9) + 1))
+        offsets = [0] + sorted(set(int(x) for x in rng.integers(1, V, P - 1))) + [V]
+        mode = str(rng.choice(["inv_m", "normal", "normal_lp"]))
+        out.append((i, M, H, V, offsets, mode, float(rng.choice([1.0, 1 / 0.7, -0.5]))))
+    return out
+
+
+@pytest.mark.parametrize("spec", _random_splits(), ids=lambda s: f"r{s[0]}_M{s[1]}_V{s[3]}_P{len(s[4]) - 1}")
+def test_random_shard_splits(spec):
+    """Seeded random shapes split at random vocabulary boundaries (shards of any width,
+    down to one column), against the oracle on the whole vocabulary."""
+    i, M, H, V, offsets, mode, scale = spec
+    c = inputs.make_case(f"rsh{i}", 210 + i, M, H, V, scale=scale, grad_mode=mode,
+                         compute_entropy=True, ignore_frac=0.05)
+    print(f"[shards] random {spec}", flush=True)
+    lp, lse, ent, dXp, dW = run_sharded(c, offsets)
+    o = ref.forward(c.X, c.W, c.targets, c.ignore_index, c.scale, True)
+    rdX, rdW = ref.backward(c.X, c.W, c.targets, c.ignore_index, c.scale, c.grad_logprob,
+                            c.grad_entropy)
+    gu.check_forward(dict(logprob=_np(lp), lse=_np(lse), entropy=_np(ent)), o, True, f"rsh{i}")
+    gu.check_grads(_np(dXp), gu.bf16_to_np(dW), rdX, rdW, f"rsh{i}")
