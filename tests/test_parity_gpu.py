@@ -174,3 +174,37 @@ def test_grad_zero_sum_property():
     res = gu.run_flce(c)
     dW = res["dW"]
     assert np.abs(dW.sum(0)).max() <= 2e-2 * np.abs(dW).sum(0).max()
+
+
+@pytest.mark.parametrize("how", ["scale_zero", "weight_zero"])
+def test_uniform_softmax_closed_forms(how):
+    """Every logit 0 (scale 0, or W = 0): the softmax is uniform, so on valid rows
+    lse = entropy = ln V and logprob = -ln V; ignored rows give 0.  With scale 0 both
+    gradients vanish exactly (every d-logit carries a factor of the scale); with W = 0, dX
+    vanishes exactly and dW = dz^T X is checked against the oracle.  The vocabulary is
+    ragged (1500 and 700 columns), so the masked tail of the last tile must stay out of
+    the sums however the scale treats it."""
+    import math
+    if how == "scale_zero":
+        c = inputs.make_case("uniform_s0", 122, 600, 136, 1500, scale=0.0, ignore_frac=0.1,
+                             grad_mode="normal")
+    else:
+        c = inputs.make_case("uniform_w0", 123, 300, 64, 700, ignore_frac=0.1, grad_mode="normal")
+        c.W = np.zeros_like(c.W)
+    print(f"[parity] uniform {how} M={c.M} H={c.H} V={c.V}", flush=True)
+    res = gu.run_flce(c)
+    valid = ref.valid_rows(c.targets, c.V, c.ignore_index)
+    assert 0 < valid.sum() < c.M
+    lnV = math.log(c.V)
+    np.testing.assert_allclose(res["lse"], lnV, rtol=0, atol=2e-6)
+    np.testing.assert_allclose(res["logprob"][valid], -lnV, rtol=0, atol=2e-6)
+    np.testing.assert_allclose(res["entropy"][valid], lnV, rtol=0, atol=2e-6)
+    assert np.all(res["logprob"][~valid] == 0.0) and np.all(res["entropy"][~valid] == 0.0)
+    assert np.all(res["dX"] == 0.0)
+    if how == "scale_zero":
+        assert np.all(res["dW"] == 0.0)
+    else:
+        o, dX, dW = _oracle(c)
+        assert np.all(dX == 0.0) and np.max(np.abs(dW)) > 0
+        gu.check_forward(res, o, True, "uniform_w0")
+        gu.check_grads(res["dX"], res["dW"], dX, dW, "uniform_w0")
