@@ -208,3 +208,19 @@ def test_uniform_softmax_closed_forms(how):
         assert np.all(dX == 0.0) and np.max(np.abs(dW)) > 0
         gu.check_forward(res, o, True, "uniform_w0")
         gu.check_grads(res["dX"], res["dW"], dX, dW, "uniform_w0")
+
+
+@pytest.mark.parametrize("col", [0, 255, 256, 1299])
+def test_every_target_in_one_column(col):
+    """Every valid row targets the same vocabulary column (the first, the edges of the
+    first 256-column tile, the last column of a ragged last tile): the target-logit
+    correction of the d-logits, rare on random targets, is taken by every row of every
+    tile that holds that column."""
+    c = inputs.make_case("one_col", 124, 700, 128, 1300, ignore_frac=0.05, grad_mode="normal")
+    valid = ref.valid_rows(c.targets, c.V, c.ignore_index)
+    c.targets = np.where(valid, col, c.targets).astype(np.int64)
+    print(f"[parity] one column {col} M={c.M} H={c.H} V={c.V}", flush=True)
+    res = gu.run_flce(c)
+    o, dX, dW = _oracle(c)
+    gu.check_forward(res, o, True, f"one_col{col}")
+    gu.check_grads(res["dX"], res["dW"], dX, dW, f"one_col{col}")
