@@ -224,3 +224,29 @@ def test_every_target_in_one_column(col):
     o, dX, dW = _oracle(c)
     gu.check_forward(res, o, True, f"one_col{col}")
     gu.check_grads(res["dX"], res["dW"], dX, dW, f"one_col{col}")
+
+
+def test_targets_beyond_32_bits_are_not_valid():
+    """Targets are 64-bit: values whose low 32 bits name a vocabulary column
+    (2^32 + 5, -2^32 + 7, 2^63 - 1, -2^63) are out of range, so those rows are ignored
+    by the forward, the backward and the scalar NLL reduction alike."""
+    import torch
+    from log_prob_amd import flce
+    c = inputs.make_case("t64", 125, 400, 64, 900, grad_mode="normal")
+    big = np.array([2**32 + 5, -2**32 + 7, 2**63 - 1, -2**63], dtype=np.int64)
+    rows = np.array([0, 1, 255, 399])
+    c.targets[rows] = big
+    print(f"[parity] 64-bit targets M={c.M} H={c.H} V={c.V}", flush=True)
+    res = gu.run_flce(c)
+    o, dX, dW = _oracle(c)
+    assert not ref.valid_rows(c.targets, c.V, c.ignore_index)[rows].any()
+    gu.check_forward(res, o, True, "t64")
+    gu.check_grads(res["dX"], res["dW"], dX, dW, "t64")
+    assert np.all(res["logprob"][rows] == 0) and np.all(res["entropy"][rows] == 0)
+    assert np.all(res["dX"][rows] == 0)
+    lp = torch.from_numpy(res["logprob"].astype(np.float32)).cuda()
+    red = flce.nll_reduce(lp, torch.from_numpy(c.targets).cuda(), c.V, c.ignore_index)
+    total, n, _ = ref.nll_reduce(res["logprob"].astype(np.float64), c.targets, c.V, c.ignore_index)
+    r = red.cpu().numpy()
+    assert int(r[1]) == n == c.M - len(rows)
+    assert r[0] == pytest.approx(total, rel=1e-12)
