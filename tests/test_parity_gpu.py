@@ -250,3 +250,15 @@ def test_targets_beyond_32_bits_are_not_valid():
     r = red.cpu().numpy()
     assert int(r[1]) == n == c.M - len(rows)
     assert r[0] == pytest.approx(total, rel=1e-12)
+
+
+@pytest.mark.parametrize("H", [16384, 65544])
+def test_long_hidden_dimension(H):
+    """K loops of 256 and 1025 steps (65544 = 1024 * 64 + 8: a last K step with a single
+    16-byte chunk of each row), with ragged M and V, against the oracle."""
+    c = inputs.make_case("long_h", 126, 100, H, 300, ignore_frac=0.05, grad_mode="normal")
+    print(f"[parity] long H M={c.M} H={c.H} V={c.V}", flush=True)
+    res = gu.run_flce(c)
+    o, dX, dW = _oracle(c)
+    gu.check_forward(res, o, True, f"long_h{H}")
+    gu.check_grads(res["dX"], res["dW"], dX, dW, f"long_h{H}")
