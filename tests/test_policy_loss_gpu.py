@@ -143,3 +143,17 @@ def test_policy_loss_gradient_through_backward():
     gg = g.cpu().numpy()
     assert np.array_equal(gg == 0, g_ref == 0)
     gu.check_grads(gu.bf16_to_np(dX), gu.bf16_to_np(dW), rdX, rdW, "policy_e2e")
+
+
+def test_policy_loss_targets_beyond_32_bits():
+    """Targets whose low 32 bits name a vocabulary column but which lie outside [0, V)
+    as 64-bit values leave their tokens out of the loss, the counts and the gradient."""
+    V = 50257
+    lp, old, adv, t = _draw(8, 4000, V)
+    rows = np.array([0, 17, 2047, 3999])
+    t[rows] = np.array([2**32 + 5, -2**32 + 7, 2**63 - 1, -2**63], dtype=np.int64)
+    print("[policy] 64-bit targets", flush=True)
+    out = _check(lp, old, adv, t, V, 0.2, 0.28, 0.0, "t64")
+    assert int(out[1]) == int(np.sum((t != IGN) & (t >= 0) & (t < V)))
+    ptl, _, _, g = _run(lp, old, adv, t, V, 0.2, 0.28)
+    assert np.all(ptl[rows] == 0) and np.all(g[rows] == 0)
