@@ -106,9 +106,16 @@ def from_logits(Z: np.ndarray, t: np.ndarray, ignore_index: int, compute_entropy
     return out
 
 
-def row_block(V: int, budget_bytes: int = 1 << 29) -> int:
+# Bytes of one [rows, V] float64 logit block.  Only the memory footprint depends on it:
+# rows are independent, so the blocks' results are the rows' results.  The pins force
+# small values so that every row loop runs over many blocks.
+ROW_BLOCK_BYTES = 1 << 29
+
+
+def row_block(V: int, budget_bytes=None) -> int:
     """Rows per block so that one [rows, V] float64 block stays within the budget."""
-    return max(1, int(budget_bytes // (8 * max(V, 1))))
+    b = ROW_BLOCK_BYTES if budget_bytes is None else budget_bytes
+    return max(1, int(b // (8 * max(V, 1))))
 
 
 def forward_f64(Xd, Wd, t, ignore_index, scale, compute_entropy=True):
@@ -207,16 +214,22 @@ def dw_rows(X_bits, W_bits, t, vrows, ignore_index, scale, lse, E,
     Xd = decode_bf16(X_bits)
     M = Xd.shape[0]
     V = W_bits.shape[0]
-    Wv = decode_bf16(W_bits[vrows])
     s = float(np.float64(np.float32(scale)))
     t = np.asarray(t, np.int64)
     valid = valid_rows(t, V, ignore_index)
     a, b = _ab(np.arange(M), valid, grad_logprob, grad_entropy)
-    Zc = logits(Xd, Wv, scale)                      # [M, len(vrows)]
-    Pc = np.exp(Zc - np.asarray(lse)[:, None])
-    onehot = (t[:, None] == vrows[None, :]) & valid[:, None]
-    dZc = a[:, None] * (onehot - Pc) + b[:, None] * Pc * (np.asarray(E)[:, None] - Zc)
-    return s * (dZc.T @ Xd)
+    lse = np.asarray(lse, np.float64)
+    E = np.asarray(E, np.float64)
+    out = np.zeros((len(vrows), Xd.shape[1]))
+    step = row_block(M)                             # entries per [M, entries] block
+    for i in range(0, len(vrows), step):
+        vb = vrows[i:i + step]
+        Zc = logits(Xd, decode_bf16(W_bits[vb]), scale)   # [M, len(vb)]
+        Pc = np.exp(Zc - lse[:, None])
+        onehot = (t[:, None] == vb[None, :]) & valid[:, None]
+        dZc = a[:, None] * (onehot - Pc) + b[:, None] * Pc * (E[:, None] - Zc)
+        out[i:i + step] = s * (dZc.T @ Xd)
+    return out
 
 
 def nll_reduce(logprob, t, V, ignore_index):

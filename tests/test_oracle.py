@@ -75,6 +75,43 @@ def _bits(x):
     return inputs.f32_to_bf16_bits(np.asarray(x, np.float32))
 
 
+def test_row_blocks_many_against_one_and_brute_force(monkeypatch):
+    """Every block loop of the oracle (rows of the forward, the backward and dx_rows;
+    vocabulary entries of dw_rows) run over many small blocks gives the single-block
+    results and the pure-Python brute force's.  A loop that overwrote instead of
+    accumulating, or wrote a block to the wrong rows, fails here."""
+    M, H, V = 8, 6, 11
+    X, W, t, s, glp, gent = _tiny_problem(5, M=M, H=H, V=V)
+    rows = np.array([6, 0, 7, 3, 2])
+    vrows = np.array([10, 0, 4, 5, 9, 1, int(t[0])])
+
+    def run():
+        o = ref.forward(X, W, t, -100, s, True)
+        dX, dW = ref.backward(X, W, t, -100, s, glp, gent)
+        dxr = ref.dx_rows(X, W, t, rows, -100, s, glp, gent)
+        dwr = ref.dw_rows(X, W, t, vrows, -100, s, o["lse"], o["E"], glp, gent)
+        return o, dX, dW, dxr, dwr
+
+    one = run()
+    assert ref.row_block(V) >= M and ref.row_block(M) >= len(vrows)
+    monkeypatch.setattr(ref, "ROW_BLOCK_BYTES", 8 * max(M, V) * 2)   # 2 rows / entries per block
+    assert ref.row_block(V) == 2 and ref.row_block(M) == 2
+    many = run()
+    Xl = [[brute.bf16_to_float(v) for v in row] for row in X]
+    Wl = [[brute.bf16_to_float(v) for v in row] for row in W]
+    bf = brute.solve(Xl, Wl, [int(v) for v in t], -100, s, [float(g) for g in glp],
+                     [float(g) for g in gent])
+    bdX, bdW = np.array(bf["dX"]), np.array(bf["dW"])
+    for res in (one, many):
+        o, dX, dW, dxr, dwr = res
+        for k in ("lse", "logprob", "entropy"):
+            np.testing.assert_allclose(o[k], bf[k], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dX, bdX, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dW, bdW, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dxr, bdX[rows], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dwr, bdW[vrows], rtol=0, atol=1e-13)
+
+
 def test_closed_forms_through_linear_head():
     """Uniform and two-level logits built from crafted bf16 X and W."""
     # W = 0: every logit is 0 -> lse = log V, logprob = -log V, entropy = log V

@@ -43,6 +43,14 @@ MUTANTS = {
     "scale_not_applied": ("return s * (Xd @ Wd.T)", "return Xd @ Wd.T"),
     "valid_ignores_range": ("return (t != ignore_index) & (t >= 0) & (t < V)",
                             "return (t != ignore_index)"),
+    # mistakes that only a run over several row blocks can show
+    "dw_block_overwrites": ("dW += s * (dZ.T @ Xr)", "dW = s * (dZ.T @ Xr)"),
+    "dx_rows_block_misplaced": ("out[i:i + step] = s * (o[\"dZ\"] @ Wd)",
+                                "out[:len(r)] = s * (o[\"dZ\"] @ Wd)"),
+    "forward_block_skips_tail": ("for r0 in range(0, M, step):\n        r = slice(r0, min(M, r0 + step))",
+                                 "for r0 in range(0, M - step, step):\n        r = slice(r0, min(M, r0 + step))"),
+    "dw_rows_block_misplaced": ("out[i:i + step] = s * (dZc.T @ Xd)",
+                                "out[:len(vb)] = s * (dZc.T @ Xd)"),
 }
 
 
@@ -108,7 +116,34 @@ def _pin_torch(ref):
     assert np.allclose(dW, Wt.grad.numpy(), atol=1e-10)
 
 
-PINS = [_pin_closed_forms, _pin_brute, _pin_zero_sum, _pin_torch]
+def _pin_blocked(ref):
+    """The row loops over many small blocks against the brute force."""
+    M, H, V = 8, 6, 11
+    X, W, t, s, glp, gent = pins._tiny_problem(5, M=M, H=H, V=V)
+    saved = ref.ROW_BLOCK_BYTES
+    ref.ROW_BLOCK_BYTES = 8 * max(M, V) * 2       # 2 rows / vocabulary entries per block
+    try:
+        rows = np.array([6, 0, 7, 3, 2])
+        vrows = np.array([10, 0, 4, 5, 9, 1])
+        o = ref.forward(X, W, t, -100, s, True)
+        dX, dW = ref.backward(X, W, t, -100, s, glp, gent)
+        dxr = ref.dx_rows(X, W, t, rows, -100, s, glp, gent)
+        dwr = ref.dw_rows(X, W, t, vrows, -100, s, o["lse"], o["E"], glp, gent)
+    finally:
+        ref.ROW_BLOCK_BYTES = saved
+    Xl = [[brute.bf16_to_float(v) for v in row] for row in X]
+    Wl = [[brute.bf16_to_float(v) for v in row] for row in W]
+    bf = brute.solve(Xl, Wl, [int(v) for v in t], -100, s, list(map(float, glp)),
+                     list(map(float, gent)))
+    for k in ("lse", "logprob", "entropy"):
+        assert np.allclose(o[k], bf[k], atol=1e-10, rtol=0)
+    bdX, bdW = np.array(bf["dX"]), np.array(bf["dW"])
+    assert np.allclose(dX, bdX, atol=1e-10, rtol=0) and np.allclose(dW, bdW, atol=1e-10, rtol=0)
+    assert np.allclose(dxr, bdX[rows], atol=1e-10, rtol=0)
+    assert np.allclose(dwr, bdW[vrows], atol=1e-10, rtol=0)
+
+
+PINS = [_pin_closed_forms, _pin_brute, _pin_zero_sum, _pin_torch, _pin_blocked]
 
 
 def test_pins_pass_on_real_oracle():
