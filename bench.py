@@ -136,7 +136,11 @@ def copy_probe(mib):
 
 
 def cpu_baseline(case, rows_req):
-    """Time the fp64 oracle (forward + backward) on the first R tokens of the workload."""
+    """Time the fp64 oracle (forward, then backward) on the first R tokens of the workload.
+
+    The oracle's forward forms the logits of the R rows (2RHV fp64 FLOP); its backward
+    forms them again, then dX and dW (6RHV): 8RHV performed in all, the same count as
+    the GPU step's four classifier GEMMs."""
     from oracle import flce_ref as ref
     M, H, V = case.M, case.H, case.V
     Wd = ref.decode_bf16(case.W)
@@ -145,28 +149,35 @@ def cpu_baseline(case, rows_req):
     _run_oracle_rows(ref, case, Wd, 8)
     R = rows_req if rows_req > 0 else 64
     while True:
-        t0 = time.perf_counter()
-        _run_oracle_rows(ref, case, Wd, R)
-        dt = time.perf_counter() - t0
+        tf, tb = _run_oracle_rows(ref, case, Wd, R)
+        dt = tf + tb
         if rows_req > 0 or dt >= 10.0 or R >= M:
             break
         R = int(min(M, max(R + 1, R * min(8.0, 15.0 / max(dt, 1e-3)))))
-    flops = 8.0 * R * H * V
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _CORES, "kind": "oracle",
-            "sample": f"fp64 NumPy oracle, forward + backward of the first {R} of {M} tokens "
-                      f"(H={H}, V={V}, full vocabulary), {dt:.1f} s wall; rate counted as "
-                      f"8*R*H*V like the GPU step (the oracle itself does 6*R*H*V, no recompute)"}
+    rhv = float(R) * H * V
+    return {"value": 8.0 * rhv / dt / 1e12, "unit": "TFLOP/s", "cores": _CORES,
+            "kind": "oracle",
+            "sample": f"fp64 NumPy oracle on the first {R} of {M} tokens (H={H}, V={V}, full "
+                      f"vocabulary): forward {tf:.1f} s (2RHV fp64 FLOP: the logits) + backward "
+                      f"{tb:.1f} s (6RHV: the logits again, dX, dW); value = the 8RHV fp64 FLOP "
+                      f"performed / {dt:.1f} s",
+            "forward_tflops": 2.0 * rhv / tf / 1e12,
+            "backward_tflops": 6.0 * rhv / tb / 1e12,
+            "step_equivalent_s": dt * M / R}
 
 
 def _run_oracle_rows(ref, case, Wd, R):
+    """Seconds of the oracle's forward and of its backward over the first R rows."""
     rows = np.arange(R)
-    o = ref.forward_rows(case.X, case.W, case.targets, rows, case.ignore_index, case.scale,
-                         case.compute_entropy, Wd=Wd)
+    t0 = time.perf_counter()
+    ref.forward_rows(case.X, case.W, case.targets, rows, case.ignore_index, case.scale,
+                     case.compute_entropy, Wd=Wd)
+    t1 = time.perf_counter()
     Xd = ref.decode_bf16(case.X[:R])
     glp = None if case.grad_logprob is None else case.grad_logprob[:R]
     gent = None if case.grad_entropy is None else case.grad_entropy[:R]
-    dX, dW = ref.backward_f64(Xd, Wd, case.targets[:R], case.ignore_index, case.scale, glp, gent)
-    return o, dX, dW
+    ref.backward_f64(Xd, Wd, case.targets[:R], case.ignore_index, case.scale, glp, gent)
+    return t1 - t0, time.perf_counter() - t1
 
 
 def main():
@@ -252,6 +263,21 @@ def main():
     for _ in range(2):
         fwd()
     fwd_ms = float(np.median(timed(fwd, max(args.steps, 5))))
+    # the same step with an entropy gradient as well: grad_entropy = N(0,1)/M
+    ent_grad = None
+    if ent and gent is None:
+        gen = torch.Generator(device=dev).manual_seed(2026)
+        gent_v = torch.randn(M, device=dev, dtype=torch.float32, generator=gen) / M
+
+        def step_entgrad():
+            fwd()
+            flce.backward(X, W, t, lse, entropy, glp, gent_v, case.ignore_index, case.scale,
+                          workspace=ws, out=(dX, dW))
+        step_entgrad()
+        eg_ms = float(np.median(timed(step_entgrad, max(args.steps, 5))))
+        ent_grad = {"ms": round(eg_ms, 4),
+                    "tflops": round(8.0 * M * H * V / (eg_ms * 1e-3) / 1e12, 2),
+                    "grad_entropy": "N(0,1)/M"}
     # token waves: the same forward with a workspace that holds 4096-row waves of partials
     wave_rows = min(4096, -(-M // 256) * 256)
     ws_wave = torch.empty(flce.forward_workspace_min(M, H, V, ent) * (wave_rows // 256),
@@ -330,6 +356,10 @@ def main():
         "fwd_tflops": round(tf_f, 2),
         "fwd_pct_peak": round(100.0 * tf_f / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed": round(wall, 3),
+        "fwd_bwd_with_grad_entropy": ent_grad,
+        "fwd_workspace_bytes": fwd_b,
+        "bwd_workspace_bytes": bwd_b,
+        "bwd_chunk_cols": flce.backward_chunk_cols(M, H, V, bwd_b),
         "fwd_token_waves": {"wave_rows": wave_rows, "ms": round(fwd_wave_ms, 4),
                             "tflops": round(flop_f / (fwd_wave_ms * 1e-3) / 1e12, 2),
                             "workspace_bytes": int(ws_wave.numel()), "full_workspace_bytes": fwd_b},

@@ -74,24 +74,48 @@ typedef enum {
  * Workspace bytes needed by flce_forward (*fwd_bytes) and the preferred size for
  * flce_backward (*bwd_bytes) for this problem shape.  One buffer of
  * max(*fwd_bytes, *bwd_bytes) serves both.  Either output pointer may be NULL.
- * Sizes: 1 <= M < 2^31, 1 <= H < 2^20 with H % 8 == 0, 1 <= V < 2^31.
+ * Sizes accepted by every call: 0 <= M <= 2^30 (M = 0 is an empty batch),
+ * 8 <= H <= 2^20 with H % 8 == 0, 1 <= V <= 2^30, and at most 2^31 - 1 workgroups
+ * per launch (ceil(M / 256) * ceil(V / 256) and ceil(V / 256) * ceil(H / 256)).
+ * Negative M, or H or V <= 0: FLCE_ERR_INVALID_VALUE; larger sizes, or H not a
+ * multiple of 8: FLCE_ERR_UNSUPPORTED.
  */
 flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_entropy,
                                    size_t* fwd_bytes, size_t* bwd_bytes);
 
 /*
- * Smallest workspace flce_backward accepts.  The backward walks the vocabulary
- * in chunks whose width it derives from the workspace it is given: the
- * preferred size holds up to 4 GiB of bf16 d-logits per chunk (every column at once
- * when they fit), the minimum holds one tile
- * column (256 vocabulary entries) per chunk plus an fp32 dX accumulator.
- * Results differ between chunk widths only by fp32 summation order in dX.
+ * Backward workspace.  The backward runs in token waves and vocabulary chunks whose
+ * sizes it derives from the workspace it is given (the token-wave scheduling of the
+ * Liger-Kernel commit "native Blackwell tensor-parallel fused scaled linear
+ * cross-entropy", sections "Summary", "Implementation / Backward" and "Correctness":
+ * dW stored by the first wave and added to by later ones; Liger-Kernel PR 1294,
+ * "Kernel design notes": d-logits in the input dtype in a reusable buffer).  The
+ * workspace holds the bf16 d-logits of one wave over one chunk; an fp32 dX
+ * accumulator for one wave's rows when a wave takes more than one chunk; and, when
+ * there is more than one wave, an fp32 dW accumulator of V x H.  The preferred size
+ * (*bwd_bytes of flce_workspace_query) is one wave of every row with up to 4 GiB of
+ * d-logits per chunk (every column at once when they fit).  With less, the call
+ * takes the schedule that fits and moves the fewest extra bytes: narrower chunks, or
+ * waves of 256 to 16384 rows.  The minimum is the smallest of: one wave with
+ * 256-column chunks (d-logits + fp32 dX accumulator of M rows), one wave with every
+ * column (d-logits only), 256-row waves with 256-column chunks or with every column
+ * (+ the fp32 dW accumulator): once M > 256 it is at most 4 V H + 1024 H + 131072
+ * bytes (each part rounded up to 256 bytes), whatever M.  Results of different
+ * schedules differ only by fp32
+ * summation order (dX across chunks, dW across waves); every schedule is
+ * deterministic.
  */
 flce_status_t flce_backward_workspace_min(int64_t M, int64_t H, int64_t V, size_t* bytes);
 
-/* Chunk width (vocabulary columns) flce_backward would use with this workspace. */
+/* Chunk width (vocabulary columns) flce_backward would use with this workspace;
+ * FLCE_ERR_WORKSPACE_TOO_SMALL below the minimum. */
 flce_status_t flce_backward_chunk_cols(int64_t M, int64_t H, int64_t V, size_t workspace_bytes,
                                        int64_t* chunk_cols);
+
+/* Token rows per wave flce_backward would use with this workspace (a multiple of 256;
+ * M rounded up to 256 means one wave); FLCE_ERR_WORKSPACE_TOO_SMALL below the minimum. */
+flce_status_t flce_backward_wave_rows(int64_t M, int64_t H, int64_t V, size_t workspace_bytes,
+                                      int64_t* rows);
 
 /*
  * Smallest workspace flce_forward accepts, and the wave height it uses with a given
@@ -205,9 +229,10 @@ flce_status_t flce_forward_merge_shards(const int64_t* targets, int64_t M, int64
                                         float* entropy, const void* gathered,
                                         size_t shard_stride_bytes, struct ihipStream_t* stream);
 
-/* Workspace bytes for flce_backward_shard: the minimum (one 256-column d-logit
- * chunk) and the preferred size (up to 4 GiB of bf16 d-logits per chunk).
- * Either output may be NULL. */
+/* Workspace bytes for flce_backward_shard: the minimum and the preferred size, as
+ * for flce_backward but without a dX accumulator (dX_partial is the caller's fp32
+ * buffer): d-logits of one wave over one chunk, plus the fp32 dW_shard accumulator
+ * when the rows run in more than one wave.  Either output may be NULL. */
 flce_status_t flce_backward_shard_workspace_query(int64_t M, int64_t H, int64_t V_shard,
                                                   size_t* min_bytes, size_t* preferred_bytes);
 

@@ -3,6 +3,7 @@
 // enqueues nothing and needs no device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -99,14 +100,100 @@ int64_t wave_rows_for_workspace(int64_t M, int64_t V, bool ent, size_t bytes) {
   return lo * kTile;
 }
 
-size_t bwd_bytes_for_chunk(int64_t M, int64_t H, int64_t V, int64_t chunk) {
+// The backward's schedule: token waves of `rows` rows (a multiple of 256; rows >= Mpad
+// is one wave of every row) and vocabulary chunks of `chunk` columns.  The workspace
+// holds the bf16 d-logits of one wave's chunk, then, when a wave takes more than one
+// chunk and dX is bf16, the fp32 dX accumulator of one wave, then, when there is more
+// than one wave, the fp32 dW accumulator of the whole vocabulary (dW of wave 0 is
+// stored into it, later waves add, the last one writes bf16): the token-wave form of
+// the backward in the Liger-Kernel commit "native Blackwell tensor-parallel fused
+// scaled linear cross-entropy", sections "Implementation / Backward" and "Correctness".
+struct BwdPlan {
+  int64_t rows = 0, chunk = 0;
+  bool dx_acc = false, dw_acc = false;
+  size_t off_dx = 0, off_dw = 0, total = 0;
+};
+
+BwdPlan bwd_plan(int64_t M, int64_t H, int64_t V, int64_t rows, int64_t chunk, bool dx_bf16) {
   const int64_t Mpad = cdiv(M, kTile) * kTile;
   const int64_t Vpad = cdiv(V, kTile) * kTile;
-  size_t b = align_up(size_t(Mpad) * size_t(chunk) * 2);
-  if (chunk < Vpad) b += align_up(size_t(M) * size_t(H) * sizeof(float));
-  return b;
+  BwdPlan p;
+  p.rows = rows < Mpad ? rows : Mpad;
+  p.chunk = chunk;
+  const int64_t wave_m = p.rows < M ? p.rows : M;  // token rows of the largest wave
+  size_t b = align_up(size_t(p.rows) * size_t(chunk) * 2);
+  p.dx_acc = dx_bf16 && chunk < Vpad;
+  if (p.dx_acc) {
+    p.off_dx = b;
+    b += align_up(size_t(wave_m) * size_t(H) * sizeof(float));
+  }
+  p.dw_acc = p.rows < Mpad;
+  if (p.dw_acc) {
+    p.off_dw = b;
+    b += align_up(size_t(V) * size_t(H) * sizeof(float));
+  }
+  p.total = b;
+  return p;
 }
 
+// Widest chunk (a multiple of 256, at most min(Vpad, kMaxChunk)) for waves of `rows`
+// rows whose plan fits in `bytes`; 0 if none.
+int64_t widest_chunk(int64_t M, int64_t H, int64_t V, int64_t rows, bool dx_bf16, size_t bytes) {
+  const int64_t Vpad = cdiv(V, kTile) * kTile;
+  if (Vpad <= kMaxChunk && bwd_plan(M, H, V, rows, Vpad, dx_bf16).total <= bytes) return Vpad;
+  // narrower chunks: the size grows with the chunk from here on
+  const BwdPlan p0 = bwd_plan(M, H, V, rows, kTile, dx_bf16);
+  if (p0.total > bytes) return 0;
+  const size_t fixed = p0.total - align_up(size_t(p0.rows) * size_t(kTile) * 2);
+  int64_t c = int64_t((bytes - fixed) / (size_t(p0.rows) * 2)) / kTile * kTile;
+  const int64_t cap = (Vpad <= kMaxChunk ? Vpad - kTile : kMaxChunk);
+  if (c > cap) c = cap;
+  while (c > kTile && bwd_plan(M, H, V, rows, c, dx_bf16).total > bytes) c -= kTile;
+  return c >= kTile ? c : 0;
+}
+
+// HBM bytes a plan moves beyond the d-logits themselves, plus its launches (10 us each,
+// at 8 TB/s): the fp32 dX accumulator is read and written once per extra chunk, the
+// fp32 dW accumulator once per extra wave.  Used only to rank plans that fit.
+double plan_cost(int64_t M, int64_t H, int64_t V, const BwdPlan& p) {
+  const int64_t Vpad = cdiv(V, kTile) * kTile;
+  const double n_chunks = double(cdiv(Vpad, p.chunk)), n_waves = double(cdiv(M, p.rows));
+  double c = 3.0 * 80e6 * n_chunks * n_waves;
+  if (p.chunk < Vpad) c += (n_chunks - 1.0) * 8.0 * double(M) * double(H);
+  if (p.dw_acc) c += (n_waves - 1.0) * 8.0 * double(V) * double(H);
+  return c;
+}
+
+// The schedule flce_backward (dx_bf16) or flce_backward_shard runs with `bytes` of
+// workspace: one wave of every row with the widest chunk that fits, or, when that
+// costs more (or does not fit), waves of 256 to 16384 rows with the fp32 dW
+// accumulator, whichever moves the fewest extra bytes; total 0 if nothing fits.
+BwdPlan plan_for_workspace(int64_t M, int64_t H, int64_t V, bool dx_bf16, size_t bytes) {
+  const int64_t Mpad = cdiv(M, kTile) * kTile;
+  BwdPlan best;
+  if (Mpad == 0) {  // no token: nothing is staged
+    const int64_t Vpad = cdiv(V, kTile) * kTile;
+    best.chunk = Vpad < kMaxChunk ? Vpad : kMaxChunk;
+    return best;
+  }
+  double best_cost = 0.0;
+  auto consider = [&](int64_t rows) {
+    const int64_t c = widest_chunk(M, H, V, rows, dx_bf16, bytes);
+    if (c == 0) return;
+    const BwdPlan p = bwd_plan(M, H, V, rows, c, dx_bf16);
+    const double cost = plan_cost(M, H, V, p);
+    if (best.total == 0 || cost < best_cost) {
+      best = p;
+      best_cost = cost;
+    }
+  };
+  consider(Mpad);  // one wave of every row
+  for (int64_t rows = 16384; rows >= kTile; rows /= 2)
+    if (rows < Mpad) consider(rows);
+  return best;
+}
+
+// Preferred chunk: the d-logits of one wave of every row within kDzBudget.
 int64_t preferred_chunk(int64_t M, int64_t V) {
   const int64_t Mpad = cdiv(M, kTile) * kTile;
   const int64_t Vpad = cdiv(V, kTile) * kTile;
@@ -117,19 +204,17 @@ int64_t preferred_chunk(int64_t M, int64_t V) {
   return c < Vpad ? c : Vpad;
 }
 
-// Widest chunk (multiple of 256, at most Vpad) whose buffers fit in `bytes`; 0 if none.
-int64_t chunk_for_workspace(int64_t M, int64_t H, int64_t V, size_t bytes) {
+// Smallest workspace any schedule fits in (independent of M once waves are possible).
+size_t bwd_min_bytes(int64_t M, int64_t H, int64_t V, bool dx_bf16) {
   const int64_t Mpad = cdiv(M, kTile) * kTile;
   const int64_t Vpad = cdiv(V, kTile) * kTile;
-  if (Mpad == 0) return Vpad < kMaxChunk ? Vpad : kMaxChunk;  // nothing is staged
-  if (Vpad <= kMaxChunk && bwd_bytes_for_chunk(M, H, V, Vpad) <= bytes) return Vpad;
-  const size_t acc = align_up(size_t(M) * size_t(H) * sizeof(float));
-  if (bytes <= acc) return 0;
-  int64_t c = int64_t((bytes - acc) / (size_t(Mpad) * 2)) / kTile * kTile;
-  if (c > kMaxChunk) c = kMaxChunk;
-  while (c >= kTile && bwd_bytes_for_chunk(M, H, V, c) > bytes) c -= kTile;
-  if (c >= Vpad) c = Vpad - kTile;
-  return c >= kTile ? c : 0;
+  size_t m = bwd_plan(M, H, V, Mpad, kTile, dx_bf16).total;
+  if (Vpad <= kMaxChunk) m = std::min(m, bwd_plan(M, H, V, Mpad, Vpad, dx_bf16).total);
+  if (Mpad > kTile) {
+    m = std::min(m, bwd_plan(M, H, V, kTile, kTile, dx_bf16).total);
+    if (Vpad <= kMaxChunk) m = std::min(m, bwd_plan(M, H, V, kTile, Vpad, dx_bf16).total);
+  }
+  return m;
 }
 
 flce_status_t hip_fail(hipError_t e, const char* what) {
@@ -183,7 +268,8 @@ flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_
   flce_status_t st = check_shape(M, H, V);
   if (st != FLCE_OK) return st;
   if (fwd_bytes) *fwd_bytes = fwd_layout(M, V, compute_entropy == 1).total;
-  if (bwd_bytes) *bwd_bytes = bwd_bytes_for_chunk(M, H, V, preferred_chunk(M, V));
+  if (bwd_bytes)
+    *bwd_bytes = bwd_plan(M, H, V, cdiv(M, kTile) * kTile, preferred_chunk(M, V), true).total;
   return ok();
 }
 
@@ -221,7 +307,7 @@ flce_status_t flce_backward_workspace_min(int64_t M, int64_t H, int64_t V, size_
   flce_status_t st = check_shape(M, H, V);
   if (st != FLCE_OK) return st;
   if (!bytes) return fail(FLCE_ERR_INVALID_VALUE, "bytes is NULL");
-  *bytes = bwd_bytes_for_chunk(M, H, V, kTile);
+  *bytes = bwd_min_bytes(M, H, V, true);
   return ok();
 }
 
@@ -230,11 +316,24 @@ flce_status_t flce_backward_chunk_cols(int64_t M, int64_t H, int64_t V, size_t w
   flce_status_t st = check_shape(M, H, V);
   if (st != FLCE_OK) return st;
   if (!chunk_cols) return fail(FLCE_ERR_INVALID_VALUE, "chunk_cols is NULL");
-  const int64_t c = chunk_for_workspace(M, H, V, workspace_bytes);
-  if (c == 0)
+  const BwdPlan p = plan_for_workspace(M, H, V, true, workspace_bytes);
+  if (p.chunk == 0)
     return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the minimum %zu",
-                workspace_bytes, bwd_bytes_for_chunk(M, H, V, kTile));
-  *chunk_cols = c;
+                workspace_bytes, bwd_min_bytes(M, H, V, true));
+  *chunk_cols = p.chunk;
+  return ok();
+}
+
+flce_status_t flce_backward_wave_rows(int64_t M, int64_t H, int64_t V, size_t workspace_bytes,
+                                      int64_t* rows) {
+  flce_status_t st = check_shape(M, H, V);
+  if (st != FLCE_OK) return st;
+  if (!rows) return fail(FLCE_ERR_INVALID_VALUE, "rows is NULL");
+  const BwdPlan p = plan_for_workspace(M, H, V, true, workspace_bytes);
+  if (p.chunk == 0)
+    return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the minimum %zu",
+                workspace_bytes, bwd_min_bytes(M, H, V, true));
+  *rows = p.rows;
   return ok();
 }
 
@@ -441,32 +540,33 @@ flce_status_t flce_forward_merge(const int64_t* targets, int64_t M, int64_t H, i
   return ok();
 }
 
-flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets, int64_t M,
-                           int64_t H, int64_t V, int64_t ignore_index, float scale,
-                           int compute_entropy, float* logprob, float* lse, float* entropy,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (M == 0) return check_empty(H, V, compute_entropy);
-  if (!X || !W || !targets || !logprob || !lse || !workspace)
-    return fail(FLCE_ERR_INVALID_VALUE,
-                "NULL pointer among X, W, targets, logprob, lse, workspace");
+}  // extern "C"
+
+namespace {
+
+// Checks of a forward call's arguments other than the workspace.
+flce_status_t check_forward_call(const void* X, const void* W, const int64_t* targets,
+                                 int64_t M, int64_t H, int64_t V, float scale,
+                                 int compute_entropy, const float* logprob, const float* lse,
+                                 const float* entropy) {
+  if (!X || !W || !targets || !logprob || !lse)
+    return fail(FLCE_ERR_INVALID_VALUE, "NULL pointer among X, W, targets, logprob, lse");
   flce_status_t st = check_shape(M, H, V);
   if (st != FLCE_OK) return st;
   if (compute_entropy != 0 && compute_entropy != 1)
     return fail(FLCE_ERR_INVALID_VALUE, "compute_entropy must be 0 or 1");
   if (!aligned(targets, 8)) return fail(FLCE_ERR_UNSUPPORTED, "targets must be 8-byte aligned");
-  if (!aligned(workspace, kAlign))
-    return fail(FLCE_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   st = check_forward_inputs(X, W, scale);
   if (st != FLCE_OK) return st;
-  st = check_forward_outputs(compute_entropy, logprob, lse, entropy);
-  if (st != FLCE_OK) return st;
-  const bool ent = compute_entropy == 1;
-  // token waves: as many 256-row tiles per wave as the workspace holds partials for
-  const int64_t rows = wave_rows_for_workspace(M, V, ent, workspace_bytes);
-  if (rows == 0)
-    return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "forward needs at least %zu workspace bytes, got %zu",
-                fwd_layout(kTile, V, ent).total, workspace_bytes);
-  char* ws = static_cast<char*>(workspace);
+  return check_forward_outputs(compute_entropy, logprob, lse, entropy);
+}
+
+// The forward in token waves of `rows` rows (a multiple of 256) through the workspace ws:
+// per wave, the tile kernel, the target logits and the merge.
+flce_status_t forward_waves(const void* X, const void* W, const int64_t* targets, int64_t M,
+                            int64_t H, int64_t V, int64_t ignore_index, float scale, bool ent,
+                            float* logprob, float* lse, float* entropy, char* ws, int64_t rows,
+                            hipStream_t stream) {
   for (int64_t r0 = 0; r0 < M; r0 += rows) {
     const int64_t mw = M - r0 < rows ? M - r0 : rows;
     const FwdLayout L = fwd_layout(mw, V, ent);
@@ -484,6 +584,31 @@ flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets,
     if (e != hipSuccess) return hip_fail(e, "forward merge kernel launch");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets, int64_t M,
+                           int64_t H, int64_t V, int64_t ignore_index, float scale,
+                           int compute_entropy, float* logprob, float* lse, float* entropy,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (M == 0) return check_empty(H, V, compute_entropy);
+  flce_status_t st = check_forward_call(X, W, targets, M, H, V, scale, compute_entropy, logprob,
+                                        lse, entropy);
+  if (st != FLCE_OK) return st;
+  if (!workspace) return fail(FLCE_ERR_INVALID_VALUE, "workspace is NULL");
+  if (!aligned(workspace, kAlign))
+    return fail(FLCE_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const bool ent = compute_entropy == 1;
+  // token waves: as many 256-row tiles per wave as the workspace holds partials for
+  const int64_t rows = wave_rows_for_workspace(M, V, ent, workspace_bytes);
+  if (rows == 0)
+    return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "forward needs at least %zu workspace bytes, got %zu",
+                fwd_layout(kTile, V, ent).total, workspace_bytes);
+  return forward_waves(X, W, targets, M, H, V, ignore_index, scale, ent, logprob, lse, entropy,
+                       static_cast<char*>(workspace), rows, stream);
 }
 
 }  // extern "C"
@@ -507,98 +632,102 @@ flce_status_t check_backward_inputs(const void* X, const void* W, const int64_t*
   return FLCE_OK;
 }
 
-// The backward over vocabulary chunks of `chunk` columns of W (rows v_off .. v_off + V - 1
-// of a vocabulary of V_total ids).  dX goes either to dX_bf16 (through the fp32
-// accumulator `acc` in the workspace when there is more than one chunk) or, when
-// dX_bf16 is NULL, to the caller's fp32 `acc`, which it overwrites (acc_in false) or
-// adds to (acc_in true).
-flce_status_t backward_chunks(const void* X, const void* W, const int64_t* targets, int64_t M,
-                              int64_t H, int64_t V, int64_t v_off, int64_t V_total,
-                              int64_t ignore_index, float scale, const float* lse,
-                              const float* entropy, const float* grad_logprob,
-                              const float* grad_entropy, uint16_t* dX_bf16, float* acc,
-                              bool acc_in, void* dW, uint16_t* dz, int64_t chunk,
-                              hipStream_t stream) {
-  const int64_t n_mt = cdiv(M, kTile), Mpad = n_mt * kTile;
+// The backward under plan P: W holds rows v_off .. v_off + V - 1 of a vocabulary of
+// V_total ids.  For each token wave and each vocabulary chunk: the d-logits of the
+// wave's rows over the chunk, the chunk's rows of dW (K = the wave's rows) and the
+// wave's rows of dX (K = the chunk's columns).  dX goes either to dX_bf16 (through the
+// wave's fp32 accumulator in the workspace when a wave takes more than one chunk) or,
+// when dX_bf16 is NULL, to the caller's fp32 dX_f32, which it overwrites (acc_in false)
+// or adds to (acc_in true).  With more than one wave dW accumulates in fp32 in the
+// workspace across waves in wave order (deterministic), and the last wave writes bf16.
+flce_status_t backward_run(const void* X, const void* W, const int64_t* targets, int64_t M,
+                           int64_t H, int64_t V, int64_t v_off, int64_t V_total,
+                           int64_t ignore_index, float scale, const float* lse,
+                           const float* entropy, const float* grad_logprob,
+                           const float* grad_entropy, uint16_t* dX_bf16, float* dX_f32,
+                           bool acc_in, void* dW, char* ws, const BwdPlan& P,
+                           hipStream_t stream) {
   const int64_t Vpad = cdiv(V, kTile) * kTile;
-  const int64_t n_chunks = cdiv(Vpad, chunk);
+  const int64_t n_chunks = cdiv(Vpad, P.chunk);
+  const int64_t n_waves = cdiv(M, P.rows);
   const bool entgrad = grad_entropy != nullptr;
-  for (int64_t c = 0; c < n_chunks; ++c) {
-    const int64_t vbase = c * chunk;
-    const int64_t kc = (Vpad - vbase) < chunk ? (Vpad - vbase) : chunk;
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws);
+  float* dx_acc = P.dx_acc ? reinterpret_cast<float*>(ws + P.off_dx) : nullptr;
+  float* dw_acc = P.dw_acc ? reinterpret_cast<float*>(ws + P.off_dw) : nullptr;
+  const uint16_t* Xb = static_cast<const uint16_t*>(X);
+  for (int64_t w = 0; w < n_waves; ++w) {
+    const int64_t r0 = w * P.rows;
+    const int64_t mw = (M - r0) < P.rows ? (M - r0) : P.rows;
+    const int64_t n_mt = cdiv(mw, kTile);
+    for (int64_t c = 0; c < n_chunks; ++c) {
+      const int64_t vbase = c * P.chunk;
+      const int64_t kc = (Vpad - vbase) < P.chunk ? (Vpad - vbase) : P.chunk;
 
-    flce::DlogitsArgs d{};
-    d.X = static_cast<const uint16_t*>(X);
-    d.W = static_cast<const uint16_t*>(W);
-    d.targets = targets;
-    d.M = int(M);
-    d.H = int(H);
-    d.V = int(V);
-    d.v_off = v_off;
-    d.V_total = V_total;
-    d.ignore_index = ignore_index;
-    d.scale = scale;
-    d.lse = lse;
-    d.entropy = entropy;
-    d.grad_logprob = grad_logprob;
-    d.grad_entropy = grad_entropy;
-    d.vbase = int(vbase);
-    d.n_mt = int(n_mt);
-    d.n_vt = int(kc / kTile);
-    d.dz = dz;
-    d.ldz = long(chunk);
-    hipError_t e = flce::launch_dlogits(d, entgrad, stream);
-    if (e != hipSuccess) return hip_fail(e, "d-logits kernel launch");
+      flce::DlogitsArgs d{};
+      d.X = Xb + r0 * H;
+      d.W = static_cast<const uint16_t*>(W);
+      d.targets = targets + r0;
+      d.M = int(mw);
+      d.H = int(H);
+      d.V = int(V);
+      d.v_off = v_off;
+      d.V_total = V_total;
+      d.ignore_index = ignore_index;
+      d.scale = scale;
+      d.lse = lse + r0;
+      d.entropy = entropy ? entropy + r0 : nullptr;
+      d.grad_logprob = grad_logprob ? grad_logprob + r0 : nullptr;
+      d.grad_entropy = grad_entropy ? grad_entropy + r0 : nullptr;
+      d.vbase = int(vbase);
+      d.n_mt = int(n_mt);
+      d.n_vt = int(kc / kTile);
+      d.dz = dz;
+      d.ldz = long(P.chunk);
+      hipError_t e = flce::launch_dlogits(d, entgrad, stream);
+      if (e != hipSuccess) return hip_fail(e, "d-logits kernel launch");
 
-    flce::GemmDwArgs w{};
-    w.dz = dz;
-    w.ldz = long(chunk);
-    w.X = static_cast<const uint16_t*>(X);
-    w.dW = static_cast<uint16_t*>(dW);
-    w.M = int(M);
-    w.Mpad = int(Mpad);
-    w.H = int(H);
-    w.V = int(V);
-    w.vbase = int(vbase);
-    w.chunk_cols = int(kc);
-    w.n_i = int(kc / kTile);
-    w.n_h = int(cdiv(H, kTile));
-    e = flce::launch_gemm_dw(w, stream);
-    if (e != hipSuccess) return hip_fail(e, "dW GEMM launch");
+      flce::GemmDwArgs g{};
+      g.dz = dz;
+      g.ldz = long(P.chunk);
+      g.X = Xb + r0 * H;
+      g.dW = static_cast<uint16_t*>(dW);
+      g.acc = dw_acc;
+      g.M = int(mw);
+      g.Mpad = int(n_mt * kTile);
+      g.H = int(H);
+      g.V = int(V);
+      g.vbase = int(vbase);
+      g.chunk_cols = int(kc);
+      g.n_i = int(kc / kTile);
+      g.n_h = int(cdiv(H, kTile));
+      g.mode = n_waves == 1 ? 0 : (w == 0 ? 1 : (w == n_waves - 1 ? 3 : 2));
+      e = flce::launch_gemm_dw(g, stream);
+      if (e != hipSuccess) return hip_fail(e, "dW GEMM launch");
 
-    flce::GemmDxArgs x{};
-    x.dz = dz;
-    x.ldz = long(chunk);
-    x.W = static_cast<const uint16_t*>(W);
-    x.acc = acc;
-    x.dX = dX_bf16;
-    x.M = int(M);
-    x.H = int(H);
-    x.V = int(V);
-    x.vbase = int(vbase);
-    x.kcols = int(kc);
-    x.n_m = int(n_mt);
-    x.n_h = int(cdiv(H, kTile));
-    if (dX_bf16)
-      x.mode = n_chunks == 1 ? 0 : (c == 0 ? 1 : (c == n_chunks - 1 ? 3 : 2));
-    else
-      x.mode = (c == 0 && !acc_in) ? 1 : 2;
-    e = flce::launch_gemm_dx(x, stream);
-    if (e != hipSuccess) return hip_fail(e, "dX GEMM launch");
+      flce::GemmDxArgs x{};
+      x.dz = dz;
+      x.ldz = long(P.chunk);
+      x.W = static_cast<const uint16_t*>(W);
+      x.dX = dX_bf16 ? dX_bf16 + r0 * H : nullptr;
+      x.M = int(mw);
+      x.H = int(H);
+      x.V = int(V);
+      x.vbase = int(vbase);
+      x.kcols = int(kc);
+      x.n_m = int(n_mt);
+      x.n_h = int(cdiv(H, kTile));
+      if (dX_bf16) {
+        x.acc = dx_acc;
+        x.mode = n_chunks == 1 ? 0 : (c == 0 ? 1 : (c == n_chunks - 1 ? 3 : 2));
+      } else {
+        x.acc = dX_f32 + r0 * H;
+        x.mode = (c == 0 && !acc_in) ? 1 : 2;
+      }
+      e = flce::launch_gemm_dx(x, stream);
+      if (e != hipSuccess) return hip_fail(e, "dX GEMM launch");
+    }
   }
   return ok();
-}
-
-// Widest d-logit chunk (a multiple of 256, at most the padded shard width) that fits
-// `bytes` when the workspace holds nothing else; 0 if none.
-int64_t shard_chunk_for_workspace(int64_t M, int64_t V, size_t bytes) {
-  const int64_t Mpad = cdiv(M, kTile) * kTile;
-  const int64_t Vpad = cdiv(V, kTile) * kTile;
-  int64_t c = int64_t(bytes / (size_t(Mpad) * 2)) / kTile * kTile;
-  if (c > kMaxChunk) c = kMaxChunk;
-  if (c > Vpad) c = Vpad;
-  while (c >= kTile && align_up(size_t(Mpad) * size_t(c) * 2) > bytes) c -= kTile;
-  return c >= kTile ? c : 0;
 }
 
 }  // namespace
@@ -618,10 +747,10 @@ flce_status_t flce_backward(const void* X, const void* W, const int64_t* targets
   st = check_backward_inputs(X, W, targets, scale, lse, entropy, grad_logprob, grad_entropy, dX,
                              dW, workspace);
   if (st != FLCE_OK) return st;
-  const int64_t chunk = chunk_for_workspace(M, H, V, workspace_bytes);
-  if (chunk == 0)
+  const BwdPlan P = plan_for_workspace(M, H, V, true, workspace_bytes);
+  if (P.chunk == 0)
     return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "backward needs at least %zu workspace bytes, got %zu",
-                bwd_bytes_for_chunk(M, H, V, kTile), workspace_bytes);
+                bwd_min_bytes(M, H, V, true), workspace_bytes);
 
   if (!grad_logprob && !grad_entropy) {
     hipError_t e = flce::launch_fill_zero_u16(static_cast<uint16_t*>(dX), long(M * H), stream);
@@ -630,17 +759,9 @@ flce_status_t flce_backward(const void* X, const void* W, const int64_t* targets
     if (e != hipSuccess) return hip_fail(e, "zero-fill kernel launch");
     return ok();
   }
-
-  const int64_t Mpad = cdiv(M, kTile) * kTile;
-  const int64_t Vpad = cdiv(V, kTile) * kTile;
-  char* ws = static_cast<char*>(workspace);
-  uint16_t* dz = reinterpret_cast<uint16_t*>(ws);
-  float* acc = chunk < Vpad
-                   ? reinterpret_cast<float*>(ws + align_up(size_t(Mpad) * size_t(chunk) * 2))
-                   : nullptr;
-  return backward_chunks(X, W, targets, M, H, V, 0, V, ignore_index, scale, lse, entropy,
-                         grad_logprob, grad_entropy, static_cast<uint16_t*>(dX), acc, false, dW,
-                         dz, chunk, stream);
+  return backward_run(X, W, targets, M, H, V, 0, V, ignore_index, scale, lse, entropy,
+                      grad_logprob, grad_entropy, static_cast<uint16_t*>(dX), nullptr, false, dW,
+                      static_cast<char*>(workspace), P, stream);
 }
 
 flce_status_t flce_backward_shard_workspace_query(int64_t M, int64_t H, int64_t V_shard,
@@ -648,9 +769,9 @@ flce_status_t flce_backward_shard_workspace_query(int64_t M, int64_t H, int64_t 
   flce_status_t st = check_shape(M, H, V_shard);
   if (st != FLCE_OK) return st;
   const int64_t Mpad = cdiv(M, kTile) * kTile;
-  if (min_bytes) *min_bytes = align_up(size_t(Mpad) * size_t(kTile) * 2);
+  if (min_bytes) *min_bytes = bwd_min_bytes(M, H, V_shard, false);
   if (preferred_bytes)
-    *preferred_bytes = align_up(size_t(Mpad) * size_t(preferred_chunk(M, V_shard)) * 2);
+    *preferred_bytes = bwd_plan(M, H, V_shard, Mpad, preferred_chunk(M, V_shard), false).total;
   return ok();
 }
 
@@ -682,11 +803,11 @@ flce_status_t flce_backward_shard(const void* X, const void* W_shard, const int6
   st = check_backward_inputs(X, W_shard, targets, scale, lse, entropy, grad_logprob,
                              grad_entropy, dX_partial, dW_shard, workspace);
   if (st != FLCE_OK) return st;
-  const int64_t chunk = shard_chunk_for_workspace(M, V_shard, workspace_bytes);
-  if (chunk == 0)
+  const BwdPlan P = plan_for_workspace(M, H, V_shard, false, workspace_bytes);
+  if (P.chunk == 0)
     return fail(FLCE_ERR_WORKSPACE_TOO_SMALL,
                 "shard backward needs at least %zu workspace bytes, got %zu",
-                align_up(size_t(cdiv(M, kTile) * kTile) * size_t(kTile) * 2), workspace_bytes);
+                bwd_min_bytes(M, H, V_shard, false), workspace_bytes);
 
   if (!grad_logprob && !grad_entropy) {
     hipError_t e = flce::launch_fill_zero_u16(static_cast<uint16_t*>(dW_shard),
@@ -697,10 +818,9 @@ flce_status_t flce_backward_shard(const void* X, const void* W_shard, const int6
     if (e != hipSuccess) return hip_fail(e, "zero-fill kernel launch");
     return ok();
   }
-  return backward_chunks(X, W_shard, targets, M, H, V_shard, v_offset, V_total, ignore_index,
-                         scale, lse, entropy, grad_logprob, grad_entropy, nullptr, dX_partial,
-                         accumulate == 1, dW_shard, static_cast<uint16_t*>(workspace), chunk,
-                         stream);
+  return backward_run(X, W_shard, targets, M, H, V_shard, v_offset, V_total, ignore_index,
+                      scale, lse, entropy, grad_logprob, grad_entropy, nullptr, dX_partial,
+                      accumulate == 1, dW_shard, static_cast<char*>(workspace), P, stream);
 }
 
 flce_status_t flce_nll_reduce(const float* logprob, const int64_t* targets, int64_t M,

@@ -77,12 +77,14 @@ struct DlogitsArgs {
 struct GemmDwArgs {
   const uint16_t* dz;   // bf16 Mpad x ldz, tile-blocked (256-row bands of 256 x 64 blocks)
   long ldz;
-  const uint16_t* X;    // bf16 [M, H]
+  const uint16_t* X;    // bf16 [M, H]: the token rows of dz
   uint16_t* dW;         // bf16 [V, H]
+  float* acc;           // fp32 [V, H] accumulator across token waves (modes 1-3)
   int M, Mpad, H, V;
   int vbase;
   int chunk_cols;       // padded width of the chunk (multiple of 256)
   int n_i, n_h;         // tiles along the chunk and along H
+  int mode;             // 0 write bf16, 1 write acc, 2 add to acc, 3 add and write bf16
 };
 
 struct GemmDxArgs {

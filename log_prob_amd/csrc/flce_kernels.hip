@@ -50,32 +50,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NTHREADS = 256;    // 4 waves of 64 in a 2 x 2 grid over the workgroup tile
-// Pipeline options (tuning builds may override the defaults).
-#ifndef FLCE_SCHED_PIPE
-#define FLCE_SCHED_PIPE 1
-#endif
-#ifndef FLCE_FENCE_BARRIER
-#define FLCE_FENCE_BARRIER 1
-#endif
-#ifndef FLCE_LOAD_GROUPS
-#define FLCE_LOAD_GROUPS 16
-#endif
-#ifndef FLCE_LOAD_EARLY
-#define FLCE_LOAD_EARLY -1
-#endif
-
 // Pin the instruction order of a sub-step: the fragment reads of sub-step kk + 1
 // alternate with the first MFMAs of sub-step kk, so each read is issued a whole
 // sub-step before its first use.  Left to itself the scheduler reuses fragment
 // registers right after their last MFMA and issues each read only one MFMA group
 // ahead, exposing the LDS latency.
-constexpr bool SCHED_PIPE = FLCE_SCHED_PIPE != 0;
+constexpr bool SCHED_PIPE = true;
 // A stage's loads are issued in LOAD_GROUPS groups per MFMA sub-step (at most one
-// group per MFMA), placed between the sub-step's MFMA groups: LOAD_EARLY of them (by
-// default half) under the last sub-step of the step before, the others under
-// sub-step 0.
-constexpr int LOAD_GROUPS = FLCE_LOAD_GROUPS;
-constexpr int LOAD_EARLY = FLCE_LOAD_EARLY;
+// group per MFMA), placed between the sub-step's MFMA groups: half of them under the
+// last sub-step of the step before (right after the barrier that frees their stage),
+// the others under sub-step 0.  Measured best: 16 groups and half early (8 groups
+// tie; 4 or 12 early loads cost 1.5-3%).
+constexpr int LOAD_GROUPS = 16;
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // beyond every descriptor's num_records
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format
 
@@ -108,23 +94,14 @@ struct Shape {
                 "whole loads per wave");
   static_assert(NST >= 2 && NST <= 4, "stages");
 };
-#ifndef FLCE_BIG_BK
-#define FLCE_BIG_BK 64
-#endif
-#ifndef FLCE_BIG_NST
-#define FLCE_BIG_NST 2
-#endif
 // One workgroup per CU: 256 x 256 tiles, waves of 128 x 128, 128 KiB of LDS stages.
-using BigShape = Shape<256, 256, FLCE_BIG_BK, FLCE_BIG_NST, 1>;
+using BigShape = Shape<256, 256, 64, 2, 1>;
 // The forward runs BigShape.  Eight waves of 128 x 64 (two per SIMD, Shape<256, 256,
 // 64, 2, 2, 2, 4>) hide more stalls but read 1.5x the LDS; with the lean K loop they
 // measured 5% slower.
 using FwdShape = BigShape;
 static_assert(FwdShape::TM == kFwdTileM && FwdShape::TN == kFwdTileN, "host and kernel tile");
-#ifndef FLCE_FWD_GROUP_M
-#define FLCE_FWD_GROUP_M (2048 / kFwdTileM)
-#endif
-constexpr int FWD_GROUP_M = FLCE_FWD_GROUP_M;  // forward tile rows per L2 group
+constexpr int FWD_GROUP_M = 2048 / kFwdTileM;  // forward tile rows per L2 group
 
 // The backward kernels run BigShape; their epilogues stage a 256 x 256 bf16 output
 // tile (128 KiB) in the LDS the pipeline used.
@@ -599,7 +576,7 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
                                          const TileSrc& A, const TileSrc& B, int K) {
   static_assert(S::NST == 2, "two LDS stages");
   constexpr int KK = S::KK, D = S::DMA_STAGE;
-  constexpr int EARLY = LOAD_EARLY < 0 ? D / 2 : (LOAD_EARLY < D ? LOAD_EARLY : D);
+  constexpr int EARLY = D / 2;
   constexpr int F = S::MB * S::NB, GR = LOAD_GROUPS < F ? LOAD_GROUPS : F;
   static_assert(EARLY > 0 && EARLY < 64, "early loads");
   static_assert(KK % 2 == 0, "sub-step 0 of every stage uses register set 0");
@@ -663,10 +640,8 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[S::MB][S::NB], char* smem
       mfma_block<S::MB, S::NB>(acc, af[kk & 1], bfr[kk & 1]);
       sched_substep<S, A_KC, B_KC, true>();
     }
-#if FLCE_FENCE_BARRIER
     // keep the barrier after every MFMA issued so far (the compiler would hoist it)
     __builtin_amdgcn_sched_barrier(0);
-#endif
     wait_vmcnt<0>();
     __syncthreads();
     // stage kt is free now: it receives step kt + 2 (after the last step this reads
@@ -1094,7 +1069,8 @@ __global__ __launch_bounds__(64 * TL_ROWS) void target_logit_kernel(FwdTileArgs 
 }
 
 // Merge of the per-tile partials of each row: m* = max m_j, S = sum s_j e^(m_j - m*),
-// U = sum e^(m_j - m*) (u_j + (m_j - m*) s_j); lse = m* + log S, entropy = log S - U / S.
+// U = sum e^(m_j - m*) (u_j + (m_j - m*) s_j); lse = m* + log S,
+// logprob = min(z_t - lse, 0), entropy = max(log S - U / S, 0).
 // The tiles j run over every shard of the table in order (one shard when the
 // vocabulary is not split); the target logit comes from the shard that owns the target.
 // A workgroup takes MERGE_ROWS rows; its MERGE_SLICES waves split each row's tiles
@@ -1154,8 +1130,14 @@ __global__ __launch_bounds__(MERGE_ROWS * MERGE_SLICES) void fwd_merge_kernel(Fw
     zt = p.base[p.sh.zt[r] + row];
   }
   p.lse[row] = ms + logS;
-  p.logprob[row] = valid ? zt - (ms + logS) : 0.f;
-  if constexpr (ENT) p.entropy[row] = valid ? logS - U / S : 0.f;
+  // A log-probability is at most 0 and an entropy at least 0.  When one logit holds
+  // nearly all of a row's probability both values sit next to that bound, and fp32
+  // rounding can put them a few ulps past it: the target logit (its own dot product)
+  // and lse (from the MFMA accumulators) round differently, and the shifted sum of the
+  // row's maximum element can come out a hair above 0.  The bounds are applied
+  // exactly, which only moves a value towards the true one.
+  p.logprob[row] = valid ? fminf(zt - (ms + logS), 0.f) : 0.f;
+  if constexpr (ENT) p.entropy[row] = valid ? fmaxf(logS - U / S, 0.f) : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -1307,7 +1289,83 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// The fp32 side of an output tile (modes 1-3), for dX across vocabulary chunks and dW
+// across token waves.  t.acc and t.out point at the tile's element (0, 0) of an fp32
+// accumulator and of the bf16 result, both with leading dimension t.ld; rows
+// [0, t.nrows) and columns [0, t.ncols) of the tile exist.  Each wave moves its
+// 128 x 128 block through a private 32 KiB LDS slice, 64 rows at a time, so the fp32
+// accumulator is read and written in 16-byte pieces (a half-wave covers 512 contiguous
+// bytes of a row) and all of a lane's loads of a slice are in flight together;
+// per-element accesses in the accumulator layout would wait on one read-modify-write
+// after another.  Slice layout: row r (0..63) at 512 r bytes, column c at float
+// (c ^ 32 ((r >> 2) & 1)), so the two half-waves of a staging write (rows r and r + 4)
+// fall on different banks.
+// mode 1: acc = v; mode 2: acc += v; mode 3: out = bf16(acc + v).
+struct F32Tile {
+  float* acc;
+  uint16_t* out;
+  long ld;
+  int nrows, ncols;
+  int mode;
+};
+
+__device__ __forceinline__ void tile_f32(const f32x16 (&acc)[4][4], char* smem, const F32Tile& t,
+                                         int wave, int lane) {
+  const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
+  float* sl = reinterpret_cast<float*>(smem + wave * 32768);
+  const int lc = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = 32 * mi + acc_row(lane, e);  // (r >> 2) & 1 == hi
+          sl[r * 128 + ((32 * nb + lc) ^ (hi << 5))] = acc_read(acc[2 * s + mi][nb][e]);
+        }
+    __syncthreads();
+    const int rb = wr0 + 64 * s, cb = wc0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // granule g = 64 it + lane: row g / 32, columns 4 (g % 32) .. + 3
+      float4 old[16];
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int g = 64 * (16 * half + it) + lane, r = g >> 5, c = 4 * (g & 31);
+        const int m = rb + r, h = cb + c;
+        old[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t.mode != 1 && m < t.nrows && h < t.ncols)
+          old[it] = *reinterpret_cast<const float4*>(t.acc + (long)m * t.ld + h);
+      }
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int g = 64 * (16 * half + it) + lane, r = g >> 5, c = 4 * (g & 31);
+        const int m = rb + r, h = cb + c;
+        const float4 v = *reinterpret_cast<const float4*>(sl + r * 128 + (c ^ (((r >> 2) & 1) << 5)));
+        const float4 u = t.mode == 1 ? v
+                                     : make_float4(old[it].x + v.x, old[it].y + v.y,
+                                                   old[it].z + v.z, old[it].w + v.w);
+        if (m < t.nrows && h < t.ncols) {
+          if (t.mode == 3) {
+            const f32x2 lo = {u.x, u.y}, hi2 = {u.z, u.w};
+            const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+            const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2));
+            *reinterpret_cast<uint2*>(t.out + (long)m * t.ld + h) = make_uint2(a, b);
+          } else {
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, u),
+                                        reinterpret_cast<u32x4*>(t.acc + (long)m * t.ld + h));
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // dW[vbase + i, h] = sum_m dzs[m, i] X[m, h]: A = dzs^T (MN), B = X^T (MN), K = Mpad.
+// mode 0: write bf16; 1-3: the fp32 accumulator across token waves (see tile_f32).
 __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
   int ti, th;
@@ -1326,72 +1384,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
   const int rows = min(min(TILE, p.chunk_cols - i0), p.V - (p.vbase + i0));
-  store_acc_bf16(smem, acc, wr0, wc0, lane, p.dW + (long)(p.vbase + i0) * p.H + h0, p.H, rows,
-                 p.H - h0);
-}
-
-// The fp32 side of a dX tile (modes 1-3).  Each wave moves its 128 x 128 block through
-// a private 32 KiB LDS slice, 64 rows at a time, so the fp32 accumulator is read and
-// written in 16-byte pieces (a half-wave covers 512 contiguous bytes of a row) and all
-// of a lane's loads of a slice are in flight together; per-element accesses in the
-// accumulator layout would wait on one read-modify-write after another.  Slice layout:
-// row r (0..63) at 512 r bytes, column c at float (c ^ 32 ((r >> 2) & 1)), so the two
-// half-waves of a staging write (rows r and r + 4) fall on different banks.
-// mode 1: acc = v; mode 2: acc += v; mode 3: dX = bf16(acc + v).
-__device__ __forceinline__ void dx_tile_f32(const f32x16 (&acc)[4][4], char* smem,
-                                            const GemmDxArgs& p, int m0, int h0, int wave,
-                                            int lane) {
-  const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
-  float* sl = reinterpret_cast<float*>(smem + wave * 32768);
-  const int lc = lane & 31, hi = lane >> 5;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = 32 * mi + acc_row(lane, e);  // (r >> 2) & 1 == hi
-          sl[r * 128 + ((32 * nb + lc) ^ (hi << 5))] = acc_read(acc[2 * s + mi][nb][e]);
-        }
-    __syncthreads();
-    const int rb = m0 + wr0 + 64 * s, cb = h0 + wc0;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // granule g = 64 it + lane: row g / 32, columns 4 (g % 32) .. + 3
-      float4 old[16];
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int g = 64 * (16 * half + it) + lane, r = g >> 5, c = 4 * (g & 31);
-        const int m = rb + r, h = cb + c;
-        old[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (p.mode != 1 && m < p.M && h < p.H)
-          old[it] = *reinterpret_cast<const float4*>(p.acc + (long)m * p.H + h);
-      }
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int g = 64 * (16 * half + it) + lane, r = g >> 5, c = 4 * (g & 31);
-        const int m = rb + r, h = cb + c;
-        const float4 v = *reinterpret_cast<const float4*>(sl + r * 128 + (c ^ (((r >> 2) & 1) << 5)));
-        const float4 t = p.mode == 1 ? v
-                                     : make_float4(old[it].x + v.x, old[it].y + v.y,
-                                                   old[it].z + v.z, old[it].w + v.w);
-        if (m < p.M && h < p.H) {
-          if (p.mode == 3) {
-            const f32x2 lo = {t.x, t.y}, hi2 = {t.z, t.w};
-            const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
-            const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2));
-            *reinterpret_cast<uint2*>(p.dX + (long)m * p.H + h) = make_uint2(a, b);
-          } else {
-            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, t),
-                                        reinterpret_cast<u32x4*>(p.acc + (long)m * p.H + h));
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
+  const long o = (long)(p.vbase + i0) * p.H + h0;
+  if (p.mode == 0)
+    store_acc_bf16(smem, acc, wr0, wc0, lane, p.dW + o, p.H, rows, p.H - h0);
+  else
+    tile_f32(acc, smem, F32Tile{p.acc + o, p.dW + o, p.H, rows, p.H - h0, p.mode}, wave, lane);
 }
 
 // dX[m, h] (+)= sum_i dzs[m, i] W[vbase + i, h]: A = dzs (KC), B = W^T (MN), K = kcols.
@@ -1417,7 +1414,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
     store_acc_bf16(smem, acc, wr0, wc0, lane, p.dX + (long)m0 * p.H + h0, p.H, p.M - m0,
                    p.H - h0);
   } else {
-    dx_tile_f32(acc, smem, p, m0, h0, wave, lane);
+    const long o = (long)m0 * p.H + h0;
+    tile_f32(acc, smem, F32Tile{p.acc + o, p.dX + o, p.H, p.M - m0, p.H - h0, p.mode}, wave,
+             lane);
   }
 }
 

@@ -26,6 +26,22 @@ def bf16_to_np(t):
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def to_np(t):
+    """Any torch tensor -> float64 numpy."""
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def bf16_bits(t):
+    """bf16 torch tensor -> its uint16 bit patterns as numpy."""
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bits_to_np(bits):
+    """bf16 bit patterns (uint16 numpy) -> float64 numpy (exact)."""
+    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
 def run_flce(case, fwd_ws=None, bwd_ws=None, need_backward=True):
     """Forward (+ backward) through the C ABI; returns numpy float64 results."""
     import torch

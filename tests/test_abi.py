@@ -273,3 +273,41 @@ def test_empty_batch_needs_no_device():
     # the empty backward must write dW = 0, so it needs dW (checked before any launch)
     assert _bwd(lib, M=0, dW=None) == 1
     assert _bwd(lib, M=0, dW=18) == 2
+
+
+def test_size_limits_match_the_header():
+    """Each edge of the documented size limits: 0 <= M <= 2^30, 8 <= H <= 2^20 with
+    H % 8 == 0, 1 <= V <= 2^30."""
+    lib = flce.load()
+    fb, bb = ctypes.c_size_t(), ctypes.c_size_t()
+
+    def q(M, H, V):
+        return lib.flce_workspace_query(M, H, V, 1, ctypes.byref(fb), ctypes.byref(bb))
+    assert q(0, 8, 1) == 0
+    assert q(1 << 30, 8, 1) == 0 and q((1 << 30) + 1, 8, 1) == 2
+    assert q(1, 1 << 20, 1) == 0 and q(1, (1 << 20) + 8, 1) == 2
+    assert q(1, 8, 1 << 30) == 0 and q(1, 8, (1 << 30) + 1) == 2
+    assert q(-1, 8, 1) == 1 and q(1, 0, 1) == 1 and q(1, 8, 0) == 1
+    assert q(1, 4, 1) == 2 and q(1, 12, 1) == 2
+    # more than 2^31 - 1 workgroups of 256 x 256 tiles
+    assert q(1 << 30, 8, 1 << 18) == 2
+
+
+@pytest.mark.parametrize("M,H,V", [(4096, 4096, 512), (4097, 64, 1000), (600, 136, 3000),
+                                   (8192, 8192, 131072), (32767, 2048, 151936), (1, 8, 1),
+                                   ((1 << 20) + 1, 64, 512)])
+def test_backward_schedule_sizes(M, H, V):
+    """The smallest backward workspace is never above the preferred one, is accepted
+    (and one byte less is not), and the preferred size runs every row in one wave."""
+    Mpad = -(-M // 256) * 256
+    lo = flce.backward_workspace_min(M, H, V)
+    _, pref = flce.workspace_query(M, H, V, True)
+    assert lo <= pref
+    assert flce.backward_wave_rows(M, H, V, pref) == Mpad
+    rows = flce.backward_wave_rows(M, H, V, lo)
+    assert rows % 256 == 0 and 256 <= rows <= Mpad
+    assert flce.backward_chunk_cols(M, H, V, lo) % 256 == 0
+    with pytest.raises(flce.FlceError):
+        flce.backward_wave_rows(M, H, V, lo - 1)
+    with pytest.raises(flce.FlceError):
+        flce.backward_chunk_cols(M, H, V, lo - 1)

@@ -262,3 +262,82 @@ def test_long_hidden_dimension(H):
     o, dX, dW = _oracle(c)
     gu.check_forward(res, o, True, f"long_h{H}")
     gu.check_grads(res["dX"], res["dW"], dX, dW, f"long_h{H}")
+
+
+def test_target_is_the_dominant_logit():
+    """Rows whose target holds nearly all of the probability (the usual row of a trained
+    policy): X[m] = k_m W[t_m], so z_t = k_m |W_t|^2 stands far above the row's other
+    logits, with k_m up to 64 x 4.  logprob is at most 0 exactly, 0 <= entropy <= ln V,
+    and every output matches the oracle."""
+    M, H, V = 700, 256, 3000
+    c = inputs.make_case("dominant", 131, M, H, V, ignore_frac=0.05, grad_mode="normal")
+    rng = np.random.default_rng(131)
+    valid = ref.valid_rows(c.targets, V, c.ignore_index)
+    Wf = inputs.decode_bf16_to_f32(c.W)
+    k = (64.0 * rng.uniform(0.05, 4.0, M)).astype(np.float32)
+    k[: M // 4] = rng.uniform(3.0, 12.0, M // 4)        # also targets only moderately ahead
+    X = k[:, None] * Wf[np.where(valid, c.targets, 0)]
+    c.X[valid] = inputs.f32_to_bf16_bits(X[valid])
+    print(f"[parity] dominant target M={M} H={H} V={V}", flush=True)
+    res = gu.run_flce(c)
+    o, dX, dW = _oracle(c)
+    assert np.all(res["logprob"] <= 0.0)
+    assert np.all(res["entropy"] >= 0.0) and np.all(res["entropy"] <= np.log(V) + 1e-6)
+    assert np.max(o["logprob"][valid]) > -1e-6          # the oracle's rows are dominant
+    gu.check_forward(res, o, True, "dominant")
+    gu.check_grads(res["dX"], res["dW"], dX, dW, "dominant")
+
+
+def _guarded(numel, dtype, guard_bytes=4096):
+    """A tensor of `numel` elements with `guard_bytes` of canary bytes on both sides."""
+    import torch
+    esz = torch.empty(0, dtype=dtype).element_size()
+    g = guard_bytes // esz
+    buf = torch.empty(numel + 2 * g, dtype=dtype, device="cuda")
+    buf.view(torch.uint8).fill_(0xA5)
+    return buf, buf[g:g + numel], g
+
+
+def _guards_intact(buf, g):
+    import torch
+    b = buf.view(torch.uint8)
+    n = g * buf.element_size()
+    return bool((b[:n] == 0xA5).all()) and bool((b[-n:] == 0xA5).all())
+
+
+@pytest.mark.parametrize("ws_kind", ["preferred", "minimum", "minimum_plus"])
+def test_guard_regions_untouched(ws_kind):
+    """Nothing is written outside the outputs or past the workspace bytes a call is given:
+    canary bytes before and after logprob, lse, entropy, dX, dW and the workspace keep
+    their value, for the preferred workspace, the smallest one (256-row forward waves,
+    256-column backward chunks with the fp32 dX accumulator) and a size just above it."""
+    import torch
+    from log_prob_amd import flce
+    c = inputs.make_case("guards", 132, 600, 136, 3000, ignore_frac=0.05, grad_mode="normal")
+    X, W, t, glp, gent = gu.to_dev(c)
+    fwd_b, bwd_b = flce.workspace_query(c.M, c.H, c.V, True)
+    if ws_kind == "preferred":
+        sizes = (fwd_b, bwd_b)
+    else:
+        extra = 0 if ws_kind == "minimum" else 1000
+        sizes = (flce.forward_workspace_min(c.M, c.H, c.V, True) + extra,
+                 flce.backward_workspace_min(c.M, c.H, c.V) + extra)
+    bufs = [_guarded(c.M, torch.float32) for _ in range(3)]
+    dxb = _guarded(c.M * c.H, torch.bfloat16)
+    dwb = _guarded(c.V * c.H, torch.bfloat16)
+    wsf = _guarded(sizes[0], torch.uint8)
+    wsb = _guarded(sizes[1], torch.uint8)
+    print(f"[parity] guards, workspaces {sizes}", flush=True)
+    lp, lse, ent = (b[1] for b in bufs)
+    flce.forward(X, W, t, c.ignore_index, c.scale, True, workspace=wsf[1], out=(lp, lse, ent))
+    dX, dW = dxb[1].view(c.M, c.H), dwb[1].view(c.V, c.H)
+    flce.backward(X, W, t, lse, ent, glp, gent, c.ignore_index, c.scale, workspace=wsb[1],
+                  out=(dX, dW))
+    torch.cuda.synchronize()
+    for name, (buf, _, g) in zip(("logprob", "lse", "entropy", "dX", "dW", "forward workspace",
+                                  "backward workspace"), bufs + [dxb, dwb, wsf, wsb]):
+        assert _guards_intact(buf, g), f"{name}: a guard byte changed"
+    o, rdX, rdW = _oracle(c)
+    res = dict(logprob=gu.to_np(lp), lse=gu.to_np(lse), entropy=gu.to_np(ent))
+    gu.check_forward(res, o, True, "guards")
+    gu.check_grads(gu.bf16_to_np(dX), gu.bf16_to_np(dW), rdX, rdW, "guards")
