@@ -149,6 +149,28 @@ flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets,
                            void* workspace, size_t workspace_bytes, struct ihipStream_t* stream);
 
 /*
+ * flce_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It takes no
+ * workspace: the partials go to a static device scratch array of the library, 32 MiB
+ * (FLCE_NOALLOC_SCRATCH_BYTES) on each GPU it runs on, held until the process ends,
+ * and the token waves are sized to it.  The call allocates and frees nothing; it
+ * uses the scratch of the current device, so `stream` must belong to that device.
+ * Results are bitwise identical to flce_forward's.  Every value of the scratch a call
+ * reads is written earlier in that call, so nothing needs clearing, but the scratch
+ * is shared: calls that overlap on one GPU (different streams, or threads) race and
+ * must be serialised by the caller.  A vocabulary whose partials of one 256-row wave
+ * (12 bytes per 256 columns with entropy, 8 without, per row) exceed the scratch,
+ * V above about 2.8M with entropy, is rejected with FLCE_ERR_UNSUPPORTED.  The first
+ * call on a device looks the scratch's address up (hipGetSymbolAddress); a failure
+ * there is FLCE_ERR_HIP.  Other arguments and errors as flce_forward.
+ */
+#define FLCE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+flce_status_t flce_forward_noalloc(const void* X, const void* W, const int64_t* targets,
+                                   int64_t M, int64_t H, int64_t V, int64_t ignore_index,
+                                   float scale, int compute_entropy, float* logprob, float* lse,
+                                   float* entropy, struct ihipStream_t* stream);
+
+/*
  * The two halves of flce_forward, for callers that exchange or inspect the
  * per-tile statistics (a vocabulary-sharded caller gathers them across shards
  * before merging).  flce_forward_partials runs the fused GEMM + online-softmax

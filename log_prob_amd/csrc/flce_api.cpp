@@ -544,7 +544,7 @@ flce_status_t flce_forward_merge(const int64_t* targets, int64_t M, int64_t H, i
 
 namespace {
 
-// Checks of a forward call's arguments other than the workspace.
+// Checks shared by flce_forward and flce_forward_noalloc (everything but the workspace).
 flce_status_t check_forward_call(const void* X, const void* W, const int64_t* targets,
                                  int64_t M, int64_t H, int64_t V, float scale,
                                  int compute_entropy, const float* logprob, const float* lse,
@@ -609,6 +609,30 @@ flce_status_t flce_forward(const void* X, const void* W, const int64_t* targets,
                 fwd_layout(kTile, V, ent).total, workspace_bytes);
   return forward_waves(X, W, targets, M, H, V, ignore_index, scale, ent, logprob, lse, entropy,
                        static_cast<char*>(workspace), rows, stream);
+}
+
+static_assert(flce::kScratchBytes == FLCE_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
+
+flce_status_t flce_forward_noalloc(const void* X, const void* W, const int64_t* targets,
+                                   int64_t M, int64_t H, int64_t V, int64_t ignore_index,
+                                   float scale, int compute_entropy, float* logprob, float* lse,
+                                   float* entropy, hipStream_t stream) {
+  if (M == 0) return check_empty(H, V, compute_entropy);
+  flce_status_t st = check_forward_call(X, W, targets, M, H, V, scale, compute_entropy, logprob,
+                                        lse, entropy);
+  if (st != FLCE_OK) return st;
+  const bool ent = compute_entropy == 1;
+  const int64_t rows = wave_rows_for_workspace(M, V, ent, flce::kScratchBytes);
+  if (rows == 0)
+    return fail(FLCE_ERR_UNSUPPORTED,
+                "V=%lld needs %zu bytes of partials per 256-row wave; the static scratch of "
+                "flce_forward_noalloc holds %zu (use flce_forward with a workspace)",
+                (long long)V, fwd_layout(kTile, V, ent).total, flce::kScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = flce::scratch_device_address(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "device scratch address");
+  return forward_waves(X, W, targets, M, H, V, ignore_index, scale, ent, logprob, lse, entropy,
+                       static_cast<char*>(scratch), rows, stream);
 }
 
 }  // extern "C"

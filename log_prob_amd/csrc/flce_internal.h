@@ -112,6 +112,12 @@ struct PolicyLossArgs {
   double denominator;        // > 0: the normaliser N; else the number of valid rows
 };
 
+// Device scratch of flce_forward_noalloc: a file-scope __device__ array in
+// flce_kernels.hip, one copy per GPU, held until the process ends.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+// Address of the current device's copy of that array (hipGetSymbolAddress).
+hipError_t scratch_device_address(void** ptr);
+
 hipError_t launch_fwd_tile(const FwdTileArgs& a, bool entropy, hipStream_t s);
 hipError_t launch_target_logit(const FwdTileArgs& a, hipStream_t s);
 hipError_t launch_fwd_merge(const FwdMergeArgs& a, bool entropy, hipStream_t s);

@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <utility>
 
 #include "flce_internal.h"
@@ -1558,6 +1559,37 @@ __global__ void fill_u16_kernel(uint16_t* __restrict__ p, long n) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const long stride = (long)gridDim.x * blockDim.x;
   for (long j = i; j < n; j += stride) p[j] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free forward: the partials of its token waves.  A
+// __device__ array is module memory: each GPU the library runs on holds its own copy,
+// at its own address, from the module's load until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: kernels get the
+// address from scratch_device_address() instead.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of each GPU's copy, looked up once per device (on the first call that
+// needs it, with that device current) and kept.
+constexpr int kScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_addr[kScratchDevices];
+
+hipError_t scratch_device_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *ptr = g_scratch_addr[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

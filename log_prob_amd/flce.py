@@ -14,13 +14,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libflce.so")
 
 FLCE_OK = 0
+# bytes of the static device scratch flce_forward_noalloc uses (FLCE_NOALLOC_SCRATCH_BYTES)
+FLCE_NOALLOC_SCRATCH_BYTES = 32 << 20
 STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_INVALID_VALUE", 2: "FLCE_ERR_UNSUPPORTED",
           3: "FLCE_ERR_WORKSPACE_TOO_SMALL", 4: "FLCE_ERR_HIP"}
 
 # Every symbol include/flce.h declares.
 EXPORTS = ("flce_workspace_query", "flce_forward_workspace_min", "flce_forward_wave_rows",
            "flce_backward_workspace_min", "flce_backward_chunk_cols",
-           "flce_backward_wave_rows", "flce_forward", "flce_forward_partials", "flce_forward_merge", "flce_backward",
+           "flce_backward_wave_rows", "flce_forward", "flce_forward_noalloc", "flce_forward_partials", "flce_forward_merge", "flce_backward",
            "flce_forward_partials_shard", "flce_forward_merge_shards",
            "flce_backward_shard_workspace_query", "flce_backward_shard", "flce_nll_reduce",
            "flce_nll_mean_grad", "flce_policy_loss_reduce", "flce_policy_loss_grad",
@@ -53,6 +55,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.flce_backward_chunk_cols.argtypes = [I64, I64, I64, SZ, c.POINTER(I64)]
     lib.flce_backward_wave_rows.argtypes = [I64, I64, I64, SZ, c.POINTER(I64)]
     lib.flce_forward.argtypes = [P, P, P, I64, I64, I64, I64, c.c_float, c.c_int, P, P, P, P, SZ, P]
+    lib.flce_forward_noalloc.argtypes = [P, P, P, I64, I64, I64, I64, c.c_float, c.c_int, P, P, P,
+                                         P]
     lib.flce_forward_partials.argtypes = [P, P, P, I64, I64, I64, I64, c.c_float, c.c_int, P, SZ,
                                           P]
     lib.flce_forward_merge.argtypes = [P, I64, I64, I64, I64, c.c_int, P, P, P, P, SZ, P]
@@ -75,7 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "flce_policy_loss_grad", "flce_workspace_query",
                  "flce_forward_workspace_min", "flce_forward_wave_rows",
                  "flce_backward_workspace_min", "flce_backward_chunk_cols",
-                 "flce_backward_wave_rows", "flce_forward", "flce_forward_partials", "flce_forward_merge", "flce_backward",
+                 "flce_backward_wave_rows", "flce_forward", "flce_forward_noalloc", "flce_forward_partials", "flce_forward_merge", "flce_backward",
                  "flce_forward_partials_shard", "flce_forward_merge_shards",
                  "flce_backward_shard_workspace_query", "flce_backward_shard"):
         getattr(lib, name).restype = c.c_int
@@ -191,6 +195,31 @@ def forward(X, W, targets, ignore_index: int = -100, scale: float = 1.0,
     _check(load().flce_forward(_ptr(X), _ptr(W), _ptr(targets), M, H, V, int(ignore_index),
                                float(scale), int(bool(compute_entropy)), _ptr(logprob), _ptr(lse),
                                _ptr(entropy), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return logprob, lse, entropy
+
+
+def forward_noalloc(X, W, targets, ignore_index: int = -100, scale: float = 1.0,
+                    compute_entropy: bool = True, out=None):
+    """flce_forward_noalloc: the forward through the library's static device scratch (no
+    workspace).  With `out` = (logprob, lse, entropy-or-None) nothing is allocated here
+    either; calls overlapping on one GPU share the scratch and must not run concurrently."""
+    import torch
+    M, H = X.shape
+    V = W.shape[0]
+    _require(X, "X", torch.bfloat16, (M, H))
+    _require(W, "W", torch.bfloat16, (V, H))
+    _require(targets, "targets", torch.int64, (M,))
+    dev = X.device
+    if out is None:
+        logprob = torch.empty(M, dtype=torch.float32, device=dev)
+        lse = torch.empty(M, dtype=torch.float32, device=dev)
+        entropy = torch.empty(M, dtype=torch.float32, device=dev) if compute_entropy else None
+    else:
+        logprob, lse, entropy = out
+    _check(load().flce_forward_noalloc(_ptr(X), _ptr(W), _ptr(targets), M, H, V,
+                                       int(ignore_index), float(scale),
+                                       int(bool(compute_entropy)), _ptr(logprob), _ptr(lse),
+                                       _ptr(entropy), _stream(dev)))
     return logprob, lse, entropy
 
 

@@ -275,6 +275,40 @@ def test_empty_batch_needs_no_device():
     assert _bwd(lib, M=0, dW=18) == 2
 
 
+def _fwd_noalloc(lib, X=16, W=16, t=16, M=4, H=8, V=3, ign=-100, scale=1.0, ent=1, lp=16,
+                 lse=16, entropy=16):
+    return lib.flce_forward_noalloc(X, W, t, M, H, V, ign, scale, ent, lp, lse, entropy, None)
+
+
+def test_forward_noalloc_rejections_need_no_device():
+    """The allocation-free forward checks its arguments like flce_forward, and rejects a
+    vocabulary whose one 256-row wave of partials does not fit its static scratch, all
+    before any HIP call.  (Only rejected calls are made here: a call that passes would
+    launch kernels on these placeholder pointers.)"""
+    lib = flce.load()
+    INV, UNS = 1, 2
+    assert flce.FLCE_NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert _fwd_noalloc(lib, X=None) == INV
+    assert _fwd_noalloc(lib, t=None) == INV
+    assert _fwd_noalloc(lib, lse=None) == INV
+    assert _fwd_noalloc(lib, ent=2) == INV
+    assert _fwd_noalloc(lib, entropy=None) == INV
+    assert _fwd_noalloc(lib, scale=float("nan")) == INV
+    assert _fwd_noalloc(lib, H=12) == UNS
+    assert _fwd_noalloc(lib, X=24) == UNS
+    assert _fwd_noalloc(lib, M=1 << 31) == UNS
+    # the partials of a 256-row wave: 3 (entropy) or 2 arrays of 256 fp32 per vocabulary
+    # tile, each array rounded up to 256 bytes, plus 1 KiB of target logits
+    for ent, arrays in ((1, 3), (0, 2)):
+        n_vt = (flce.FLCE_NOALLOC_SCRATCH_BYTES - 1024) // (arrays * 1024)
+        assert flce.forward_wave_rows(256, 8, 256 * n_vt, flce.FLCE_NOALLOC_SCRATCH_BYTES,
+                                      bool(ent)) == 256
+        assert _fwd_noalloc(lib, V=256 * n_vt + 1, ent=ent) == UNS
+        assert b"scratch" in lib.flce_last_error_message()
+    # an empty batch is a valid call that touches nothing
+    assert _fwd_noalloc(lib, X=None, W=None, t=None, M=0, lp=None, lse=None, entropy=None) == 0
+
+
 def test_size_limits_match_the_header():
     """Each edge of the documented size limits: 0 <= M <= 2^30, 8 <= H <= 2^20 with
     H % 8 == 0, 1 <= V <= 2^30."""
