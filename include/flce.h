@@ -96,7 +96,9 @@ flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_
  * (*bwd_bytes of flce_workspace_query) is one wave of every row with up to 4 GiB of
  * d-logits per chunk (every column at once when they fit).  With less, the call
  * takes the schedule that fits and moves the fewest extra bytes: narrower chunks, or
- * waves of 256 to 16384 rows.  The minimum is the smallest of: one wave with
+ * waves of 256 to 16384 rows.  A step (one wave over one chunk) of at most 8e12 FLOP
+ * (6 x rows x H x chunk) runs pipelined when two d-logit buffers fit: one launch per
+ * step computes the step's dW and dX together with the next step's d-logits.  The minimum is the smallest of: one wave with
  * 256-column chunks (d-logits + fp32 dX accumulator of M rows), one wave with every
  * column (d-logits only), 256-row waves with 256-column chunks or with every column
  * (+ the fp32 dW accumulator): once M > 256 it is at most 4 V H + 1024 H + 131072
@@ -111,6 +113,14 @@ flce_status_t flce_backward_workspace_min(int64_t M, int64_t H, int64_t V, size_
  * FLCE_ERR_WORKSPACE_TOO_SMALL below the minimum. */
 flce_status_t flce_backward_chunk_cols(int64_t M, int64_t H, int64_t V, size_t workspace_bytes,
                                        int64_t* chunk_cols);
+
+/* The whole schedule flce_backward would run with this workspace: token rows per wave,
+ * chunk width, and whether it runs pipelined (1: one launch per step, the dW and dX
+ * tiles of one step with the d-logit tiles of the next, over two d-logit buffers) or
+ * as three launches per step (0).  Any output may be NULL; FLCE_ERR_WORKSPACE_TOO_SMALL
+ * below the minimum. */
+flce_status_t flce_backward_schedule(int64_t M, int64_t H, int64_t V, size_t workspace_bytes,
+                                     int64_t* rows, int64_t* chunk_cols, int* pipelined);
 
 /* Token rows per wave flce_backward would use with this workspace (a multiple of 256;
  * M rounded up to 256 means one wave); FLCE_ERR_WORKSPACE_TOO_SMALL below the minimum. */

@@ -110,18 +110,29 @@ int64_t wave_rows_for_workspace(int64_t M, int64_t V, bool ent, size_t bytes) {
 // scaled linear cross-entropy", sections "Implementation / Backward" and "Correctness".
 struct BwdPlan {
   int64_t rows = 0, chunk = 0;
+  bool pipe = false;               // grouped launches over two d-logit buffers
+  int nbuf = 1;                    // d-logit buffers
   bool dx_acc = false, dw_acc = false;
-  size_t off_dx = 0, off_dw = 0, total = 0;
+  size_t dz_bytes = 0, off_dx = 0, off_dw = 0, total = 0;
 };
 
-BwdPlan bwd_plan(int64_t M, int64_t H, int64_t V, int64_t rows, int64_t chunk, bool dx_bf16) {
+// Steps (token waves x vocabulary chunks) of a schedule.
+int64_t plan_steps(int64_t M, int64_t V, int64_t rows, int64_t chunk) {
+  return cdiv(M, rows) * cdiv(cdiv(V, kTile) * kTile, chunk);
+}
+
+BwdPlan bwd_plan(int64_t M, int64_t H, int64_t V, int64_t rows, int64_t chunk, bool dx_bf16,
+                 bool pipe) {
   const int64_t Mpad = cdiv(M, kTile) * kTile;
   const int64_t Vpad = cdiv(V, kTile) * kTile;
   BwdPlan p;
   p.rows = rows < Mpad ? rows : Mpad;
   p.chunk = chunk;
+  p.pipe = pipe;
+  p.nbuf = (pipe && Mpad > 0 && plan_steps(M, V, p.rows, chunk) > 1) ? 2 : 1;
   const int64_t wave_m = p.rows < M ? p.rows : M;  // token rows of the largest wave
-  size_t b = align_up(size_t(p.rows) * size_t(chunk) * 2);
+  p.dz_bytes = align_up(size_t(p.rows) * size_t(chunk) * 2);
+  size_t b = size_t(p.nbuf) * p.dz_bytes;
   p.dx_acc = dx_bf16 && chunk < Vpad;
   if (p.dx_acc) {
     p.off_dx = b;
@@ -138,36 +149,49 @@ BwdPlan bwd_plan(int64_t M, int64_t H, int64_t V, int64_t rows, int64_t chunk, b
 
 // Widest chunk (a multiple of 256, at most min(Vpad, kMaxChunk)) for waves of `rows`
 // rows whose plan fits in `bytes`; 0 if none.
-int64_t widest_chunk(int64_t M, int64_t H, int64_t V, int64_t rows, bool dx_bf16, size_t bytes) {
+int64_t widest_chunk(int64_t M, int64_t H, int64_t V, int64_t rows, bool dx_bf16, bool pipe,
+                     size_t bytes) {
   const int64_t Vpad = cdiv(V, kTile) * kTile;
-  if (Vpad <= kMaxChunk && bwd_plan(M, H, V, rows, Vpad, dx_bf16).total <= bytes) return Vpad;
+  if (Vpad <= kMaxChunk && bwd_plan(M, H, V, rows, Vpad, dx_bf16, pipe).total <= bytes)
+    return Vpad;
   // narrower chunks: the size grows with the chunk from here on
-  const BwdPlan p0 = bwd_plan(M, H, V, rows, kTile, dx_bf16);
+  const BwdPlan p0 = bwd_plan(M, H, V, rows, kTile, dx_bf16, pipe);
   if (p0.total > bytes) return 0;
-  const size_t fixed = p0.total - align_up(size_t(p0.rows) * size_t(kTile) * 2);
-  int64_t c = int64_t((bytes - fixed) / (size_t(p0.rows) * 2)) / kTile * kTile;
+  const size_t fixed = p0.total - size_t(p0.nbuf) * p0.dz_bytes;
+  int64_t c = int64_t((bytes - fixed) / (size_t(p0.nbuf) * size_t(p0.rows) * 2)) / kTile * kTile;
   const int64_t cap = (Vpad <= kMaxChunk ? Vpad - kTile : kMaxChunk);
   if (c > cap) c = cap;
-  while (c > kTile && bwd_plan(M, H, V, rows, c, dx_bf16).total > bytes) c -= kTile;
+  while (c > kTile && bwd_plan(M, H, V, rows, c, dx_bf16, pipe).total > bytes) c -= kTile;
   return c >= kTile ? c : 0;
 }
 
+// Pipelined launches only for steps of at most this much work (6 x rows x H x chunk
+// FLOP).  Measured on MI355X: at M = H = 4096, V = 32768 (3.3e12 FLOP in one step) two
+// launches instead of three take the backward from 2.60 to 2.42 ms; at M = H = 8192,
+// V = 131072 (5.3e13) the grouped dW + dX launch costs 3% (36.4 -> 37.6 ms: the XCDs
+// leave the dW phase at different times, and the W columns the dX tiles of all XCDs
+// read in step stop being shared through the memory-side cache), and at M = 32767,
+// H = 2048, V = 151936 the best pipelined schedule is 1% behind the sequential one.
+constexpr double kPipeMaxStepFlop = 8e12;
+
 // HBM bytes a plan moves beyond the d-logits themselves, plus its launches (10 us each,
 // at 8 TB/s): the fp32 dX accumulator is read and written once per extra chunk, the
-// fp32 dW accumulator once per extra wave.  Used only to rank plans that fit.
+// fp32 dW accumulator once per extra wave; a pipelined plan makes one launch per step
+// (plus one) instead of three.  Used only to rank plans that fit.
 double plan_cost(int64_t M, int64_t H, int64_t V, const BwdPlan& p) {
   const int64_t Vpad = cdiv(V, kTile) * kTile;
   const double n_chunks = double(cdiv(Vpad, p.chunk)), n_waves = double(cdiv(M, p.rows));
-  double c = 3.0 * 80e6 * n_chunks * n_waves;
+  const double steps = n_chunks * n_waves;
+  double c = 80e6 * (p.pipe ? steps + 1.0 : 3.0 * steps);
   if (p.chunk < Vpad) c += (n_chunks - 1.0) * 8.0 * double(M) * double(H);
   if (p.dw_acc) c += (n_waves - 1.0) * 8.0 * double(V) * double(H);
   return c;
 }
 
 // The schedule flce_backward (dx_bf16) or flce_backward_shard runs with `bytes` of
-// workspace: one wave of every row with the widest chunk that fits, or, when that
-// costs more (or does not fit), waves of 256 to 16384 rows with the fp32 dW
-// accumulator, whichever moves the fewest extra bytes; total 0 if nothing fits.
+// workspace: among one wave of every row and waves of 16384 down to 256 rows, each
+// pipelined (two d-logit buffers) or not, with the widest chunk that fits, the one that
+// moves the fewest extra bytes; chunk 0 if nothing fits.
 BwdPlan plan_for_workspace(int64_t M, int64_t H, int64_t V, bool dx_bf16, size_t bytes) {
   const int64_t Mpad = cdiv(M, kTile) * kTile;
   BwdPlan best;
@@ -178,13 +202,16 @@ BwdPlan plan_for_workspace(int64_t M, int64_t H, int64_t V, bool dx_bf16, size_t
   }
   double best_cost = 0.0;
   auto consider = [&](int64_t rows) {
-    const int64_t c = widest_chunk(M, H, V, rows, dx_bf16, bytes);
-    if (c == 0) return;
-    const BwdPlan p = bwd_plan(M, H, V, rows, c, dx_bf16);
-    const double cost = plan_cost(M, H, V, p);
-    if (best.total == 0 || cost < best_cost) {
-      best = p;
-      best_cost = cost;
+    for (int pipe = 1; pipe >= 0; --pipe) {
+      const int64_t c = widest_chunk(M, H, V, rows, dx_bf16, pipe == 1, bytes);
+      if (c == 0) continue;
+      if (pipe == 1 && 6.0 * double(rows) * double(H) * double(c) > kPipeMaxStepFlop) continue;
+      const BwdPlan p = bwd_plan(M, H, V, rows, c, dx_bf16, pipe == 1);
+      const double cost = plan_cost(M, H, V, p);
+      if (best.chunk == 0 || cost < best_cost) {
+        best = p;
+        best_cost = cost;
+      }
     }
   };
   consider(Mpad);  // one wave of every row
@@ -208,11 +235,11 @@ int64_t preferred_chunk(int64_t M, int64_t V) {
 size_t bwd_min_bytes(int64_t M, int64_t H, int64_t V, bool dx_bf16) {
   const int64_t Mpad = cdiv(M, kTile) * kTile;
   const int64_t Vpad = cdiv(V, kTile) * kTile;
-  size_t m = bwd_plan(M, H, V, Mpad, kTile, dx_bf16).total;
-  if (Vpad <= kMaxChunk) m = std::min(m, bwd_plan(M, H, V, Mpad, Vpad, dx_bf16).total);
+  size_t m = bwd_plan(M, H, V, Mpad, kTile, dx_bf16, false).total;
+  if (Vpad <= kMaxChunk) m = std::min(m, bwd_plan(M, H, V, Mpad, Vpad, dx_bf16, false).total);
   if (Mpad > kTile) {
-    m = std::min(m, bwd_plan(M, H, V, kTile, kTile, dx_bf16).total);
-    if (Vpad <= kMaxChunk) m = std::min(m, bwd_plan(M, H, V, kTile, Vpad, dx_bf16).total);
+    m = std::min(m, bwd_plan(M, H, V, kTile, kTile, dx_bf16, false).total);
+    if (Vpad <= kMaxChunk) m = std::min(m, bwd_plan(M, H, V, kTile, Vpad, dx_bf16, false).total);
   }
   return m;
 }
@@ -269,7 +296,8 @@ flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_
   if (st != FLCE_OK) return st;
   if (fwd_bytes) *fwd_bytes = fwd_layout(M, V, compute_entropy == 1).total;
   if (bwd_bytes)
-    *bwd_bytes = bwd_plan(M, H, V, cdiv(M, kTile) * kTile, preferred_chunk(M, V), true).total;
+    *bwd_bytes =
+        bwd_plan(M, H, V, cdiv(M, kTile) * kTile, preferred_chunk(M, V), true, false).total;
   return ok();
 }
 
@@ -321,6 +349,20 @@ flce_status_t flce_backward_chunk_cols(int64_t M, int64_t H, int64_t V, size_t w
     return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the minimum %zu",
                 workspace_bytes, bwd_min_bytes(M, H, V, true));
   *chunk_cols = p.chunk;
+  return ok();
+}
+
+flce_status_t flce_backward_schedule(int64_t M, int64_t H, int64_t V, size_t workspace_bytes,
+                                     int64_t* rows, int64_t* chunk_cols, int* pipelined) {
+  flce_status_t st = check_shape(M, H, V);
+  if (st != FLCE_OK) return st;
+  const BwdPlan p = plan_for_workspace(M, H, V, true, workspace_bytes);
+  if (p.chunk == 0)
+    return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the minimum %zu",
+                workspace_bytes, bwd_min_bytes(M, H, V, true));
+  if (rows) *rows = p.rows;
+  if (chunk_cols) *chunk_cols = p.chunk;
+  if (pipelined) *pipelined = p.pipe ? 1 : 0;
   return ok();
 }
 
@@ -674,82 +716,115 @@ flce_status_t backward_run(const void* X, const void* W, const int64_t* targets,
   const int64_t Vpad = cdiv(V, kTile) * kTile;
   const int64_t n_chunks = cdiv(Vpad, P.chunk);
   const int64_t n_waves = cdiv(M, P.rows);
+  const int64_t steps = n_chunks * n_waves;
   const bool entgrad = grad_entropy != nullptr;
-  uint16_t* dz = reinterpret_cast<uint16_t*>(ws);
   float* dx_acc = P.dx_acc ? reinterpret_cast<float*>(ws + P.off_dx) : nullptr;
   float* dw_acc = P.dw_acc ? reinterpret_cast<float*>(ws + P.off_dw) : nullptr;
   const uint16_t* Xb = static_cast<const uint16_t*>(X);
-  for (int64_t w = 0; w < n_waves; ++w) {
+
+  // the three kernels' arguments for step k = (wave k / n_chunks, chunk k % n_chunks)
+  struct Step {
+    flce::DlogitsArgs d;
+    flce::GemmDwArgs g;
+    flce::GemmDxArgs x;
+  };
+  auto step_args = [&](int64_t k) {
+    const int64_t w = k / n_chunks, c = k % n_chunks;
     const int64_t r0 = w * P.rows;
     const int64_t mw = (M - r0) < P.rows ? (M - r0) : P.rows;
     const int64_t n_mt = cdiv(mw, kTile);
-    for (int64_t c = 0; c < n_chunks; ++c) {
-      const int64_t vbase = c * P.chunk;
-      const int64_t kc = (Vpad - vbase) < P.chunk ? (Vpad - vbase) : P.chunk;
+    const int64_t vbase = c * P.chunk;
+    const int64_t kc = (Vpad - vbase) < P.chunk ? (Vpad - vbase) : P.chunk;
+    uint16_t* dz = reinterpret_cast<uint16_t*>(ws + size_t(k % P.nbuf) * P.dz_bytes);
+    Step s{};
+    flce::DlogitsArgs& d = s.d;
+    d.X = Xb + r0 * H;
+    d.W = static_cast<const uint16_t*>(W);
+    d.targets = targets + r0;
+    d.M = int(mw);
+    d.H = int(H);
+    d.V = int(V);
+    d.v_off = v_off;
+    d.V_total = V_total;
+    d.ignore_index = ignore_index;
+    d.scale = scale;
+    d.lse = lse + r0;
+    d.entropy = entropy ? entropy + r0 : nullptr;
+    d.grad_logprob = grad_logprob ? grad_logprob + r0 : nullptr;
+    d.grad_entropy = grad_entropy ? grad_entropy + r0 : nullptr;
+    d.vbase = int(vbase);
+    d.n_mt = int(n_mt);
+    d.n_vt = int(kc / kTile);
+    d.dz = dz;
+    d.ldz = long(P.chunk);
 
-      flce::DlogitsArgs d{};
-      d.X = Xb + r0 * H;
-      d.W = static_cast<const uint16_t*>(W);
-      d.targets = targets + r0;
-      d.M = int(mw);
-      d.H = int(H);
-      d.V = int(V);
-      d.v_off = v_off;
-      d.V_total = V_total;
-      d.ignore_index = ignore_index;
-      d.scale = scale;
-      d.lse = lse + r0;
-      d.entropy = entropy ? entropy + r0 : nullptr;
-      d.grad_logprob = grad_logprob ? grad_logprob + r0 : nullptr;
-      d.grad_entropy = grad_entropy ? grad_entropy + r0 : nullptr;
-      d.vbase = int(vbase);
-      d.n_mt = int(n_mt);
-      d.n_vt = int(kc / kTile);
-      d.dz = dz;
-      d.ldz = long(P.chunk);
-      hipError_t e = flce::launch_dlogits(d, entgrad, stream);
+    flce::GemmDwArgs& g = s.g;
+    g.dz = dz;
+    g.ldz = long(P.chunk);
+    g.X = Xb + r0 * H;
+    g.dW = static_cast<uint16_t*>(dW);
+    g.acc = dw_acc;
+    g.M = int(mw);
+    g.Mpad = int(n_mt * kTile);
+    g.H = int(H);
+    g.V = int(V);
+    g.vbase = int(vbase);
+    g.chunk_cols = int(kc);
+    g.n_i = int(kc / kTile);
+    g.n_h = int(cdiv(H, kTile));
+    g.mode = n_waves == 1 ? 0 : (w == 0 ? 1 : (w == n_waves - 1 ? 3 : 2));
+
+    flce::GemmDxArgs& x = s.x;
+    x.dz = dz;
+    x.ldz = long(P.chunk);
+    x.W = static_cast<const uint16_t*>(W);
+    x.dX = dX_bf16 ? dX_bf16 + r0 * H : nullptr;
+    x.M = int(mw);
+    x.H = int(H);
+    x.V = int(V);
+    x.vbase = int(vbase);
+    x.kcols = int(kc);
+    x.n_m = int(n_mt);
+    x.n_h = int(cdiv(H, kTile));
+    if (dX_bf16) {
+      x.acc = dx_acc;
+      x.mode = n_chunks == 1 ? 0 : (c == 0 ? 1 : (c == n_chunks - 1 ? 3 : 2));
+    } else {
+      x.acc = dX_f32 + r0 * H;
+      x.mode = (c == 0 && !acc_in) ? 1 : 2;
+    }
+    return s;
+  };
+
+  if (!P.pipe) {
+    for (int64_t k = 0; k < steps; ++k) {
+      const Step s = step_args(k);
+      hipError_t e = flce::launch_dlogits(s.d, entgrad, stream);
       if (e != hipSuccess) return hip_fail(e, "d-logits kernel launch");
-
-      flce::GemmDwArgs g{};
-      g.dz = dz;
-      g.ldz = long(P.chunk);
-      g.X = Xb + r0 * H;
-      g.dW = static_cast<uint16_t*>(dW);
-      g.acc = dw_acc;
-      g.M = int(mw);
-      g.Mpad = int(n_mt * kTile);
-      g.H = int(H);
-      g.V = int(V);
-      g.vbase = int(vbase);
-      g.chunk_cols = int(kc);
-      g.n_i = int(kc / kTile);
-      g.n_h = int(cdiv(H, kTile));
-      g.mode = n_waves == 1 ? 0 : (w == 0 ? 1 : (w == n_waves - 1 ? 3 : 2));
-      e = flce::launch_gemm_dw(g, stream);
+      e = flce::launch_gemm_dw(s.g, stream);
       if (e != hipSuccess) return hip_fail(e, "dW GEMM launch");
-
-      flce::GemmDxArgs x{};
-      x.dz = dz;
-      x.ldz = long(P.chunk);
-      x.W = static_cast<const uint16_t*>(W);
-      x.dX = dX_bf16 ? dX_bf16 + r0 * H : nullptr;
-      x.M = int(mw);
-      x.H = int(H);
-      x.V = int(V);
-      x.vbase = int(vbase);
-      x.kcols = int(kc);
-      x.n_m = int(n_mt);
-      x.n_h = int(cdiv(H, kTile));
-      if (dX_bf16) {
-        x.acc = dx_acc;
-        x.mode = n_chunks == 1 ? 0 : (c == 0 ? 1 : (c == n_chunks - 1 ? 3 : 2));
-      } else {
-        x.acc = dX_f32 + r0 * H;
-        x.mode = (c == 0 && !acc_in) ? 1 : 2;
-      }
-      e = flce::launch_gemm_dx(x, stream);
+      e = flce::launch_gemm_dx(s.x, stream);
       if (e != hipSuccess) return hip_fail(e, "dX GEMM launch");
     }
+    return ok();
+  }
+  // pipelined: launch k runs the GEMMs of step k - 1 and the d-logits of step k, which
+  // write the other d-logit buffer
+  for (int64_t k = 0; k <= steps; ++k) {
+    flce::PipeArgs a{};
+    if (k < steps) {
+      a.dl = step_args(k).d;
+      a.n_dl = a.dl.n_mt * a.dl.n_vt;
+    }
+    if (k > 0) {
+      const Step s = step_args(k - 1);
+      a.dw = s.g;
+      a.dx = s.x;
+      a.n_dw = s.g.n_i * s.g.n_h;
+      a.n_dx = s.x.n_m * s.x.n_h;
+    }
+    const hipError_t e = flce::launch_bwd_pipe(a, entgrad, stream);
+    if (e != hipSuccess) return hip_fail(e, "pipelined backward launch");
   }
   return ok();
 }
@@ -795,7 +870,8 @@ flce_status_t flce_backward_shard_workspace_query(int64_t M, int64_t H, int64_t 
   const int64_t Mpad = cdiv(M, kTile) * kTile;
   if (min_bytes) *min_bytes = bwd_min_bytes(M, H, V_shard, false);
   if (preferred_bytes)
-    *preferred_bytes = bwd_plan(M, H, V_shard, Mpad, preferred_chunk(M, V_shard), false).total;
+    *preferred_bytes =
+        bwd_plan(M, H, V_shard, Mpad, preferred_chunk(M, V_shard), false, false).total;
   return ok();
 }
 

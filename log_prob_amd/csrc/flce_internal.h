@@ -100,6 +100,15 @@ struct GemmDxArgs {
   int mode;             // 0 write bf16, 1 write acc, 2 add to acc, 3 add and write bf16
 };
 
+// One launch of the pipelined backward: the dW and dX tiles of one step and the d-logit
+// tiles of the next (a kind with no tiles has count 0).
+struct PipeArgs {
+  DlogitsArgs dl;
+  GemmDwArgs dw;
+  GemmDxArgs dx;
+  int n_dl, n_dw, n_dx;   // tiles: dl.n_mt * dl.n_vt, dw.n_i * dw.n_h, dx.n_m * dx.n_h
+};
+
 // Clipped policy loss over per-token log-probs (see flce_policy_loss_reduce).
 struct PolicyLossArgs {
   const float* logprob;      // [M]
@@ -123,6 +132,7 @@ hipError_t launch_target_logit(const FwdTileArgs& a, hipStream_t s);
 hipError_t launch_fwd_merge(const FwdMergeArgs& a, bool entropy, hipStream_t s);
 hipError_t launch_dlogits(const DlogitsArgs& a, bool entropy_grad, hipStream_t s);
 hipError_t launch_gemm_dw(const GemmDwArgs& a, hipStream_t s);
+hipError_t launch_bwd_pipe(const PipeArgs& a, bool entropy_grad, hipStream_t s);
 hipError_t launch_gemm_dx(const GemmDxArgs& a, hipStream_t s);
 hipError_t launch_fill_zero_u16(uint16_t* p, long n, hipStream_t s);
 hipError_t launch_policy_loss_reduce(const PolicyLossArgs& a, float* per_token_loss,

@@ -116,11 +116,10 @@ static_assert(BigShape::TN == TILE, "backward tile");
 // on XCD b % 8.  Ids are renumbered so each XCD receives a contiguous range of
 // logical ids, walked in groups of `group_m` tile rows (tile row fastest): the
 // workgroups resident on one XCD then share a few operand tiles in its L2.
-__device__ __forceinline__ void tile_coords(int bid, int nblocks, int n_m, int n_n, int group_m,
-                                            int& tm, int& tn) {
-  const int per = nblocks >> 3;
-  int L = bid;
-  if (bid < (per << 3)) L = (bid & 7) * per + (bid >> 3);
+// Logical id L of a grid of n_m x n_n tiles -> tile (tm, tn): groups of `group_m` tile
+// rows, tile row fastest within a group.
+__device__ __forceinline__ void group_coords(int L, int n_m, int n_n, int group_m, int& tm,
+                                             int& tn) {
   const int width = group_m * n_n;
   const int g = L / width;
   const int first = g * group_m;
@@ -128,6 +127,14 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int n_m, int n
   const int inner = L - g * width;
   tm = first + inner % gm;
   tn = inner / gm;
+}
+
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int n_m, int n_n, int group_m,
+                                            int& tm, int& tn) {
+  const int per = nblocks >> 3;
+  int L = bid;
+  if (bid < (per << 3)) L = (bid & 7) * per + (bid >> 3);
+  group_coords(L, n_m, n_n, group_m, tm, tn);
 }
 
 // ---------------------------------------------------------------------------
@@ -1215,15 +1222,13 @@ __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4]
 // rows):  scale dz = scale (a ([v = t] - p) + b p (E - scale acc))
 //                  = p (c0 + cb acc) + [v = t] sa,
 // c0 = scale (b E - a), cb = -scale^2 b, sa = scale a.
+// LDS of the d-logit tile: the pipeline, then the bf16 output tile and the per-row arrays
+constexpr int LDS_DLOGITS = BigShape::PIPE_BYTES > LDS_OUT + 5 * TILE * 4
+                                ? BigShape::PIPE_BYTES
+                                : LDS_OUT + 5 * TILE * 4;
+
 template <bool ENTGRAD>
-__global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
-  // the pipeline, then the bf16 output tile and the per-row arrays
-  constexpr int ROW_BYTES = 5 * TILE * 4;
-  constexpr int LDS_DLOGITS =
-      BigShape::PIPE_BYTES > LDS_OUT + ROW_BYTES ? BigShape::PIPE_BYTES : LDS_OUT + ROW_BYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_DLOGITS];
-  int mt, vt;
-  tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, 8, mt, vt);
+__device__ __forceinline__ void dlogits_tile(const DlogitsArgs& p, int mt, int vt, char* smem) {
   const int row0 = mt * TILE, ccol0 = vt * TILE, col0 = p.vbase + ccol0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -1287,6 +1292,14 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
   else
     stage_dlogits<ENTGRAD, true>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1,
                                  colmask, dst);
+}
+
+template <bool ENTGRAD>
+__global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_DLOGITS];
+  int mt, vt;
+  tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, 8, mt, vt);
+  dlogits_tile<ENTGRAD>(p, mt, vt, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1367,12 +1380,7 @@ __device__ __forceinline__ void tile_f32(const f32x16 (&acc)[4][4], char* smem, 
 
 // dW[vbase + i, h] = sum_m dzs[m, i] X[m, h]: A = dzs^T (MN), B = X^T (MN), K = Mpad.
 // mode 0: write bf16; 1-3: the fp32 accumulator across token waves (see tile_f32).
-__global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
-  int ti, th;
-  // groups run along H: the few X^T tiles stay in L2 while each dzs tile is read by
-  // one group of an XCD at a time, so dzs streams from HBM about once per H group
-  tile_coords(blockIdx.x, gridDim.x, p.n_h, p.n_i, 8, th, ti);
+__device__ __forceinline__ void dw_tile(const GemmDwArgs& p, int ti, int th, char* smem) {
   const int i0 = ti * TILE, h0 = th * TILE;
   f32x16 acc[4][4];
   // dzs has Mpad rows (rows past M hold zeros); X has only M rows.
@@ -1392,14 +1400,18 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
     tile_f32(acc, smem, F32Tile{p.acc + o, p.dW + o, p.H, rows, p.H - h0, p.mode}, wave, lane);
 }
 
+__global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
+  int ti, th;
+  // groups run along H: the few X^T tiles stay in L2 while each dzs tile is read by
+  // one group of an XCD at a time, so dzs streams from HBM about once per H group
+  tile_coords(blockIdx.x, gridDim.x, p.n_h, p.n_i, 8, th, ti);
+  dw_tile(p, ti, th, smem);
+}
+
 // dX[m, h] (+)= sum_i dzs[m, i] W[vbase + i, h]: A = dzs (KC), B = W^T (MN), K = kcols.
 // mode 0: write bf16; 1: write fp32 accumulator; 2: accumulate fp32; 3: accumulate and write bf16.
-__global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
-  int tm, th;
-  // groups run along H: in step, the XCDs read the same W columns (shared through the
-  // memory-side cache) while each streams d-logit bands of its own
-  tile_coords(blockIdx.x, gridDim.x, p.n_h, p.n_m, 8, th, tm);
+__device__ __forceinline__ void dx_tile(const GemmDxArgs& p, int tm, int th, char* smem) {
   const int m0 = tm * TILE, h0 = th * TILE;
   f32x16 acc[4][4];
   // the chunk's kcols (padded) columns of dzs (band tm of the blocked buffer); W has
@@ -1418,6 +1430,59 @@ __global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
     const long o = (long)m0 * p.H + h0;
     tile_f32(acc, smem, F32Tile{p.acc + o, p.dX + o, p.H, p.M - m0, p.H - h0, p.mode}, wave,
              lane);
+  }
+}
+
+__global__ __launch_bounds__(NTHREADS) void gemm_dx_kernel(GemmDxArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
+  int tm, th;
+  // groups run along H: in step, the XCDs read the same W columns (shared through the
+  // memory-side cache) while each streams d-logit bands of its own
+  tile_coords(blockIdx.x, gridDim.x, p.n_h, p.n_m, 8, th, tm);
+  dx_tile(p, tm, th, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined backward: one launch runs the dW and dX tiles of one step (a token wave x
+// vocabulary chunk, reading that step's d-logit buffer) together with the d-logit
+// tiles of the next step (writing the other buffer), so no tile of a launch depends on
+// another one, and the backward takes n + 1 launches for n steps instead of 3 n.  Each
+// XCD (workgroup id modulo 8) takes an eighth of each kind of tile, contiguous in that
+// kind's L2-grouped order, and works through its dW tiles first, then its dX tiles,
+// then its d-logit tiles; ids past an XCD's share exit at once.
+static_assert(LDS_DLOGITS >= LDS_BIG, "one LDS size serves every tile kind");
+
+__device__ __forceinline__ void xcd_share(int n, int x, int& lo, int& cnt) {
+  lo = (int)((long)n * x / 8);
+  cnt = (int)((long)n * (x + 1) / 8) - lo;
+}
+
+template <bool ENTGRAD>
+__global__ __launch_bounds__(NTHREADS) void bwd_pipe_kernel(PipeArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_DLOGITS];
+  const int x = blockIdx.x & 7;
+  int pos = blockIdx.x >> 3, lo, cnt;
+  xcd_share(p.n_dw, x, lo, cnt);
+  if (pos < cnt) {
+    int ti, th;
+    group_coords(lo + pos, p.dw.n_h, p.dw.n_i, 8, th, ti);
+    dw_tile(p.dw, ti, th, smem);
+    return;
+  }
+  pos -= cnt;
+  xcd_share(p.n_dx, x, lo, cnt);
+  if (pos < cnt) {
+    int tm, th;
+    group_coords(lo + pos, p.dx.n_h, p.dx.n_m, 8, th, tm);
+    dx_tile(p.dx, tm, th, smem);
+    return;
+  }
+  pos -= cnt;
+  xcd_share(p.n_dl, x, lo, cnt);
+  if (pos < cnt) {
+    int mt, vt;
+    group_coords(lo + pos, p.dl.n_mt, p.dl.n_vt, 8, mt, vt);
+    dlogits_tile<ENTGRAD>(p.dl, mt, vt, smem);
   }
 }
 
@@ -1624,6 +1689,16 @@ hipError_t launch_dlogits(const DlogitsArgs& a, bool entgrad, hipStream_t s) {
     bwd_dlogits_kernel<true><<<g, NTHREADS, 0, s>>>(a);
   else
     bwd_dlogits_kernel<false><<<g, NTHREADS, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pipe(const PipeArgs& a, bool entgrad, hipStream_t s) {
+  const long per = (a.n_dw + 7) / 8 + (a.n_dx + 7) / 8 + (a.n_dl + 7) / 8;
+  if (per == 0) return hipSuccess;
+  if (entgrad)
+    bwd_pipe_kernel<true><<<(unsigned)(8 * per), NTHREADS, 0, s>>>(a);
+  else
+    bwd_pipe_kernel<false><<<(unsigned)(8 * per), NTHREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 

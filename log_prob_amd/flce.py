@@ -22,7 +22,8 @@ STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_INVALID_VALUE", 2: "FLCE_ERR_UNSUPPORTED",
 # Every symbol include/flce.h declares.
 EXPORTS = ("flce_workspace_query", "flce_forward_workspace_min", "flce_forward_wave_rows",
            "flce_backward_workspace_min", "flce_backward_chunk_cols",
-           "flce_backward_wave_rows", "flce_forward", "flce_forward_noalloc", "flce_forward_partials", "flce_forward_merge", "flce_backward",
+           "flce_backward_wave_rows", "flce_backward_schedule", "flce_forward",
+           "flce_forward_noalloc", "flce_forward_partials", "flce_forward_merge", "flce_backward",
            "flce_forward_partials_shard", "flce_forward_merge_shards",
            "flce_backward_shard_workspace_query", "flce_backward_shard", "flce_nll_reduce",
            "flce_nll_mean_grad", "flce_policy_loss_reduce", "flce_policy_loss_grad",
@@ -54,6 +55,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.flce_backward_workspace_min.argtypes = [I64, I64, I64, c.POINTER(SZ)]
     lib.flce_backward_chunk_cols.argtypes = [I64, I64, I64, SZ, c.POINTER(I64)]
     lib.flce_backward_wave_rows.argtypes = [I64, I64, I64, SZ, c.POINTER(I64)]
+    lib.flce_backward_schedule.argtypes = [I64, I64, I64, SZ, c.POINTER(I64), c.POINTER(I64),
+                                           c.POINTER(c.c_int)]
     lib.flce_forward.argtypes = [P, P, P, I64, I64, I64, I64, c.c_float, c.c_int, P, P, P, P, SZ, P]
     lib.flce_forward_noalloc.argtypes = [P, P, P, I64, I64, I64, I64, c.c_float, c.c_int, P, P, P,
                                          P]
@@ -79,7 +82,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "flce_policy_loss_grad", "flce_workspace_query",
                  "flce_forward_workspace_min", "flce_forward_wave_rows",
                  "flce_backward_workspace_min", "flce_backward_chunk_cols",
-                 "flce_backward_wave_rows", "flce_forward", "flce_forward_noalloc", "flce_forward_partials", "flce_forward_merge", "flce_backward",
+                 "flce_backward_wave_rows", "flce_backward_schedule", "flce_forward",
+           "flce_forward_noalloc", "flce_forward_partials", "flce_forward_merge", "flce_backward",
                  "flce_forward_partials_shard", "flce_forward_merge_shards",
                  "flce_backward_shard_workspace_query", "flce_backward_shard"):
         getattr(lib, name).restype = c.c_int
@@ -135,6 +139,14 @@ def backward_wave_rows(M: int, H: int, V: int, workspace_bytes: int) -> int:
     r = ctypes.c_int64()
     _check(load().flce_backward_wave_rows(M, H, V, workspace_bytes, ctypes.byref(r)))
     return r.value
+
+
+def backward_schedule(M: int, H: int, V: int, workspace_bytes: int):
+    """(rows per token wave, chunk columns, pipelined) of flce_backward's schedule."""
+    r, cc, pp = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int()
+    _check(load().flce_backward_schedule(M, H, V, workspace_bytes, ctypes.byref(r),
+                                         ctypes.byref(cc), ctypes.byref(pp)))
+    return r.value, cc.value, bool(pp.value)
 
 
 def backward_shard_workspace_query(M: int, H: int, V_shard: int) -> Tuple[int, int]:

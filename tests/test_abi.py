@@ -345,3 +345,19 @@ def test_backward_schedule_sizes(M, H, V):
         flce.backward_wave_rows(M, H, V, lo - 1)
     with pytest.raises(flce.FlceError):
         flce.backward_chunk_cols(M, H, V, lo - 1)
+
+
+def test_backward_schedule_choices():
+    """The smallest workspace runs three launches per step (the two d-logit buffers of a
+    pipelined schedule need more); the preferred one pipelines small steps (M = H = 4096,
+    V = 32768: one step of 3.3e12 FLOP) and not large ones (M = H = 8192, V = 131072)."""
+    for M, H, V in ((4096, 4096, 32768), (8192, 8192, 131072), (600, 136, 3000)):
+        lo = flce.backward_workspace_min(M, H, V)
+        assert flce.backward_schedule(M, H, V, lo)[2] is False
+    assert flce.backward_schedule(4096, 4096, 32768,
+                                  flce.workspace_query(4096, 4096, 32768)[1]) == (4096, 32768, True)
+    assert flce.backward_schedule(8192, 8192, 131072,
+                                  flce.workspace_query(8192, 8192, 131072)[1]) == (8192, 131072, False)
+    rows, chunk, _ = flce.backward_schedule(600, 136, 3000, 1 << 30)
+    assert (rows, chunk) == (flce.backward_wave_rows(600, 136, 3000, 1 << 30),
+                             flce.backward_chunk_cols(600, 136, 3000, 1 << 30))
