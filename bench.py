@@ -106,9 +106,10 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per fwd_tile launch from the committed rocprofv3 counter summary, or
-    None if the kernel sources changed since those counters were taken."""
+def profile_figures():
+    """From the committed rocprofv3 summary: HBM bytes per fwd_tile launch (counters)
+    and the traced average duration of the launches the roofline loop times; both None
+    if the kernel sources changed since that profile was taken."""
     try:
         kv = {}
         with open(PROFILE) as f:
@@ -117,10 +118,11 @@ def measured_traffic():
                     k, v = line.split(":", 1)
                     kv[k.strip()] = v.strip()
         if kv.get("kernel_source_sha256") != kernel_source_hash():
-            return None
-        return float(kv["fwd_tile_traffic_bytes_per_launch"])
+            return None, None
+        return (float(kv["fwd_tile_traffic_bytes_per_launch"]),
+                float(kv.get("fwd_tile_roofline_loop_avg_ms", "nan")))
     except (OSError, KeyError, ValueError):
-        return None
+        return None, None
 
 
 def copy_probe(mib):
@@ -328,6 +330,7 @@ def main():
                                "fwd_bwd_tflops": round(8.0 * M * H * Vs / ((sf + sb) * 1e-3) / 1e12, 2)}
         del gathered
 
+    traffic, prof_ms = profile_figures()
     flop_f = 2.0 * M * H * V
     flop_fb = 8.0 * M * H * V
     tf_fb = flop_fb / (ms * 1e-3) / 1e12
@@ -366,10 +369,15 @@ def main():
         "vocab_shard_rank": shard_out,
         "roofline": {"bound": "mfma", "kernel": "fwd_tile_kernel (fused GEMM + online softmax)",
                      "achieved": round(k_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(k_tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                     "frac": round(k_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "traffic_unit": "HBM bytes/launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, scaled)",
                      "algorithmic_bytes": 2 * M * H + 2 * V * H + 8 * M + 12 * M,
-                     "avg_launch_ms": round(k_avg, 4), "flops_per_launch": flop_f},
+                     "avg_launch_ms": round(k_avg, 4), "flops_per_launch": flop_f,
+                     "profile_avg_launch_ms": prof_ms,
+                     "note": "achieved = flops_per_launch / avg_launch_ms, HIP events around "
+                             "each of the last steps launches (the forward kernel plus the "
+                             "0.04 ms target-logit kernel); profile_avg_launch_ms = the same "
+                             "launches in the committed rocprofv3 trace of this command"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
