@@ -75,10 +75,13 @@ typedef enum {
  * flce_backward (*bwd_bytes) for this problem shape.  One buffer of
  * max(*fwd_bytes, *bwd_bytes) serves both.  Either output pointer may be NULL.
  * Sizes accepted by every call: 0 <= M <= 2^30 (M = 0 is an empty batch),
- * 8 <= H <= 2^20 with H % 8 == 0, 1 <= V <= 2^30, and at most 2^31 - 1 workgroups
- * per launch (ceil(M / 256) * ceil(V / 256) and ceil(V / 256) * ceil(H / 256)).
- * Negative M, or H or V <= 0: FLCE_ERR_INVALID_VALUE; larger sizes, or H not a
- * multiple of 8: FLCE_ERR_UNSUPPORTED.
+ * 8 <= H <= 2^20 with H % 8 == 0, 1 <= V <= 2^30.  Negative M, or H or V <= 0:
+ * FLCE_ERR_INVALID_VALUE; larger sizes, or H not a multiple of 8:
+ * FLCE_ERR_UNSUPPORTED.  A dispatch covers at most 2^32 - 1 work-items, so very
+ * large problems run in more token waves (and narrower chunks) than the workspace
+ * alone would need; *fwd_bytes is the size of the tallest such forward wave.  The
+ * one-launch calls (flce_forward_partials and its shard form, flce_forward_merge)
+ * return FLCE_ERR_UNSUPPORTED for a batch taller than one launch can take.
  */
 flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_entropy,
                                    size_t* fwd_bytes, size_t* bwd_bytes);

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdint>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -33,7 +34,10 @@ constexpr int64_t kTile = flce::kTile;
 constexpr int64_t kMaxM = int64_t(1) << 30;
 constexpr int64_t kMaxV = int64_t(1) << 30;
 constexpr int64_t kMaxH = int64_t(1) << 20;
-constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+// A dispatch covers at most 2^32 - 1 work-items per dimension: the tile kernels run
+// 256 threads per workgroup, the target-logit kernel 64 per row, the merge 8 per row.
+constexpr int64_t kMaxWorkgroups = 0xFFFFFFFFLL / 256;
+constexpr int64_t kMaxWaveRows = (0xFFFFFFFFLL / 64) / 256 * 256;
 constexpr size_t kAlign = 256;
 // Preferred size of one d-logit chunk buffer: 4 GiB.  Wider chunks mean fewer passes
 // over the fp32 dX accumulator and fewer launches; past about 2000 K steps the dX GEMM's
@@ -60,10 +64,6 @@ flce_status_t check_shape(int64_t M, int64_t H, int64_t V) {
     return fail(FLCE_ERR_UNSUPPORTED, "shape too large (limits M, V <= 2^30, H <= 2^20)");
   if (H % 8 != 0)
     return fail(FLCE_ERR_UNSUPPORTED, "H must be a multiple of 8 (got %lld)", (long long)H);
-  const int64_t n_mt = cdiv(M, kTile), n_vt = cdiv(V, kTile), n_ht = cdiv(H, kTile);
-  if (cdiv(M, flce::kFwdTileM) * cdiv(V, flce::kFwdTileN) > kMaxGrid || n_mt * n_vt > kMaxGrid ||
-      n_vt * n_ht > kMaxGrid)
-    return fail(FLCE_ERR_UNSUPPORTED, "shape needs more than 2^31 - 1 workgroups");
   return FLCE_OK;
 }
 
@@ -87,10 +87,19 @@ FwdLayout fwd_layout(int64_t rows, int64_t V, bool ent) {
   return L;
 }
 
-// Tallest wave (a multiple of 256 rows, at most Mpad) whose forward partials fit in
-// `bytes`; 0 if not even one 256-row wave fits.
+// Tallest forward wave one set of launches can take: the tile grid and the per-row
+// kernels within the dispatch limits (at least 256 rows for every V <= 2^30).
+int64_t max_wave_rows(int64_t V) {
+  const int64_t by_grid = kMaxWorkgroups / cdiv(V, flce::kFwdTileN) * flce::kFwdTileM;
+  const int64_t r = by_grid < kMaxWaveRows ? by_grid : kMaxWaveRows;
+  return r / kTile * kTile;
+}
+
+// Tallest wave (a multiple of 256 rows, at most Mpad and max_wave_rows) whose forward
+// partials fit in `bytes`; 0 if not even one 256-row wave fits.
 int64_t wave_rows_for_workspace(int64_t M, int64_t V, bool ent, size_t bytes) {
-  const int64_t Mpad = cdiv(M, kTile) * kTile;
+  int64_t Mpad = cdiv(M, kTile) * kTile;
+  if (Mpad > max_wave_rows(V)) Mpad = max_wave_rows(V);
   if (fwd_layout(Mpad, V, ent).total <= bytes) return Mpad;
   int64_t lo = 0, hi = Mpad / kTile;  // in tiles: lo fits (or 0), hi does not
   while (hi - lo > 1) {
@@ -119,6 +128,15 @@ struct BwdPlan {
 // Steps (token waves x vocabulary chunks) of a schedule.
 int64_t plan_steps(int64_t M, int64_t V, int64_t rows, int64_t chunk) {
   return cdiv(M, rows) * cdiv(cdiv(V, kTile) * kTile, chunk);
+}
+
+// Every launch of a schedule within the dispatch limits: the d-logit, dW and dX grids
+// of the largest step (their sum when pipelined).
+bool grids_ok(int64_t H, int64_t rows, int64_t chunk, bool pipe) {
+  const int64_t n_mt = cdiv(rows, kTile), n_ct = cdiv(chunk, kTile), n_ht = cdiv(H, kTile);
+  const int64_t dl = n_mt * n_ct, dw = n_ct * n_ht, dx = n_mt * n_ht;
+  if (pipe) return dl + dw + dx + 24 <= kMaxWorkgroups;
+  return dl <= kMaxWorkgroups && dw <= kMaxWorkgroups && dx <= kMaxWorkgroups;
 }
 
 BwdPlan bwd_plan(int64_t M, int64_t H, int64_t V, int64_t rows, int64_t chunk, bool dx_bf16,
@@ -152,7 +170,11 @@ BwdPlan bwd_plan(int64_t M, int64_t H, int64_t V, int64_t rows, int64_t chunk, b
 int64_t widest_chunk(int64_t M, int64_t H, int64_t V, int64_t rows, bool dx_bf16, bool pipe,
                      size_t bytes) {
   const int64_t Vpad = cdiv(V, kTile) * kTile;
-  if (Vpad <= kMaxChunk && bwd_plan(M, H, V, rows, Vpad, dx_bf16, pipe).total <= bytes)
+  const int64_t Mpad = cdiv(M, kTile) * kTile;
+  const int64_t R = rows < Mpad ? rows : Mpad;
+  if (!grids_ok(H, R, kTile, pipe)) return 0;
+  if (Vpad <= kMaxChunk && grids_ok(H, R, Vpad, pipe) &&
+      bwd_plan(M, H, V, rows, Vpad, dx_bf16, pipe).total <= bytes)
     return Vpad;
   // narrower chunks: the size grows with the chunk from here on
   const BwdPlan p0 = bwd_plan(M, H, V, rows, kTile, dx_bf16, pipe);
@@ -161,6 +183,11 @@ int64_t widest_chunk(int64_t M, int64_t H, int64_t V, int64_t rows, bool dx_bf16
   int64_t c = int64_t((bytes - fixed) / (size_t(p0.nbuf) * size_t(p0.rows) * 2)) / kTile * kTile;
   const int64_t cap = (Vpad <= kMaxChunk ? Vpad - kTile : kMaxChunk);
   if (c > cap) c = cap;
+  // the chunk's tile columns within the dispatch limits (for the d-logit and dW grids)
+  const int64_t n_mt = cdiv(R, kTile), n_ht = cdiv(H, kTile);
+  const int64_t by_grid = (pipe ? (kMaxWorkgroups - 24 - n_mt * n_ht) / (n_mt + n_ht)
+                                : kMaxWorkgroups / (n_mt > n_ht ? n_mt : n_ht)) * kTile;
+  if (c > by_grid) c = by_grid / kTile * kTile;
   while (c > kTile && bwd_plan(M, H, V, rows, c, dx_bf16, pipe).total > bytes) c -= kTile;
   return c >= kTile ? c : 0;
 }
@@ -235,11 +262,17 @@ int64_t preferred_chunk(int64_t M, int64_t V) {
 size_t bwd_min_bytes(int64_t M, int64_t H, int64_t V, bool dx_bf16) {
   const int64_t Mpad = cdiv(M, kTile) * kTile;
   const int64_t Vpad = cdiv(V, kTile) * kTile;
-  size_t m = bwd_plan(M, H, V, Mpad, kTile, dx_bf16, false).total;
-  if (Vpad <= kMaxChunk) m = std::min(m, bwd_plan(M, H, V, Mpad, Vpad, dx_bf16, false).total);
+  size_t m = SIZE_MAX;
+  auto take = [&](int64_t rows, int64_t chunk) {
+    const int64_t R = rows < Mpad ? rows : Mpad;
+    if (Mpad == 0 || grids_ok(H, R, chunk, false))
+      m = std::min(m, bwd_plan(M, H, V, rows, chunk, dx_bf16, false).total);
+  };
+  take(Mpad, kTile);
+  if (Vpad <= kMaxChunk) take(Mpad, Vpad);
   if (Mpad > kTile) {
-    m = std::min(m, bwd_plan(M, H, V, kTile, kTile, dx_bf16, false).total);
-    if (Vpad <= kMaxChunk) m = std::min(m, bwd_plan(M, H, V, kTile, Vpad, dx_bf16, false).total);
+    take(kTile, kTile);
+    if (Vpad <= kMaxChunk) take(kTile, Vpad);
   }
   return m;
 }
@@ -294,7 +327,10 @@ flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_
     return fail(FLCE_ERR_INVALID_VALUE, "compute_entropy must be 0 or 1");
   flce_status_t st = check_shape(M, H, V);
   if (st != FLCE_OK) return st;
-  if (fwd_bytes) *fwd_bytes = fwd_layout(M, V, compute_entropy == 1).total;
+  if (fwd_bytes) {
+    const int64_t cap = max_wave_rows(V);
+    *fwd_bytes = fwd_layout(M < cap ? M : cap, V, compute_entropy == 1).total;
+  }
   if (bwd_bytes)
     *bwd_bytes =
         bwd_plan(M, H, V, cdiv(M, kTile) * kTile, preferred_chunk(M, V), true, false).total;
@@ -391,6 +427,11 @@ flce_status_t check_forward_common(const int64_t* targets, int64_t M, int64_t H,
   if (!aligned(targets, 8)) return fail(FLCE_ERR_UNSUPPORTED, "targets must be 8-byte aligned");
   if (!aligned(workspace, kAlign))
     return fail(FLCE_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  if (M > max_wave_rows(V))
+    return fail(FLCE_ERR_UNSUPPORTED,
+                "%lld rows over V=%lld exceed one launch (at most %lld rows); flce_forward "
+                "runs such batches in token waves", (long long)M, (long long)V,
+                (long long)max_wave_rows(V));
   *L = fwd_layout(M, V, compute_entropy == 1);
   if (workspace_bytes < L->total)
     return fail(FLCE_ERR_WORKSPACE_TOO_SMALL, "forward needs %zu workspace bytes, got %zu",
@@ -529,6 +570,9 @@ flce_status_t flce_forward_merge_shards(const int64_t* targets, int64_t M, int64
                 (long long)n_shards);
   if (compute_entropy != 0 && compute_entropy != 1)
     return fail(FLCE_ERR_INVALID_VALUE, "compute_entropy must be 0 or 1");
+  if (M > kMaxWaveRows)
+    return fail(FLCE_ERR_UNSUPPORTED, "M=%lld exceeds one merge launch (at most %lld rows)",
+                (long long)M, (long long)kMaxWaveRows);
   if (shard_offsets[0] != 0)
     return fail(FLCE_ERR_INVALID_VALUE, "shard_offsets[0] must be 0 (got %lld)",
                 (long long)shard_offsets[0]);

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from log_prob_amd import flce
@@ -323,8 +324,36 @@ def test_size_limits_match_the_header():
     assert q(1, 8, 1 << 30) == 0 and q(1, 8, (1 << 30) + 1) == 2
     assert q(-1, 8, 1) == 1 and q(1, 0, 1) == 1 and q(1, 8, 0) == 1
     assert q(1, 4, 1) == 2 and q(1, 12, 1) == 2
-    # more than 2^31 - 1 workgroups of 256 x 256 tiles
-    assert q(1 << 30, 8, 1 << 18) == 2
+
+
+MAX_WG = 0xFFFFFFFF // 256      # workgroups of 256 threads in one dispatch
+
+
+@pytest.mark.parametrize("M,H,V", [(1 << 30, 8, 1 << 18), (1 << 20, 1 << 20, 1 << 20),
+                                   ((1 << 26) + 5, 64, 3000), (1 << 30, 1 << 20, 1)])
+def test_every_launch_within_the_dispatch_limit(M, H, V):
+    """Shapes whose single-launch grids would pass 2^32 work-items: the forward and the
+    backward plan smaller token waves (and chunks) so that every grid fits; the
+    one-launch partials call refuses them."""
+    big = 1 << 62
+    rows = flce.forward_wave_rows(M, H, V, big)
+    n_vt = -(-V // 256)
+    assert rows % 256 == 0 and 256 <= rows and (rows // 256) * n_vt <= MAX_WG
+    assert rows * 64 <= 0xFFFFFFFF                      # the target-logit kernel's grid
+    fb, _ = flce.workspace_query(M, H, V, True)
+    assert flce.forward_wave_rows(M, H, V, fb) == rows  # the preferred size is one such wave
+    r, c, pipe = flce.backward_schedule(M, H, V, big)
+    n_mt, n_ct, n_ht = -(-r // 256), -(-c // 256), -(-H // 256)
+    grids = (n_mt * n_ct, n_ct * n_ht, n_mt * n_ht)
+    assert (sum(grids) + 24 if pipe else max(grids)) <= MAX_WG, (r, c, pipe, grids)
+    lo = flce.backward_workspace_min(M, H, V)
+    r, c, pipe = flce.backward_schedule(M, H, V, lo)
+    n_mt, n_ct = -(-r // 256), -(-c // 256)
+    assert max(n_mt * n_ct, n_ct * n_ht, n_mt * n_ht) <= MAX_WG
+    lib = flce.load()
+    if -(-M // 256) * n_vt > MAX_WG:
+        assert lib.flce_forward_partials(16, 16, 16, M, H, V, -100, 1.0, 1, 256, big, None) == 2
+        assert b"waves" in lib.flce_last_error_message()
 
 
 @pytest.mark.parametrize("M,H,V", [(4096, 4096, 512), (4097, 64, 1000), (600, 136, 3000),
@@ -361,3 +390,44 @@ def test_backward_schedule_choices():
     rows, chunk, _ = flce.backward_schedule(600, 136, 3000, 1 << 30)
     assert (rows, chunk) == (flce.backward_wave_rows(600, 136, 3000, 1 << 30),
                              flce.backward_chunk_cols(600, 136, 3000, 1 << 30))
+
+
+def _schedule_bytes(M, H, V, rows, chunk, pipe):
+    """Workspace a schedule uses, from its description in include/flce.h: the bf16
+    d-logits of one wave over one chunk (two buffers when pipelined over more than one
+    step), the fp32 dX accumulator of one wave when a wave takes several chunks, the fp32
+    dW accumulator when there are several waves; each part rounded up to 256 bytes."""
+    up = lambda x: -(-x // 256) * 256
+    Mpad, Vpad = up(M), up(V)
+    steps = -(-M // rows) * -(-Vpad // chunk)
+    b = (2 if pipe and steps > 1 else 1) * up(rows * chunk * 2)
+    if chunk < Vpad:
+        b += up(min(rows, M) * H * 4)
+    if rows < Mpad:
+        b += up(V * H * 4)
+    return b
+
+
+def test_backward_schedules_fit_their_workspace():
+    """Seeded random shapes and workspace sizes: the reported schedule fits the bytes
+    given, keeps every launch within the dispatch limit, and pipelines only small steps;
+    below the minimum the call is refused."""
+    rng = np.random.default_rng(20261202)
+    for _ in range(400):
+        M = int(rng.choice([int(rng.integers(1, 2000)), int(rng.integers(1, 1 << 22))]))
+        H = 8 * int(rng.integers(1, 1 << int(rng.integers(3, 14))))
+        V = int(rng.choice([int(rng.integers(1, 5000)), int(rng.integers(1, 1 << 21))]))
+        lo = flce.backward_workspace_min(M, H, V)
+        _, pref = flce.workspace_query(M, H, V, True)
+        for b in (lo, int(rng.integers(lo, 2 * pref + 2)), pref):
+            rows, chunk, pipe = flce.backward_schedule(M, H, V, b)
+            Mpad = -(-M // 256) * 256
+            assert rows % 256 == 0 and chunk % 256 == 0 and 256 <= rows <= Mpad
+            assert _schedule_bytes(M, H, V, rows, chunk, pipe) <= b, (M, H, V, b, rows, chunk, pipe)
+            n_mt, n_ct, n_ht = rows // 256, chunk // 256, -(-H // 256)
+            grids = (n_mt * n_ct, n_ct * n_ht, n_mt * n_ht)
+            assert (sum(grids) + 24 if pipe else max(grids)) <= MAX_WG
+            if pipe:
+                assert 6.0 * rows * H * chunk <= 8e12
+        with pytest.raises(flce.FlceError):
+            flce.backward_schedule(M, H, V, lo - 1)
