@@ -330,7 +330,8 @@ def main():
                                "fwd_bwd_tflops": round(8.0 * M * H * Vs / ((sf + sb) * 1e-3) / 1e12, 2)}
         del gathered
 
-    traffic, prof_ms = profile_figures()
+    # the committed profile covers the bench workload only
+    traffic, prof_ms = profile_figures() if cfg == 4 else (None, None)
     flop_f = 2.0 * M * H * V
     flop_fb = 8.0 * M * H * V
     tf_fb = flop_fb / (ms * 1e-3) / 1e12

@@ -131,12 +131,17 @@ def test_config_full_size(cfg):
         o = ref.forward(case.X, case.W, case.targets, case.ignore_index, case.scale, True)
         rdX, rdW = ref.backward(case.X, case.W, case.targets, case.ignore_index, case.scale,
                                 case.grad_logprob, case.grad_entropy)
-        gu.check_forward(res, o, case.compute_entropy, "config1")
-        gu.check_grads(gdX, gu.bits_to_np(res["dW"]), rdX, rdW, "config1")
+        e_lp, e_lse = gu.check_forward(res, o, case.compute_entropy, "config1")
+        ex, ew = gu.check_grads(gdX, gu.bits_to_np(res["dW"]), rdX, rdW, "config1")
+        print(f"[configs] config 1: forward max-abs logprob {e_lp:.3g} lse {e_lse:.3g}; "
+              f"whole-tensor rel dX {ex:.3g} dW {ew:.3g}", flush=True)
         return
     g = golden(cfg)
     assert str(g["fingerprint"]) == _fingerprint(case), "inputs differ from the golden run"
-    gu.check_forward(res, g, case.compute_entropy, f"config{cfg}")
+    e_lp, e_lse = gu.check_forward(res, g, case.compute_entropy, f"config{cfg}")
+    e_ent = gu.max_abs(res["entropy"], g["entropy"]) if case.compute_entropy else 0.0
+    print(f"[configs] config {cfg}: forward max-abs logprob {e_lp:.3g} lse {e_lse:.3g} "
+          f"entropy {e_ent:.3g}", flush=True)
     # every row's largest gradient magnitude, against the oracle's full backward
     ex = float(np.max(np.abs(res["dx_rowmax"] - g["dx_rowmax"]))) / float(g["dx_absmax"])
     ew = float(np.max(np.abs(res["dw_rowmax"] - g["dw_rowmax"]))) / float(g["dw_absmax"])
