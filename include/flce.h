@@ -99,16 +99,18 @@ flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_
  * (*bwd_bytes of flce_workspace_query) is one wave of every row with up to 4 GiB of
  * d-logits per chunk (every column at once when they fit).  With less, the call
  * takes the schedule that fits and moves the fewest extra bytes: narrower chunks, or
- * waves of 256 to 16384 rows.  A step (one wave over one chunk) of at most 8e12 FLOP
- * (6 x rows x H x chunk) runs pipelined when two d-logit buffers fit: one launch per
- * step computes the step's dW and dX together with the next step's d-logits.  The minimum is the smallest of: one wave with
- * 256-column chunks (d-logits + fp32 dX accumulator of M rows), one wave with every
- * column (d-logits only), 256-row waves with 256-column chunks or with every column
- * (+ the fp32 dW accumulator): once M > 256 it is at most 4 V H + 1024 H + 131072
- * bytes (each part rounded up to 256 bytes), whatever M.  Results of different
- * schedules differ only by fp32
- * summation order (dX across chunks, dW across waves); every schedule is
- * deterministic.
+ * waves of 256 to 16384 rows.  Schedules whose steps (one wave over one chunk) are at
+ * most 8e12 FLOP (6 x rows x H x chunk) may also run pipelined when two d-logit
+ * buffers fit: one launch per step computes the step's dW and dX together with the
+ * next step's d-logits; the same fewest-extra-bytes rule, which counts launches,
+ * picks between the kinds.  The minimum is the smallest of: one wave with 256-column
+ * chunks (d-logits + fp32 dX accumulator of M rows), one wave with every column
+ * (d-logits only), 256-row waves with 256-column chunks or with every column (+ the
+ * fp32 dW accumulator): once M > 256 it is at most 4 V H + 1024 H + 131072 bytes (each
+ * part rounded up to 256 bytes), whatever M.  Results of different schedules differ
+ * only by fp32 summation order (dX across chunks, dW across waves); every schedule is
+ * deterministic, and a pipelined schedule gives the same bits as three launches per
+ * step with the same waves and chunks.
  */
 flce_status_t flce_backward_workspace_min(int64_t M, int64_t H, int64_t V, size_t* bytes);
 
