@@ -94,8 +94,9 @@ flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_
  * dW stored by the first wave and added to by later ones; Liger-Kernel PR 1294,
  * "Kernel design notes": d-logits in the input dtype in a reusable buffer).  The
  * workspace holds the bf16 d-logits of one wave over one chunk; an fp32 dX
- * accumulator for one wave's rows when a wave takes more than one chunk; and, when
- * there is more than one wave, an fp32 dW accumulator of V x H.  The preferred size
+ * accumulator for one wave's rows when a wave takes more than one chunk; when
+ * there is more than one wave, an fp32 dW accumulator of V x H; and 256 bytes of
+ * counters with which the d-logit and dW kernels hand out their last tiles.  The preferred size
  * (*bwd_bytes of flce_workspace_query) is one wave of every row with up to 4 GiB of
  * d-logits per chunk (every column at once when they fit).  With less, the call
  * takes the schedule that fits and moves the fewest extra bytes: narrower chunks, or
@@ -106,7 +107,7 @@ flce_status_t flce_workspace_query(int64_t M, int64_t H, int64_t V, int compute_
  * picks between the kinds.  The minimum is the smallest of: one wave with 256-column
  * chunks (d-logits + fp32 dX accumulator of M rows), one wave with every column
  * (d-logits only), 256-row waves with 256-column chunks or with every column (+ the
- * fp32 dW accumulator): once M > 256 it is at most 4 V H + 1024 H + 131072 bytes (each
+ * fp32 dW accumulator): once M > 256 it is at most 4 V H + 1024 H + 131328 bytes (each
  * part rounded up to 256 bytes), whatever M.  Results of different schedules differ
  * only by fp32 summation order (dX across chunks, dW across waves); every schedule is
  * deterministic, and a pipelined schedule gives the same bits as three launches per
@@ -138,7 +139,8 @@ flce_status_t flce_backward_wave_rows(int64_t M, int64_t H, int64_t V, size_t wo
  * the Liger-Kernel commit "native Blackwell tensor-parallel fused scaled linear
  * cross-entropy", sections "Summary" and "Correctness": 4K waves, two-wave tails):
  * a wave is a multiple of 256 rows whose per-tile partials (12 bytes per row per
- * 256 vocabulary columns with entropy, 8 without) fit in the workspace.  The size
+ * 256 vocabulary columns with entropy, 8 without), target logits (4 bytes per row)
+ * and 256 bytes of tile-queue counters fit in the workspace.  The size
  * from flce_workspace_query takes all rows in one wave; the minimum takes 256.
  * Results are bitwise identical for every wave height: a row's tiles and merge do
  * not depend on the wave it falls in.
@@ -197,7 +199,8 @@ flce_status_t flce_forward_noalloc(const void* X, const void* W, const int64_t* 
  *   (n_vt + j) * Mpad + m              sum_v exp(z[m, v] - max)
  *   (2 n_vt + j) * Mpad + m            sum_v exp(z[m, v] - max) (z[m, v] - max)  (entropy only)
  * and after the 2 (or 3) partial arrays (each rounded up to 256 bytes) the
- * target logit z[m, t[m]] of every valid row.  flce_forward_merge turns them into
+ * target logit z[m, t[m]] of every valid row (Mpad floats, rounded up to 256 bytes),
+ * then the 256 bytes of counters with which the tile kernel hands out its last tiles.  flce_forward_merge turns them into
  * logprob, lse and entropy; its arguments must match the partials call.
  */
 flce_status_t flce_forward_partials(const void* X, const void* W, const int64_t* targets,

@@ -36,7 +36,7 @@ constexpr int64_t kMaxV = int64_t(1) << 30;
 constexpr int64_t kMaxH = int64_t(1) << 20;
 // A dispatch covers at most 2^32 - 1 work-items per dimension: the tile kernels run
 // 256 threads per workgroup, the target-logit kernel 64 per row, the merge 8 per row.
-constexpr int64_t kMaxWorkgroups = 0xFFFFFFFFLL / 256;
+constexpr int64_t kMaxWorkgroups = flce::kMaxWorkgroups;
 constexpr int64_t kMaxWaveRows = (0xFFFFFFFFLL / 64) / 256 * 256;
 constexpr size_t kAlign = 256;
 // Preferred size of one d-logit chunk buffer: 4 GiB.  Wider chunks mean fewer passes
@@ -69,7 +69,7 @@ flce_status_t check_shape(int64_t M, int64_t H, int64_t V) {
 
 struct FwdLayout {
   int64_t n_mt, n_vt, Mpad;
-  size_t off_m, off_s, off_u, off_zt, total;
+  size_t off_m, off_s, off_u, off_zt, off_q, total;
 };
 
 // Forward workspace for a wave of `rows` token rows (rows <= Mpad of the call).
@@ -83,7 +83,8 @@ FwdLayout fwd_layout(int64_t rows, int64_t V, bool ent) {
   L.off_s = part;
   L.off_u = 2 * part;
   L.off_zt = (ent ? 3 : 2) * part;
-  L.total = L.off_zt + align_up(size_t(L.Mpad) * sizeof(float));
+  L.off_q = L.off_zt + align_up(size_t(L.Mpad) * sizeof(float));
+  L.total = L.Mpad > 0 ? L.off_q + flce::kQueueBytes : 0;  // no rows: no launch
   return L;
 }
 
@@ -122,7 +123,7 @@ struct BwdPlan {
   bool pipe = false;               // grouped launches over two d-logit buffers
   int nbuf = 1;                    // d-logit buffers
   bool dx_acc = false, dw_acc = false;
-  size_t dz_bytes = 0, off_dx = 0, off_dw = 0, total = 0;
+  size_t dz_bytes = 0, off_dx = 0, off_dw = 0, off_q = 0, total = 0;
 };
 
 // Steps (token waves x vocabulary chunks) of a schedule.
@@ -161,7 +162,8 @@ BwdPlan bwd_plan(int64_t M, int64_t H, int64_t V, int64_t rows, int64_t chunk, b
     p.off_dw = b;
     b += align_up(size_t(V) * size_t(H) * sizeof(float));
   }
-  p.total = b;
+  p.off_q = b;
+  p.total = Mpad > 0 ? b + flce::kQueueBytes : 0;  // no rows: no launch
   return p;
 }
 
@@ -475,6 +477,7 @@ flce::FwdTileArgs tile_args(const void* X, const void* W, const int64_t* targets
   a.part_s = reinterpret_cast<float*>(ws + L.off_s);
   a.part_u = ent ? reinterpret_cast<float*>(ws + L.off_u) : nullptr;
   a.zt = reinterpret_cast<float*>(ws + L.off_zt);
+  a.tq.ctr = reinterpret_cast<unsigned long long*>(ws + L.off_q);
   return a;
 }
 
@@ -540,10 +543,11 @@ flce_status_t flce_forward_partials_shard(const void* X, const void* W_shard,
   const flce::FwdTileArgs a = tile_args(X, W_shard, targets, M, H, V_shard, v_offset,
                                         ignore_index, scale, ent, L,
                                         static_cast<char*>(workspace));
-  hipError_t e = flce::launch_fwd_tile(a, ent, stream);
-  if (e != hipSuccess) return hip_fail(e, "forward tile kernel launch");
-  e = flce::launch_target_logit(a, stream);
+  // the target-logit kernel first: it zeroes the tile kernel's queue counters
+  hipError_t e = flce::launch_target_logit(a, stream);
   if (e != hipSuccess) return hip_fail(e, "target logit kernel launch");
+  e = flce::launch_fwd_tile(a, ent, stream);
+  if (e != hipSuccess) return hip_fail(e, "forward tile kernel launch");
   return ok();
 }
 
@@ -659,10 +663,10 @@ flce_status_t forward_waves(const void* X, const void* W, const int64_t* targets
     const flce::FwdTileArgs a =
         tile_args(static_cast<const uint16_t*>(X) + r0 * H, W, targets + r0, mw, H, V, 0,
                   ignore_index, scale, ent, L, ws);
-    hipError_t e = flce::launch_fwd_tile(a, ent, stream);
-    if (e != hipSuccess) return hip_fail(e, "forward tile kernel launch");
-    e = flce::launch_target_logit(a, stream);
+    hipError_t e = flce::launch_target_logit(a, stream);  // zeroes the queue counters
     if (e != hipSuccess) return hip_fail(e, "target logit kernel launch");
+    e = flce::launch_fwd_tile(a, ent, stream);
+    if (e != hipSuccess) return hip_fail(e, "forward tile kernel launch");
     const flce::FwdMergeArgs b =
         merge_args_single(targets + r0, mw, V, ignore_index, ent, logprob + r0, lse + r0,
                           ent ? entropy + r0 : nullptr, L, ws);
@@ -841,9 +845,20 @@ flce_status_t backward_run(const void* X, const void* W, const int64_t* targets,
   };
 
   if (!P.pipe) {
+    // queue counters: the d-logit launches use q0 and zero q1, the dW launches use q1 and
+    // zero q0, so each starts from zero; q0 is zeroed here for the first step
+    unsigned long long* q0 = reinterpret_cast<unsigned long long*>(ws + P.off_q);
+    unsigned long long* q1 = q0 + 8;
+    hipError_t e = flce::launch_fill_zero_u16(reinterpret_cast<uint16_t*>(q0),
+                                              long(8 * sizeof(*q0) / 2), stream);
+    if (e != hipSuccess) return hip_fail(e, "zero-fill kernel launch");
     for (int64_t k = 0; k < steps; ++k) {
-      const Step s = step_args(k);
-      hipError_t e = flce::launch_dlogits(s.d, entgrad, stream);
+      Step s = step_args(k);
+      s.d.tq.ctr = q0;
+      s.d.tq.clear = q1;
+      s.g.tq.ctr = q1;
+      s.g.tq.clear = q0;
+      e = flce::launch_dlogits(s.d, entgrad, stream);
       if (e != hipSuccess) return hip_fail(e, "d-logits kernel launch");
       e = flce::launch_gemm_dw(s.g, stream);
       if (e != hipSuccess) return hip_fail(e, "dW GEMM launch");

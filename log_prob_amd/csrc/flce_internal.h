@@ -13,6 +13,44 @@ constexpr int kFwdTileM = 256;
 constexpr int kFwdTileN = 256;
 static_assert(kTile % kFwdTileM == 0 && kTile % kFwdTileN == 0, "forward tiles pad to kTile");
 
+// Launches above this many 256-thread workgroups exceed the dispatch packet's 32-bit
+// grid size (in work-items).
+constexpr int64_t kMaxWorkgroups = 0xFFFFFFFFLL / 256;
+
+// Tail queues of a tile launch.  Workgroup b runs on XCD b % 8, and each XCD works
+// through its own contiguous stream of tiles (the tile-coordinate comment in the
+// kernel source).  The XCDs of one chip do not all run at the same speed, so the last
+// `queue` tiles of every stream are handed out at run time: the stream's own
+// workgroups take them in order from the front through that XCD's counter, and spare
+// workgroups past the tiles let an XCD that has finished its stream take tiles from
+// the back of another XCD's queue.  Counter x: low 32 bits count front claims, high 32
+// bits back claims; a claim gets a tile iff front + back < queue before it, so each
+// queued tile is taken exactly once.  The counters must be zero when the launch
+// starts: a launch zeroes the counters (`clear`) of the launch after it on the stream.
+struct TileQueue {
+  unsigned long long* ctr;    // this launch's 8 counters (unused when queue == 0)
+  unsigned long long* clear;  // 8 counters this launch sets to zero, or nullptr
+  int queue;                  // queued tiles per XCD stream (set by the launcher)
+};
+constexpr size_t kQueueBytes = 256;  // workspace for two sets of 8 counters
+
+// Queue tiles per XCD stream and spare workgroups of a launch of n tiles: about 4% of
+// each stream queued and 2% more workgroups, each a whole number per compute unit
+// (32 per XCD); none below 8 tiles per compute unit or past the dispatch limit.
+struct QueueShape {
+  int queue;
+  int64_t spare;
+};
+inline QueueShape queue_shape(int64_t n) {
+  const int64_t per = n >> 3;
+  if (per < 256) return {0, 0};
+  int64_t q = (per / 25 + 31) / 32 * 32;
+  if (q > per) q = per;
+  const int64_t spare = 8 * ((per / 50 + 31) / 32 * 32);
+  if (n + spare > kMaxWorkgroups) return {0, 0};
+  return {int(q), spare};
+}
+
 struct FwdTileArgs {
   const uint16_t* X;        // bf16 [M, H]
   const uint16_t* W;        // bf16 [V, H]: vocabulary rows v_off .. v_off + V - 1
@@ -27,6 +65,7 @@ struct FwdTileArgs {
   float* part_s;            // [n_vt, Mpad] sum exp(z - m)
   float* part_u;            // [n_vt, Mpad] sum exp(z - m) (z - m)   (entropy only)
   float* zt;                // [Mpad] target logit (target_logit_kernel, rows W holds)
+  TileQueue tq;             // the tile kernel's counters; target_logit_kernel zeroes them
 };
 
 // Vocabulary shards whose partials one merge combines (a single shard for an
@@ -72,6 +111,7 @@ struct DlogitsArgs {
   int n_mt, n_vt;             // tiles along M and along the chunk
   uint16_t* dz;               // bf16 Mpad x ldz, tile-blocked: scale * dz of the chunk
   long ldz;
+  TileQueue tq;
 };
 
 struct GemmDwArgs {
@@ -85,6 +125,7 @@ struct GemmDwArgs {
   int chunk_cols;       // padded width of the chunk (multiple of 256)
   int n_i, n_h;         // tiles along the chunk and along H
   int mode;             // 0 write bf16, 1 write acc, 2 add to acc, 3 add and write bf16
+  TileQueue tq;
 };
 
 struct GemmDxArgs {

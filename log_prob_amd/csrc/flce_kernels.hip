@@ -137,6 +137,69 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int n_m, int n
   group_coords(L, n_m, n_n, group_m, tm, tn);
 }
 
+// Queued tiles left in a counter (negative once exhausted).
+__device__ __forceinline__ long long queue_left(unsigned long long c, int q) {
+  return (long long)q - (long long)(c & 0xffffffffull) - (long long)(c >> 32);
+}
+
+// Logical id of this workgroup's tile for a launch of n tiles plus spare workgroups,
+// with the last tq.queue ids of each XCD's stream (the logical ids x * per ... of
+// tile_coords) taken through the counters of TileQueue; -1 when the workgroup finds
+// no tile.  Lane 0 of wave 0 claims: first from the front of its own XCD's queue, then
+// from the back of the queue with the most tiles left, until every queue is empty
+// (each pass either takes a tile or sees a counter that only grows, so the loop ends).
+// The bounds on both counts keep every id in range whatever the counters hold.
+// Workgroup 0 also zeroes tq.clear for a later launch.
+__device__ __forceinline__ int tile_claim(int n, const TileQueue& tq) {
+  const int bid = blockIdx.x;
+  if (bid == 0 && threadIdx.x < 8 && tq.clear)
+    __hip_atomic_store(&tq.clear[threadIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int per = n >> 3, q = tq.queue, x = bid & 7;
+  if (bid < (per << 3)) {
+    if ((bid >> 3) < per - q) return x * per + (bid >> 3);
+  } else if (bid < n) {
+    return bid;
+  }
+  if (q == 0) return -1;
+  __shared__ int claimed;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const unsigned long long uq = (unsigned long long)q;
+    int L = -1;
+    if (lane == 0) {
+      const unsigned long long old = atomicAdd(&tq.ctr[x], 1ull);
+      const unsigned long long f = old & 0xffffffffull, b = old >> 32;
+      if (f < uq && b < uq - f) L = x * per + per - q + (int)f;
+    }
+    L = __shfl(L, 0);
+    while (L < 0) {
+      const long long left =
+          lane < 8 ? queue_left(__hip_atomic_load(&tq.ctr[lane & 7], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT), q)
+                   : 0;
+      int y = -1;
+      long long most = 0;
+      for (int j = 0; j < 8; ++j) {
+        const long long r = __shfl(left, j);
+        if (r > most) {
+          most = r;
+          y = j;
+        }
+      }
+      if (y < 0) break;
+      if (lane == 0) {
+        const unsigned long long old = atomicAdd(&tq.ctr[y], 1ull << 32);
+        const unsigned long long f = old & 0xffffffffull, b = old >> 32;
+        if (b < uq && f < uq - b) L = y * per + per - 1 - (int)b;
+      }
+      L = __shfl(L, 0);
+    }
+    if (lane == 0) claimed = L;
+  }
+  __syncthreads();
+  return claimed;
+}
+
 // ---------------------------------------------------------------------------
 // One operand of the mainloop, as seen by a workgroup.
 //  K-contiguous (KC): `base` is element (row 0 of the tile, k = 0) of a [rows][K]
@@ -969,7 +1032,11 @@ __global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[S::PIPE_BYTES];
   static_assert(3 * CP * TM * 4 <= S::PIPE_BYTES, "epilogue buffers");
   int mt, vt;
-  tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, FWD_GROUP_M, mt, vt);
+  {
+    const int L = tile_claim(p.n_mt * p.n_vt, p.tq);
+    if (L < 0) return;
+    group_coords(L, p.n_mt, p.n_vt, FWD_GROUP_M, mt, vt);
+  }
   const int row0 = mt * TM, col0 = vt * TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -1052,6 +1119,9 @@ __global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(
 // One wave per row.
 constexpr int TL_ROWS = 4;
 __global__ __launch_bounds__(64 * TL_ROWS) void target_logit_kernel(FwdTileArgs p) {
+  // zero the tile kernel's queue counters: that kernel is launched after this one
+  if (blockIdx.x == 0 && threadIdx.x < 8 && p.tq.ctr)
+    __hip_atomic_store(&p.tq.ctr[threadIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * TL_ROWS + (threadIdx.x >> 6);
   if (row >= p.M) return;
@@ -1297,8 +1367,10 @@ __device__ __forceinline__ void dlogits_tile(const DlogitsArgs& p, int mt, int v
 template <bool ENTGRAD>
 __global__ __launch_bounds__(NTHREADS) void bwd_dlogits_kernel(DlogitsArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_DLOGITS];
+  const int L = tile_claim(p.n_mt * p.n_vt, p.tq);
+  if (L < 0) return;
   int mt, vt;
-  tile_coords(blockIdx.x, gridDim.x, p.n_mt, p.n_vt, 8, mt, vt);
+  group_coords(L, p.n_mt, p.n_vt, 8, mt, vt);
   dlogits_tile<ENTGRAD>(p, mt, vt, smem);
 }
 
@@ -1402,10 +1474,12 @@ __device__ __forceinline__ void dw_tile(const GemmDwArgs& p, int ti, int th, cha
 
 __global__ __launch_bounds__(NTHREADS) void gemm_dw_kernel(GemmDwArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BIG];
+  const int L = tile_claim(p.n_h * p.n_i, p.tq);
+  if (L < 0) return;
   int ti, th;
   // groups run along H: the few X^T tiles stay in L2 while each dzs tile is read by
   // one group of an XCD at a time, so dzs streams from HBM about once per H group
-  tile_coords(blockIdx.x, gridDim.x, p.n_h, p.n_i, 8, th, ti);
+  group_coords(L, p.n_h, p.n_i, 8, th, ti);
   dw_tile(p, ti, th, smem);
 }
 
@@ -1659,12 +1733,22 @@ hipError_t scratch_device_address(void** ptr) {
 
 // ---------------------------------------------------------------------------
 // Launchers (host side).  Each returns the hipGetLastError() of its launch.
+// Grid of a launch of n tiles with tail queues (sets tq.queue): the tiles plus the
+// spare workgroups.
+static unsigned queued_grid(int64_t n, TileQueue& tq) {
+  const QueueShape qs = tq.ctr ? queue_shape(n) : QueueShape{0, 0};
+  tq.queue = qs.queue;
+  return (unsigned)(n + qs.spare);
+}
+
 hipError_t launch_fwd_tile(const FwdTileArgs& a, bool ent, hipStream_t s) {
-  const unsigned g = (unsigned)((long)a.n_mt * a.n_vt);
+  FwdTileArgs b = a;
+  b.tq.clear = nullptr;
+  const unsigned g = queued_grid((int64_t)a.n_mt * a.n_vt, b.tq);
   if (ent)
-    fwd_tile_kernel<FwdShape, true><<<g, FwdShape::NTHREADS, 0, s>>>(a);
+    fwd_tile_kernel<FwdShape, true><<<g, FwdShape::NTHREADS, 0, s>>>(b);
   else
-    fwd_tile_kernel<FwdShape, false><<<g, FwdShape::NTHREADS, 0, s>>>(a);
+    fwd_tile_kernel<FwdShape, false><<<g, FwdShape::NTHREADS, 0, s>>>(b);
   return hipGetLastError();
 }
 
@@ -1684,11 +1768,12 @@ hipError_t launch_fwd_merge(const FwdMergeArgs& a, bool ent, hipStream_t s) {
 }
 
 hipError_t launch_dlogits(const DlogitsArgs& a, bool entgrad, hipStream_t s) {
-  const unsigned g = (unsigned)((long)a.n_mt * a.n_vt);
+  DlogitsArgs b = a;
+  const unsigned g = queued_grid((int64_t)a.n_mt * a.n_vt, b.tq);
   if (entgrad)
-    bwd_dlogits_kernel<true><<<g, NTHREADS, 0, s>>>(a);
+    bwd_dlogits_kernel<true><<<g, NTHREADS, 0, s>>>(b);
   else
-    bwd_dlogits_kernel<false><<<g, NTHREADS, 0, s>>>(a);
+    bwd_dlogits_kernel<false><<<g, NTHREADS, 0, s>>>(b);
   return hipGetLastError();
 }
 
@@ -1703,7 +1788,9 @@ hipError_t launch_bwd_pipe(const PipeArgs& a, bool entgrad, hipStream_t s) {
 }
 
 hipError_t launch_gemm_dw(const GemmDwArgs& a, hipStream_t s) {
-  gemm_dw_kernel<<<(unsigned)((long)a.n_i * a.n_h), NTHREADS, 0, s>>>(a);
+  GemmDwArgs b = a;
+  const unsigned g = queued_grid((int64_t)a.n_i * a.n_h, b.tq);
+  gemm_dw_kernel<<<g, NTHREADS, 0, s>>>(b);
   return hipGetLastError();
 }
 

@@ -34,40 +34,41 @@ def test_version_and_status_strings():
 
 
 def test_workspace_query_values():
-    # forward: m, s, u partials of [ceil(V/256), Mpad] fp32 + zt [Mpad]
+    # forward: m, s, u partials of [ceil(V/256), Mpad] fp32 + zt [Mpad] + 256 bytes of
+    # tile-queue counters
     fwd, bwd = flce.workspace_query(8192, 8192, 131072, True)
-    assert fwd == 3 * 512 * 8192 * 4 + 8192 * 4
+    assert fwd == 3 * 512 * 8192 * 4 + 8192 * 4 + 256
     fwd0, _ = flce.workspace_query(8192, 8192, 131072, False)
-    assert fwd0 == 2 * 512 * 8192 * 4 + 8192 * 4
+    assert fwd0 == 2 * 512 * 8192 * 4 + 8192 * 4 + 256
     # backward preferred: one d-logit chunk (2 GiB, within the 4 GiB budget) covers the
     # whole vocabulary here
-    assert bwd == 8192 * 131072 * 2
+    assert bwd == 8192 * 131072 * 2 + 256
     assert flce.backward_chunk_cols(8192, 8192, 131072, bwd) == 131072
     # smaller workspaces shrink the chunk, down to one 256-column tile plus fp32 dX
     mn = flce.backward_workspace_min(8192, 8192, 131072)
-    assert mn == 8192 * 256 * 2 + 8192 * 8192 * 4
+    assert mn == 8192 * 256 * 2 + 8192 * 8192 * 4 + 256
     assert flce.backward_chunk_cols(8192, 8192, 131072, mn) == 256
     # ragged shapes are padded to whole tiles
     fwd, _ = flce.workspace_query(64, 128, 1000, True)
-    assert fwd == 3 * 4 * 256 * 4 + 256 * 4
+    assert fwd == 3 * 4 * 256 * 4 + 256 * 4 + 256
     _, bwd = flce.workspace_query(32767, 2048, 151936, True)
     c = flce.backward_chunk_cols(32767, 2048, 151936, bwd)
     assert c % 256 == 0 and 256 <= c < 151936 + 256
     # d-logits past the 4 GiB chunk budget: 65536-column chunks (4 GiB of bf16 over
     # 32768 padded rows) plus the fp32 dX accumulator
     assert c == 65536
-    assert bwd == 32768 * 65536 * 2 + 32767 * 2048 * 4
+    assert bwd == 32768 * 65536 * 2 + 32767 * 2048 * 4 + 256
 
 
 def test_forward_token_waves():
     # one 256-row wave: 3 partial arrays of [512 tiles, 256 rows] fp32 + the target logits
     mn = flce.forward_workspace_min(8192, 8192, 131072, True)
-    assert mn == 3 * 512 * 256 * 4 + 256 * 4
-    assert flce.forward_workspace_min(8192, 8192, 131072, False) == 2 * 512 * 256 * 4 + 256 * 4
+    assert mn == 3 * 512 * 256 * 4 + 256 * 4 + 256
+    assert flce.forward_workspace_min(8192, 8192, 131072, False) == 2 * 512 * 256 * 4 + 256 * 4 + 256
     full, _ = flce.workspace_query(8192, 8192, 131072, True)
     assert flce.forward_wave_rows(8192, 8192, 131072, full) == 8192
     assert flce.forward_wave_rows(8192, 8192, 131072, mn) == 256
-    w4k = 3 * 512 * 4096 * 4 + 4096 * 4
+    w4k = 3 * 512 * 4096 * 4 + 4096 * 4 + 256
     assert flce.forward_wave_rows(8192, 8192, 131072, w4k) == 4096
     assert flce.forward_wave_rows(8192, 8192, 131072, w4k - 1) == 3840
     # the wave never exceeds the padded token count
@@ -148,11 +149,12 @@ def test_python_wrapper_raises():
 
 
 def test_shard_workspace_query():
+    # d-logits (+ 256 bytes of tile-queue counters)
     lo, pref = flce.backward_shard_workspace_query(8192, 8192, 16384)
-    assert lo == 8192 * 256 * 2
-    assert pref == 8192 * 16384 * 2          # the whole shard in one chunk
+    assert lo == 8192 * 256 * 2 + 256
+    assert pref == 8192 * 16384 * 2 + 256    # the whole shard in one chunk
     lo, pref = flce.backward_shard_workspace_query(300, 64, 1000)
-    assert lo == 512 * 256 * 2 and pref == 512 * 1024 * 2
+    assert lo == 512 * 256 * 2 + 256 and pref == 512 * 1024 * 2 + 256
 
 
 def _fps(lib, X=16, W=16, t=16, M=4, H=8, Vs=3, off=0, ign=-100, scale=1.0, ent=1, ws=256,
@@ -396,7 +398,8 @@ def _schedule_bytes(M, H, V, rows, chunk, pipe):
     """Workspace a schedule uses, from its description in include/flce.h: the bf16
     d-logits of one wave over one chunk (two buffers when pipelined over more than one
     step), the fp32 dX accumulator of one wave when a wave takes several chunks, the fp32
-    dW accumulator when there are several waves; each part rounded up to 256 bytes."""
+    dW accumulator when there are several waves, 256 bytes of tile-queue counters; each
+    part rounded up to 256 bytes."""
     up = lambda x: -(-x // 256) * 256
     Mpad, Vpad = up(M), up(V)
     steps = -(-M // rows) * -(-Vpad // chunk)
@@ -405,7 +408,7 @@ def _schedule_bytes(M, H, V, rows, chunk, pipe):
         b += up(min(rows, M) * H * 4)
     if rows < Mpad:
         b += up(V * H * 4)
-    return b
+    return b + 256
 
 
 def test_backward_schedules_fit_their_workspace():

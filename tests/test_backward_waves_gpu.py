@@ -70,8 +70,9 @@ def test_minimum_workspace_does_not_grow_with_tokens():
     H, V = 64, 512
     sizes = {M: flce.backward_workspace_min(M, H, V) for M in (4097, 5000, (1 << 20) + 1, 1 << 24)}
     assert len(set(sizes.values())) == 1, sizes
-    # and it is the 256-row, 256-column schedule with the fp32 dW accumulator
-    assert sizes[4097] == 256 * 256 * 2 + 256 * H * 4 + V * H * 4
+    # and it is the 256-row, 256-column schedule with the fp32 dW accumulator (and the
+    # 256 bytes of tile-queue counters)
+    assert sizes[4097] == 256 * 256 * 2 + 256 * H * 4 + V * H * 4 + 256
 
 
 @pytest.mark.parametrize("which", [0, 1])

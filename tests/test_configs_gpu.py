@@ -57,9 +57,17 @@ def run_config(case):
     ent = case.compute_entropy or gent is not None
     fwd_b, bwd_b = flce.workspace_query(case.M, case.H, case.V, ent)
     ws = torch.empty(max(fwd_b, bwd_b), dtype=torch.uint8, device="cuda")
-    lp, lse, entropy = flce.forward(X, W, t, case.ignore_index, case.scale, ent, workspace=ws)
+    # workspace and outputs start as 0xFF bytes (NaN partials, d-logits and outputs;
+    # all-ones tile-queue counters): a tile left out, or counters not cleared, would show
+    ws.fill_(0xFF)
+    nan = lambda *shape, dt=torch.float32: torch.full(shape, float("nan"), dtype=dt, device="cuda")
+    lp, lse, entropy = flce.forward(X, W, t, case.ignore_index, case.scale, ent, workspace=ws,
+                                    out=(nan(case.M), nan(case.M), nan(case.M) if ent else None))
+    ws.fill_(0xFF)
     dX, dW = flce.backward(X, W, t, lse, entropy if gent is not None else None, glp, gent,
-                           case.ignore_index, case.scale, workspace=ws)
+                           case.ignore_index, case.scale, workspace=ws,
+                           out=(nan(case.M, case.H, dt=torch.bfloat16),
+                                nan(case.V, case.H, dt=torch.bfloat16)))
     torch.cuda.synchronize()
     out = dict(logprob=gu.to_np(lp), lse=gu.to_np(lse),
                entropy=None if entropy is None else gu.to_np(entropy),
