@@ -145,9 +145,10 @@ __device__ __forceinline__ long long queue_left(unsigned long long c, int q) {
 // Logical id of this workgroup's tile for a launch of n tiles plus spare workgroups,
 // with the last tq.queue ids of each XCD's stream (the logical ids x * per ... of
 // tile_coords) taken through the counters of TileQueue; -1 when the workgroup finds
-// no tile.  Lane 0 of wave 0 claims: first from the front of its own XCD's queue, then
-// from the back of the queue with the most tiles left, until every queue is empty
-// (each pass either takes a tile or sees a counter that only grows, so the loop ends).
+// no tile.  Lane 0 of wave 0 claims: a workgroup of the stream first from the front of
+// its own XCD's queue, then (a spare at once) from the back of the queue with the most
+// tiles left, until every queue is empty (each pass either takes a tile or sees a
+// counter that only grows, so the loop ends).
 // The bounds on both counts keep every id in range whatever the counters hold.
 // Workgroup 0 also zeroes tq.clear for a later launch.
 __device__ __forceinline__ int tile_claim(int n, const TileQueue& tq) {
@@ -166,7 +167,7 @@ __device__ __forceinline__ int tile_claim(int n, const TileQueue& tq) {
     const int lane = threadIdx.x;
     const unsigned long long uq = (unsigned long long)q;
     int L = -1;
-    if (lane == 0) {
+    if (lane == 0 && bid < n) {
       const unsigned long long old = atomicAdd(&tq.ctr[x], 1ull);
       const unsigned long long f = old & 0xffffffffull, b = old >> 32;
       if (f < uq && b < uq - f) L = x * per + per - q + (int)f;
