@@ -3,9 +3,10 @@
 // Forward (Liger-Kernel FSLCE commit, "Summary" and "Implementation / Forward";
 // SkyRL PR 2141, "Overview"):
 //   fwd_tile     one workgroup per (256-row M tile, 256-column V tile): bf16 MFMA
-//                mainloop over H, then an epilogue that reduces the logit tile to
-//                per-row partial statistics (max m, sum of exp(z - m), and
-//                sum of exp(z - m) (z - m) for entropy).
+//                mainloop over H computing the tile transposed (vocabulary rows,
+//                token columns), then an epilogue that reduces it to per-row partial
+//                statistics (max m, sum of exp(z - m), and sum of exp(z - m) (z - m)
+//                for entropy) down each lane's registers.
 //   target_logit z[m, t[m]] as one dot product per row.
 //   fwd_merge    combines the per-tile partials of each row (max first, then the
 //                rescaled sums) into lse, logprob and entropy.
@@ -746,59 +747,6 @@ __device__ __forceinline__ int acc_row(int lane, int e) {
   return ((e >> 2) << 3) + ((lane >> 5) << 2) + (e & 3);
 }
 
-// DPP move within rows of 16 lanes: row_shl:N (CTRL 0x100 + N) gives lane i the value
-// of lane i + N, row_shr:N (CTRL 0x110 + N) that of lane i - N; a lane whose source
-// lies outside its row reads 0.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
-}
-
-// v_permlane16_swap_b32: rows 1 and 3 of a (lanes 16-31, 48-63) trade places with
-// rows 0 and 2 of b, so that afterwards a holds (own a | b of lane - 16) and b holds
-// (a of lane + 16 | own b).  Issued as inline assembly because the compiler builtin
-// hands back only the first register; the s_nop pads cover the VALU hazards around it.
-__device__ __forceinline__ void swap16(float& a, float& b) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-
-// One butterfly level of the reduce-scatter for lane distance s < 16: a lane with bit
-// s clear keeps the low half of each pair and combines it with its partner's
-// (lane + s, a row_shl), a lane with bit s set the high half (lane - s, a row_shr).
-template <int s, int P, class Op>
-__device__ __forceinline__ void rs_level(float (&v)[32 * P], bool upper, Op op) {
-#pragma unroll
-  for (int p = 0; p < P; ++p)
-#pragma unroll
-    for (int i = 0; i < s; ++i) {
-      const float lo = v[32 * p + i], hi = v[32 * p + i + s];
-      const float tl = op(lo, dpp_mov<0x100 + s>(lo));
-      const float th = op(hi, dpp_mov<0x110 + s>(hi));
-      v[32 * p + i] = upper ? th : tl;
-    }
-}
-
-// Reduce-scatter over the 32 lanes of a half-wave.  v holds 32 P values, entry
-// 32 p + j being slot j of group p.  On exit v[32 p] holds the reduction over the
-// half-wave of slot (lane % 32) of group p.  Lanes l and l ^ 16 meet through the
-// row swap, the closer pairs through DPP row shifts; no LDS traffic.
-template <int P, class Op>
-__device__ __forceinline__ void reduce_scatter32(float (&v)[32 * P], int lane, Op op) {
-#pragma unroll
-  for (int p = 0; p < P; ++p)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float a = v[32 * p + i], b = v[32 * p + i + 16];
-      swap16(a, b);
-      v[32 * p + i] = op(a, b);
-    }
-  rs_level<8, P>(v, (lane & 8) != 0, op);
-  rs_level<4, P>(v, (lane & 4) != 0, op);
-  rs_level<2, P>(v, (lane & 2) != 0, op);
-  rs_level<1, P>(v, (lane & 1) != 0, op);
-}
-
 // ---------------------------------------------------------------------------
 // An accumulator value read from its accumulation register where it is used (for
 // values used once: left to itself, the register allocator moves the tile between
@@ -932,180 +880,179 @@ __device__ __forceinline__ void store_acc_bf16(char* tile, const f32x16 (&acc)[4
 
 // ---------------------------------------------------------------------------
 // Forward tile kernel.
-//
-// Per-lane extreme of each row slot q = 16 mb + e over the lane's NB columns, on
-// sgn * acc (sgn = -1 if NEG): the row maximum of z = scale * acc is |scale| times
-// the maximum of sgn(scale) * acc.  In a RAGGED tile columns past V are skipped
-// (bit nb of colmask: column 32 nb + lane % 32 of the wave tile exists).
-// v_max3_f32 issued directly: fmaxf on values the compiler cannot prove to be quiet
-// NaNs (here, MFMA results) costs one quieting v_max per input.  NEG applies the
-// source negation modifier to all three inputs.
+
+// v_permlane32_swap_b32: the upper half-wave of a (lanes 32-63) trades places with the
+// lower half-wave of b, so that afterwards a holds (own a | b of lane - 32) and b holds
+// (a of lane + 32 | own b).  Issued as inline assembly because the compiler builtin
+// hands back only the first register; the s_nop pads cover the VALU hazards around it.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+// x and y each combined over lanes l and l ^ 32 in one swap: the result is that of x
+// in the lower half-wave and that of y in the upper one.
+template <class Op>
+__device__ __forceinline__ float halves_reduce(float x, float y, Op op) {
+  swap32(x, y);
+  return op(x, y);
+}
+
+// max(m, sgn a, sgn b) with sgn = -1 under NEG, as one v_max3_f32 issued directly:
+// fmaxf on values the compiler cannot prove to be quiet NaNs (here, MFMA results)
+// costs one quieting v_max per input.  m is already a running maximum of sgn-scaled
+// values, so only a and b take the negation modifier.
 template <bool NEG>
-__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+__device__ __forceinline__ float max3_run(float m, float a, float b) {
   float r;
   if constexpr (NEG)
-    asm("v_max3_f32 %0, -%1, -%2, -%3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    asm("v_max3_f32 %0, %1, -%2, -%3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
   else
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
   return r;
 }
 
+// Per token column of the lane, the maximum of sgn * acc over the lane's 16 MB
+// vocabulary rows (sgn = -1 if NEG; the maximum of z = scale * acc is |scale| times
+// that of sgn(scale) * acc); rows at or past `vrows` of the wave tile are skipped when
+// RAGGED.
 template <bool NEG, bool RAGGED, class S>
-__device__ __forceinline__ void lane_row_max(const f32x16 (&acc)[S::MB][S::NB],
-                                             float (&mx)[16 * S::MB], unsigned colmask) {
-  static_assert(S::NB == 4, "four columns per lane and row slot");
+__device__ __forceinline__ void lane_col_max(const f32x16 (&acc)[S::MB][S::NB], int lane,
+                                             int vrows, float (&mx)[S::NB]) {
+  constexpr float SKIP = NEG ? INFINITY : -INFINITY;  // what the maximum ignores
+#pragma unroll
+  for (int nb = 0; nb < S::NB; ++nb) mx[nb] = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < S::MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const bool v0 = !RAGGED || 32 * mb + acc_row(lane, e) < vrows;
+      const bool v1 = !RAGGED || 32 * mb + acc_row(lane, e + 1) < vrows;
+#pragma unroll
+      for (int nb = 0; nb < S::NB; ++nb)
+        mx[nb] = max3_run<NEG>(mx[nb], v0 ? acc[mb][nb][e] : SKIP, v1 ? acc[mb][nb][e + 1] : SKIP);
+    }
+}
+
+// Per token column of the lane, the shifted sums over its 16 MB vocabulary rows in
+// log2 units: s = sum 2^d and u = sum 2^d d with d = c1 z - m2 (nm2 = -m2 per column).
+template <bool ENT, bool RAGGED, class S>
+__device__ __forceinline__ void lane_col_sums(const f32x16 (&acc)[S::MB][S::NB], int lane,
+                                              int vrows, float c1, const float (&nm2)[S::NB],
+                                              float (&sv)[S::NB], float (&uv)[S::NB]) {
+#pragma unroll
+  for (int nb = 0; nb < S::NB; ++nb) sv[nb] = uv[nb] = 0.f;
 #pragma unroll
   for (int mb = 0; mb < S::MB; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float v[4];
+      const bool valid = !RAGGED || 32 * mb + acc_row(lane, e) < vrows;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) v[nb] = acc[mb][nb][e];
-      if constexpr (RAGGED) {
-        // columns past V take the value that the (negated) maximum ignores
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          v[nb] = ((colmask >> nb) & 1u) ? v[nb] : (NEG ? INFINITY : -INFINITY);
-      }
-      const float m3 = max3_raw<NEG>(v[0], v[1], v[2]);
-      // the running maximum is already negated: only the fourth input takes the modifier
-      float m;
-      if constexpr (NEG)
-        asm("v_max_f32 %0, %1, -%2" : "=v"(m) : "v"(m3), "v"(v[3]));
-      else
-        asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(m3), "v"(v[3]));
-      mx[16 * mb + e] = m;
-    }
-}
-
-// Shifted sums of the 32 row slots of blocks mb0, mb0 + 1 over the lane's NB columns,
-// in log2 units: s = sum 2^d and u = sum 2^d d with d = c1 acc - m2 (c1 = scale
-// log2 e, m2 = the row maximum of c1 acc, from the WAVES_N column parts in `red`).
-template <bool ENT, bool RAGGED, class S>
-__device__ __forceinline__ void lane_row_sums(const f32x16 (&acc)[S::MB][S::NB], const float* red,
-                                              int wr0, int lane, float c1, unsigned colmask,
-                                              int mb0, float (&sv)[32], float (&uv)[ENT ? 32 : 1]) {
-  const float ac1 = fabsf(c1);
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // rows 8 q + 4 (lane / 32) + 0..3 of block mb: slots e = 4 q + 0..3
-      const int mb = mb0 + mi;
-      const int rb = wr0 + 32 * mb + 8 * q + 4 * (lane >> 5);
-      float mh[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-      for (int cp = 0; cp < S::WAVES_N; ++cp) {
-        const float4 h = *reinterpret_cast<const float4*>(red + cp * S::TM + rb);
-        mh[0] = fmaxf(mh[0], h.x); mh[1] = fmaxf(mh[1], h.y);
-        mh[2] = fmaxf(mh[2], h.z); mh[3] = fmaxf(mh[3], h.w);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = 4 * q + j;
-        const float nm2 = -ac1 * mh[j];
-        float s = 0.f, u = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < S::NB; ++nb) {
-          float d = fmaf(acc[mb][nb][e], c1, nm2);
-          if constexpr (RAGGED) d = ((colmask >> nb) & 1u) ? d : -INFINITY;
-          const float pe = __builtin_amdgcn_exp2f(d);
-          s += pe;
-          if constexpr (ENT) u = fmaf(pe, RAGGED ? fmaxf(d, -3.0e38f) : d, u);
-        }
-        sv[16 * mi + e] = s;
-        if constexpr (ENT) uv[16 * mi + e] = u;
+      for (int nb = 0; nb < S::NB; ++nb) {
+        float d = fmaf(acc[mb][nb][e], c1, nm2[nb]);
+        if constexpr (RAGGED) d = valid ? d : -INFINITY;
+        const float pe = __builtin_amdgcn_exp2f(d);
+        sv[nb] += pe;
+        if constexpr (ENT) uv[nb] = fmaf(pe, RAGGED ? fmaxf(d, -3.0e38f) : d, uv[nb]);
       }
     }
 }
 
-// One workgroup per (TM-row, TN-column) tile of the logits.  Per wave, lane l holds
-// for row slot q = 16 mb + e (16 MB of them) the NB columns 32 nb + l % 32 of its
-// wave tile.  The row maximum over the tile's TN columns is formed first (lane, then
-// half-wave, then the two waves sharing the rows through LDS), so both column halves
-// sum against the same shift and their partials simply add; thread t < TM writes the
-// partials of tile row t.
+// One workgroup per tile of TN tokens x TM vocabulary entries of the logits, computed
+// transposed: z^T = W X^T, the MFMA rows being vocabulary entries and its columns
+// tokens.  Per wave, lane l then holds, for each of its NB token columns 32 nb + l % 32,
+// 16 MB vocabulary rows of the wave tile, so the maxima and sums over the vocabulary
+// run down the lane's own registers, meet the other half-wave in one swap, and meet the
+// other wave of the same tokens through LDS.  The maximum over the tile's TM entries is
+// formed first, so both row halves sum against the same shift and their partials simply
+// add; thread t < TN writes the partials of token t of the tile.
 template <class S, bool ENT>
 __global__ __launch_bounds__(S::NTHREADS, S::WAVES_PER_EU) void fwd_tile_kernel(FwdTileArgs p) {
-  constexpr int TM = S::TM, TN = S::TN, MB = S::MB, NB = S::NB, WM = S::WM, WN = S::WN;
-  constexpr int P = MB / 2;  // groups of 32 row slots per lane
-  constexpr int CP = S::WAVES_N;  // column parts: waves sharing the same rows
+  constexpr int TV = S::TM, TT = S::TN, NB = S::NB, WM = S::WM, WN = S::WN;
+  constexpr int RP = S::WAVES_M;  // row parts: waves sharing the same tokens
+  static_assert(NB % 2 == 0, "token columns pair up across the half-waves");
   __shared__ __attribute__((aligned(1024))) char smem[S::PIPE_BYTES];
-  static_assert(3 * CP * TM * 4 <= S::PIPE_BYTES, "epilogue buffers");
+  static_assert(3 * RP * TT * 4 <= S::PIPE_BYTES, "epilogue buffers");
   int mt, vt;
   {
     const int L = tile_claim(p.n_mt * p.n_vt, p.tq);
     if (L < 0) return;
     group_coords(L, p.n_mt, p.n_vt, FWD_GROUP_M, mt, vt);
   }
-  const int row0 = mt * TM, col0 = vt * TN;
+  const int row0 = mt * TT, col0 = vt * TV;  // first token, first vocabulary entry
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
 
-  f32x16 acc[MB][NB];
-  const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, 0};
-  const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, 0};
-  mainloop<S, true, true>(acc, smem, A, B, p.H);
+  f32x16 acc[S::MB][NB];
+  const TileSrc A{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, 0};
+  const TileSrc B{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, 0};
+  mainloop<S, true, true, true>(acc, smem, A, B, p.H);  // X (L2-resident) loads first
   // (the mainloop ends with a barrier: the LDS is free)
 
-  const int wr0 = (wave / CP) * WM, wc0 = (wave % CP) * WN, wn = wave % CP;
-  const int lc = lane & 31;
+  const int wm = wave / S::WAVES_N;
+  const int wv0 = wm * WM, wt0 = (wave % S::WAVES_N) * WN;
+  const int lc = lane & 31, hi = lane >> 5;
   const float c1 = p.scale * LOG2E;  // logits in log2 units: z2 = c1 acc
+  const float ac1 = fabsf(c1);
+  const bool ragged = col0 + TV > p.V;
+  const int vrows = p.V - col0 - wv0;  // vocabulary rows of the wave tile that exist
 
-  // epilogue LDS: row maxima per column part [CP][TM], sums [CP][2][TM]
+  // epilogue LDS: token maxima per row part [RP][TT], sums [RP][2][TT]
   float* red = reinterpret_cast<float*>(smem);
-  float* comb = red + CP * TM;
+  float* comb = red + RP * TT;
 
-  const bool ragged = col0 + TN > p.V;
-  unsigned colmask = 0;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) colmask |= (col0 + wc0 + 32 * nb + lc < p.V ? 1u : 0u) << nb;
-
-  // row maxima of sgn(c1) acc: lane, half-wave, then the column parts via LDS
+  // maxima of sgn(c1) z over the wave's vocabulary rows: lane, then half-wave (token
+  // columns 2 j + hi of the lane come out in half hi), then the row parts via LDS
   {
-    float mx[32 * P];
+    float mx[NB];
     if (!ragged) {
-      if (c1 >= 0.f) lane_row_max<false, false, S>(acc, mx, colmask);
-      else lane_row_max<true, false, S>(acc, mx, colmask);
+      if (c1 >= 0.f) lane_col_max<false, false, S>(acc, lane, vrows, mx);
+      else lane_col_max<true, false, S>(acc, lane, vrows, mx);
     } else {
-      if (c1 >= 0.f) lane_row_max<false, true, S>(acc, mx, colmask);
-      else lane_row_max<true, true, S>(acc, mx, colmask);
+      if (c1 >= 0.f) lane_col_max<false, true, S>(acc, lane, vrows, mx);
+      else lane_col_max<true, true, S>(acc, lane, vrows, mx);
     }
-    reduce_scatter32<P>(mx, lane, [](float a, float b) { return max_raw(a, b); });
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp) {
-      const int mb = 2 * pp + (lc >> 4), e = lc & 15;
-      red[wn * TM + wr0 + 32 * mb + acc_row(lane, e)] = mx[32 * pp];
-    }
+    for (int j = 0; j < NB / 2; ++j)
+      red[wm * TT + wt0 + 32 * (2 * j + hi) + lc] =
+          halves_reduce(mx[2 * j], mx[2 * j + 1], [](float a, float b) { return max_raw(a, b); });
   }
   __syncthreads();
 
-  // shifted sums against the full-row maximum, 32 row slots (two blocks) at a time
+  // shifted sums against the tile maximum of each token column
+  {
+    float nm2[NB], sv[NB], uv[NB];
 #pragma unroll
-  for (int pp = 0; pp < P; ++pp) {
-    float sv[32], uv[ENT ? 32 : 1];
+    for (int nb = 0; nb < NB; ++nb) {
+      float m = red[wt0 + 32 * nb + lc];
+#pragma unroll
+      for (int rp = 1; rp < RP; ++rp) m = fmaxf(m, red[rp * TT + wt0 + 32 * nb + lc]);
+      nm2[nb] = -ac1 * m;
+    }
     if (!ragged)
-      lane_row_sums<ENT, false, S>(acc, red, wr0, lane, c1, colmask, 2 * pp, sv, uv);
+      lane_col_sums<ENT, false, S>(acc, lane, vrows, c1, nm2, sv, uv);
     else
-      lane_row_sums<ENT, true, S>(acc, red, wr0, lane, c1, colmask, 2 * pp, sv, uv);
-    reduce_scatter32<1>(sv, lane, [](float a, float b) { return a + b; });
-    if constexpr (ENT) reduce_scatter32<1>(uv, lane, [](float a, float b) { return a + b; });
-    const int mb = 2 * pp + (lc >> 4), e = lc & 15;
-    const int rl = wr0 + 32 * mb + acc_row(lane, e);
-    comb[(wn * 2 + 0) * TM + rl] = sv[0];
-    if constexpr (ENT) comb[(wn * 2 + 1) * TM + rl] = uv[0];
+      lane_col_sums<ENT, true, S>(acc, lane, vrows, c1, nm2, sv, uv);
+#pragma unroll
+    for (int j = 0; j < NB / 2; ++j) {
+      const int t = wt0 + 32 * (2 * j + hi) + lc;
+      comb[(2 * wm) * TT + t] =
+          halves_reduce(sv[2 * j], sv[2 * j + 1], [](float a, float b) { return a + b; });
+      if constexpr (ENT)
+        comb[(2 * wm + 1) * TT + t] =
+            halves_reduce(uv[2 * j], uv[2 * j + 1], [](float a, float b) { return a + b; });
+    }
   }
   __syncthreads();
-  if (tid < TM) {
-    float mx = red[tid], sm = comb[tid], um = comb[TM + tid];
+  if (tid < TT) {
+    float mx = red[tid], sm = comb[tid], um = comb[TT + tid];
 #pragma unroll
-    for (int cp = 1; cp < CP; ++cp) {
-      mx = fmaxf(mx, red[cp * TM + tid]);
-      sm += comb[(2 * cp) * TM + tid];
-      if constexpr (ENT) um += comb[(2 * cp + 1) * TM + tid];
+    for (int rp = 1; rp < RP; ++rp) {
+      mx = fmaxf(mx, red[rp * TT + tid]);
+      sm += comb[(2 * rp) * TT + tid];
+      if constexpr (ENT) um += comb[(2 * rp + 1) * TT + tid];
     }
     const long off = (long)vt * p.Mpad + row0 + tid;
-    p.part_m[off] = fabsf(c1) * mx * LN2;
+    p.part_m[off] = ac1 * mx * LN2;
     p.part_s[off] = sm;
     if constexpr (ENT) p.part_u[off] = um * LN2;
   }
