@@ -50,6 +50,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NTHREADS = 256;    // 4 waves of 64 in a 2 x 2 grid over the workgroup tile
 // Pin the instruction order of a sub-step: the fragment reads of sub-step kk + 1
@@ -828,19 +829,6 @@ struct WaveStager {
   // Wait until this wave's staging writes are in LDS (its own reads follow).
   __device__ __forceinline__ void fence() const { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-  // Store the wave's staged rows of block row mb to a tile-blocked buffer (dst = the
-  // tile's 256 x 64 block 0, block q at dst + q BLK_ELEMS, row r at 64 r): two pieces
-  // of 32 consecutive rows, 1 KiB per instruction.
-  __device__ __forceinline__ void store_blocked(int mb, uint16_t* dst) const {
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int qb = it >> 2, r = wr0 + 32 * mb + 8 * (it & 3) + (lane >> 3), c8 = lane & 7;
-      const u32x4 v = get(r, (wc0 >> 3) + 8 * qb + c8);
-      __builtin_nontemporal_store(
-          v, reinterpret_cast<u32x4*>(dst + (long)((wc0 >> 6) + qb) * BLK_ELEMS + r * BLK_COLS + 8 * c8));
-    }
-  }
-
   // Store the wave's staged rows of block row mb to rows [0, nrows) and columns
   // [0, ncols) of a row-major matrix (dst = the tile's element (0, 0), leading
   // dimension ld; ncols a multiple of 8): 4 rows of 256 bytes per instruction.
@@ -1167,67 +1155,116 @@ __global__ __launch_bounds__(MERGE_ROWS * MERGE_SLICES) void fwd_merge_kernel(Fw
 }
 
 // ---------------------------------------------------------------------------
-// A wave's d-logits, d = 2^(c1 acc - lse2) (c0 + cb acc) + [column = target] sa
-// (per-row parameters in LDS, see bwd_dlogits_kernel), rounded to bf16, staged in the
-// wave's own part of the LDS tile and stored to the tile-blocked buffer at dst (the
-// tile's 256 x 64 block 0) 32 rows at a time.  RAGGED: columns past V (colmask bit nb
-// clear) become 0.  Every wave runs the same instruction stream whether or not it
-// holds a target (the correction is a branch per four rows that almost never has
-// active lanes), which keeps the tiles of an XCD in step.
+// Staging of a d-logit tile computed transposed (vocabulary rows, token columns in the
+// accumulators) for the tile-blocked buffer: token row r of the 256 x 256 bf16 tile at
+// byte 512 r, its 16-byte chunk c (vocabulary columns 8 c .. 8 c + 7) at chunk
+// position c ^ tswz(r).  A staging write puts 4 consecutive vocabulary entries of 32
+// consecutive token rows, all in one chunk, and tswz is a bijection of r % 32, so the
+// 64 lanes' 8-byte pieces fill 32 distinct chunk positions; a store read takes 8
+// consecutive chunks of 4 consecutive rows per 32 lanes, which tswz (r % 4 in its top
+// bits) sends to 4 distinct groups of 8 positions.  Both are free of bank conflicts
+// (128 banks), and each wave's bytes are its own.
+__device__ __forceinline__ int tswz(int r) { return ((r & 3) << 3) | ((r >> 2) & 7); }
+
+struct DzStager {
+  LDS_AS char* t3;
+  uint32_t row[4];  // byte offset of token row wt0 + 32 nb + lane % 32
+  int sw[4];
+  int wt0, wv0, lane;
+
+  __device__ __forceinline__ void init(char* tile, int wt0_, int wv0_, int lane_) {
+    wt0 = wt0_;
+    wv0 = wv0_;
+    lane = lane_;
+    t3 = (LDS_AS char*)tile;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int r = wt0 + 32 * nb + (lane & 31);
+      row[nb] = (uint32_t)r * 512u + (uint32_t)(lane >> 5) * 8u;
+      sw[nb] = tswz(r);
+    }
+  }
+
+  // vocabulary rows wv0 + 32 mb + 8 q + 4 (lane / 32) + 0..3 of token column nb
+  __device__ __forceinline__ void put(int nb, int mb, int q, const float (&d)[4]) const {
+    const int c = (wv0 >> 3) + 4 * mb + q;
+    const f32x2 p0 = {d[0], d[1]}, p1 = {d[2], d[3]};
+    const u32x2 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(p0, bf16x2)),
+                     __builtin_bit_cast(uint32_t, __builtin_convertvector(p1, bf16x2))};
+    *(LDS_AS u32x2*)(t3 + row[nb] + ((c ^ sw[nb]) << 4)) = v;
+  }
+
+  // Wait until this wave's staging writes are in LDS (its own reads follow).
+  __device__ __forceinline__ void fence() const { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+  // Store the wave's staged token rows of block nb (32 rows, its 128 vocabulary
+  // columns) to the tile-blocked buffer (dst = the tile's 256 x 64 block 0, block q at
+  // dst + q BLK_ELEMS, row r at 64 r): two pieces of 32 consecutive rows, 1 KiB per
+  // instruction.
+  __device__ __forceinline__ void store_blocked(int nb, uint16_t* dst) const {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int qb = it >> 2, r = wt0 + 32 * nb + 8 * (it & 3) + (lane >> 3), c8 = lane & 7;
+      const int c = (wv0 >> 3) + 8 * qb + c8;
+      const u32x4 v = *(LDS_AS const u32x4*)(t3 + r * 512 + ((c ^ tswz(r)) << 4));
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4*>(dst + (long)((wv0 >> 6) + qb) * BLK_ELEMS + r * BLK_COLS + 8 * c8));
+    }
+  }
+};
+
+// A wave's d-logits, d = 2^(c1 acc - lse2) (c0 + cb acc) + [row = target] sa with the
+// per-token parameters of its 4 token columns (from LDS, see bwd_dlogits_kernel),
+// rounded to bf16, staged in the wave's own part of the LDS tile and stored to the
+// tile-blocked buffer at dst (the tile's 256 x 64 block 0) 32 token rows at a time.
+// RAGGED: vocabulary rows at or past `vrows` of the wave tile become 0.  Every wave
+// runs the same instruction stream whether or not it holds a target (the correction is
+// a branch per four vocabulary rows that almost never has active lanes), which keeps
+// the tiles of an XCD in step.
 template <bool ENTGRAD, bool RAGGED>
 __device__ __forceinline__ void stage_dlogits(char* tile, const f32x16 (&acc)[4][4],
                                               const float* r_lse2, const float* r_c0,
                                               const float* r_cb, const float* r_sa,
-                                              const int* t_local, int wr0, int wc0, int lane,
-                                              float c1, unsigned colmask, uint16_t* dst) {
+                                              const int* t_local, int wv0, int wt0, int lane,
+                                              float c1, int vrows, uint16_t* dst) {
   const int lc = lane & 31, hi = lane >> 5;
-  WaveStager st;
-  st.init(tile, wr0, wc0, lane);
+  float L[4], C0[4], CB[4], SA[4];
+  int T[4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int nb = 0; nb < 4; ++nb) {
+    const int t = wt0 + 32 * nb + lc;
+    L[nb] = r_lse2[t];
+    C0[nb] = r_c0[t];
+    CB[nb] = ENTGRAD ? r_cb[t] : 0.f;
+    SA[nb] = r_sa[t];
+    T[nb] = t_local[t] - wv0 - 4 * hi;  // the target's row among the lane's, if any
+  }
+  DzStager st;
+  st.init(tile, wt0, wv0, lane);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // rows rb .. rb + 3 are the lane's slots e = 4 q .. 4 q + 3 of block mb
-      const int rb = wr0 + 32 * mb + 8 * q + 4 * hi;
-      const float4 L4 = *reinterpret_cast<const float4*>(r_lse2 + rb);
-      const float4 C4 = *reinterpret_cast<const float4*>(r_c0 + rb);
-      const float L[4] = {L4.x, L4.y, L4.z, L4.w}, C0[4] = {C4.x, C4.y, C4.z, C4.w};
-      float CB[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (ENTGRAD) {
-        const float4 B4 = *reinterpret_cast<const float4*>(r_cb + rb);
-        CB[0] = B4.x; CB[1] = B4.y; CB[2] = B4.z; CB[3] = B4.w;
-      }
-      float d[4][4];
+  for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
+      for (int q = 0; q < 4; ++q) {
+        float d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
           const float av = acc_read(acc[mb][nb][4 * q + j]);
-          const float pr = __builtin_amdgcn_exp2f(fmaf(av, c1, -L[j]));
-          float v = pr * (ENTGRAD ? fmaf(CB[j], av, C0[j]) : C0[j]);
-          if constexpr (RAGGED) v = ((colmask >> nb) & 1u) ? v : 0.f;
-          d[j][nb] = v;
+          const float pr = __builtin_amdgcn_exp2f(fmaf(av, c1, -L[nb]));
+          float v = pr * (ENTGRAD ? fmaf(CB[nb], av, C0[nb]) : C0[nb]);
+          if constexpr (RAGGED) v = 32 * mb + 8 * q + 4 * hi + j < vrows ? v : 0.f;
+          d[j] = v;
         }
-      // the target column of row rb + j lies in this lane's column nb iff
-      // t_local - wc0 - lc = 32 nb: rare, so one branch per four rows
-      const int4 T4 = *reinterpret_cast<const int4*>(t_local + rb);
-      const int DD[4] = {T4.x - wc0 - lc, T4.y - wc0 - lc, T4.z - wc0 - lc, T4.w - wc0 - lc};
-      if (((DD[0] & ~0x60) == 0) | ((DD[1] & ~0x60) == 0) | ((DD[2] & ~0x60) == 0) |
-          ((DD[3] & ~0x60) == 0)) {
-        const float4 S4 = *reinterpret_cast<const float4*>(r_sa + rb);
-        const float SA[4] = {S4.x, S4.y, S4.z, S4.w};
+        const int dd = T[nb] - 32 * mb - 8 * q;
+        if ((unsigned)dd < 4u) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) d[j][nb] += DD[j] == 32 * nb ? SA[j] : 0.f;
+          for (int j = 0; j < 4; ++j) d[j] += dd == j ? SA[nb] : 0.f;
+        }
+        st.put(nb, mb, q, d);
       }
-#pragma unroll
-      for (int jp = 0; jp < 4; jp += 2)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) st.put(mb, q, jp, nb, d[jp][nb], d[jp + 1][nb]);
-    }
     st.fence();
-    st.store_blocked(mb, dst);
+    st.store_blocked(nb, dst);
   }
 }
 
@@ -1280,10 +1317,12 @@ __device__ __forceinline__ void dlogits_tile(const DlogitsArgs& p, int mt, int v
     }
   }
 
+  // the tile computed transposed: vocabulary rows (A = W), token columns (B = X, whose
+  // loads go first in each stage)
   f32x16 acc[4][4];
-  const TileSrc A{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, 0};
-  const TileSrc B{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, 0};
-  mainloop<BigShape, true, true>(acc, smem, A, B, p.H);
+  const TileSrc A{p.W + (long)col0 * p.H, p.H, p.V - col0, p.H, 0};
+  const TileSrc B{p.X + (long)row0 * p.H, p.H, p.M - row0, p.H, 0};
+  mainloop<BigShape, true, true, true>(acc, smem, A, B, p.H);
 
   float* r_lse2 = reinterpret_cast<float*>(smem + LDS_OUT);
   float* r_c0 = r_lse2 + TILE;
@@ -1297,19 +1336,17 @@ __device__ __forceinline__ void dlogits_tile(const DlogitsArgs& p, int mt, int v
   t_local[tid] = tl;
   __syncthreads();
 
-  const int wr0 = (wave >> 1) * 128, wc0 = (wave & 1) * 128;
+  const int wv0 = (wave >> 1) * 128, wt0 = (wave & 1) * 128;
   const float c1 = p.scale * LOG2E;
   const bool ragged = col0 + TILE > p.V;
-  unsigned colmask = 0;
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) colmask |= (col0 + wc0 + 32 * nb + (lane & 31) < p.V ? 1u : 0u) << nb;
+  const int vrows = p.V - col0 - wv0;  // vocabulary rows of the wave tile that exist
   uint16_t* const dst = p.dz + (long)mt * BLK_ROWS * p.ldz + (long)(ccol0 / BLK_COLS) * BLK_ELEMS;
   if (!ragged)
-    stage_dlogits<ENTGRAD, false>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1,
-                                  colmask, dst);
+    stage_dlogits<ENTGRAD, false>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wv0, wt0, lane, c1,
+                                  vrows, dst);
   else
-    stage_dlogits<ENTGRAD, true>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wr0, wc0, lane, c1,
-                                 colmask, dst);
+    stage_dlogits<ENTGRAD, true>(smem, acc, r_lse2, r_c0, r_cb, r_sa, t_local, wv0, wt0, lane, c1,
+                                 vrows, dst);
 }
 
 template <bool ENTGRAD>
