@@ -17,8 +17,9 @@
 // Backward (Liger-Kernel PR 1294, "Kernel design notes": recompute the logits
 // tiles, emit d-logits in the input dtype into a reusable buffer, then two grad
 // GEMMs; SkyRL PR 2141, "Overview": split backward over the vocabulary):
-//   bwd_dlogits  the same mainloop, epilogue forms scale * dz in bf16 for one
-//                vocabulary chunk, stored tile-blocked (256 x 64 blocks).
+//   bwd_dlogits  the same mainloop on the same transposed tile, epilogue forms
+//                scale * dz in bf16 for one vocabulary chunk, stored tile-blocked
+//                (256 x 64 blocks).
 //   gemm_dw      dW[chunk] = dz_chunk^T X          (K = tokens)
 //   gemm_dx      dX (+)= dz_chunk W[chunk]          (K = chunk columns)
 //
