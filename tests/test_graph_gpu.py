@@ -1,6 +1,9 @@
 """The library's calls inside a captured HIP graph: every kernel launch is captured
 (no allocation, no memset, no host synchronisation inside a call), and replays give
-the eager results bit for bit, also with eager work and synchronisation between them."""
+the eager results bit for bit, also with eager work and synchronisation between them.
+At the larger shape the forward, d-logit and dW launches hand out their last tiles
+through counters in the workspace, which kernels of the same call zero: every replay
+must find them cleared."""
 import pytest
 
 from synth import inputs
@@ -9,12 +12,21 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def test_forward_backward_graph_replays_match_eager():
+@pytest.mark.parametrize("shape", [(700, 320, 1500), (4096, 8192, 65836)],
+                         ids=["small", "queued_tiles"])
+def test_forward_backward_graph_replays_match_eager(shape):
     import torch
     from log_prob_amd import flce
-    c = inputs.make_case("graph", 401, 700, 320, 1500, ignore_frac=0.05, grad_mode="normal")
-    X, W, t, glp, gent = gu.to_dev(c)
+    M, H, V = shape
+    c = inputs.make_case("graph", 401, M, H, V, ignore_frac=0.05, grad_mode="normal")
     fb, bb = flce.workspace_query(c.M, c.H, c.V, True)
+    if M > 700:
+        # three launches per step, each of at least 2048 tiles (256 per XCD)
+        rows, chunk, pipe = flce.backward_schedule(M, H, V, bb)
+        tiles = lambda n: -(-n // 256)
+        assert not pipe and rows >= M
+        assert min(tiles(M) * tiles(V), tiles(M) * tiles(chunk), tiles(chunk) * tiles(H)) >= 2048
+    X, W, t, glp, gent = gu.to_dev(c)
     ws = torch.empty(max(fb, bb), dtype=torch.uint8, device="cuda")
     lp = torch.empty(c.M, device="cuda")
     lse = torch.empty_like(lp)
