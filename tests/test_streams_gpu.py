@@ -1,6 +1,8 @@
 """Calls on several streams at once: the library keeps no state between calls (every
-buffer is the caller's), so work enqueued on two streams, or from two host threads,
-gives the same bits as the same calls run one after another."""
+buffer is the caller's, the tile-queue counters included), so work enqueued on several
+streams, or from several host threads, gives the same bits as the same calls run one
+after another.  The third case's forward, d-logit and dW launches (at least 2048 tiles
+each) hand out their last tiles through the counters of their own workspace."""
 import threading
 
 import pytest
@@ -13,6 +15,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     dict(name="s_a", case_id=501, M=700, H=320, V=1500, ignore_frac=0.05, grad_mode="normal"),
     dict(name="s_b", case_id=502, M=513, H=136, V=2600, scale=1 / 0.7, grad_mode="normal_lp"),
+    dict(name="s_q", case_id=503, M=4096, H=8192, V=65836, ignore_frac=0.05, grad_mode="normal"),
 ]
 
 
