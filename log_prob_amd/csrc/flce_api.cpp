@@ -846,12 +846,23 @@ flce_status_t backward_run(const void* X, const void* W, const int64_t* targets,
 
   if (!P.pipe) {
     // queue counters: the d-logit launches use q0 and zero q1, the dW launches use q1 and
-    // zero q0, so each starts from zero; q0 is zeroed here for the first step
+    // zero q0, so each starts from zero; q0 is zeroed here for the first step, unless no
+    // launch of the call queues tiles.  Grids differ only between the first and last
+    // wave and the first and last chunk, so the four corner steps cover every launch.
     unsigned long long* q0 = reinterpret_cast<unsigned long long*>(ws + P.off_q);
     unsigned long long* q1 = q0 + 8;
-    hipError_t e = flce::launch_fill_zero_u16(reinterpret_cast<uint16_t*>(q0),
-                                              long(8 * sizeof(*q0) / 2), stream);
-    if (e != hipSuccess) return hip_fail(e, "zero-fill kernel launch");
+    auto queues = [&](int64_t k) {
+      const Step s = step_args(k);
+      return flce::queue_shape(int64_t(s.d.n_mt) * s.d.n_vt).queue > 0 ||
+             flce::queue_shape(int64_t(s.g.n_i) * s.g.n_h).queue > 0;
+    };
+    hipError_t e = hipSuccess;
+    if (queues(0) || queues(n_chunks - 1) || queues((n_waves - 1) * n_chunks) ||
+        queues(steps - 1)) {
+      e = flce::launch_fill_zero_u16(reinterpret_cast<uint16_t*>(q0), long(8 * sizeof(*q0) / 2),
+                                     stream);
+      if (e != hipSuccess) return hip_fail(e, "zero-fill kernel launch");
+    }
     for (int64_t k = 0; k < steps; ++k) {
       Step s = step_args(k);
       s.d.tq.ctr = q0;
