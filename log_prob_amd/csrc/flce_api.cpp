@@ -35,7 +35,7 @@ constexpr int64_t kMaxM = int64_t(1) << 30;
 constexpr int64_t kMaxV = int64_t(1) << 30;
 constexpr int64_t kMaxH = int64_t(1) << 20;
 // A dispatch covers at most 2^32 - 1 work-items per dimension: the tile kernels run
-// 256 threads per workgroup, the target-logit kernel 64 per row, the merge 8 per row.
+// 256 threads per workgroup, the target-logit kernel 64 per row, the merge 16 per row.
 constexpr int64_t kMaxWorkgroups = flce::kMaxWorkgroups;
 constexpr int64_t kMaxWaveRows = (0xFFFFFFFFLL / 64) / 256 * 256;
 constexpr size_t kAlign = 256;

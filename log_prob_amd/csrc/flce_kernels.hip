@@ -1088,10 +1088,12 @@ __global__ __launch_bounds__(64 * TL_ROWS) void target_logit_kernel(FwdTileArgs 
 // logprob = min(z_t - lse, 0), entropy = max(log S - U / S, 0).
 // The tiles j run over every shard of the table in order (one shard when the
 // vocabulary is not split); the target logit comes from the shard that owns the target.
-// A workgroup takes MERGE_ROWS rows; its MERGE_SLICES waves split each row's tiles
-// (lanes read consecutive rows of one tile, so every load is a coalesced 256 bytes)
-// and combine their maxima, then their sums, through LDS.
-constexpr int MERGE_ROWS = 64, MERGE_SLICES = 8;
+// A workgroup takes MERGE_ROWS rows; its MERGE_SLICES slices split each row's tiles
+// (32 lanes read consecutive rows of one tile, so every load is a 128-byte line) and
+// combine their maxima, then their sums, through LDS.  32 rows x 16 slices measured
+// faster than 64 x 8 (fewer tiles per thread, twice the workgroups: 35 -> 22 us at
+// M = H = 8192, V = 131072) and than 16 x 32 (64-byte pieces).
+constexpr int MERGE_ROWS = 32, MERGE_SLICES = 16;
 template <bool ENT>
 __global__ __launch_bounds__(MERGE_ROWS * MERGE_SLICES) void fwd_merge_kernel(FwdMergeArgs p) {
   __shared__ float sm[3][MERGE_SLICES][MERGE_ROWS];
